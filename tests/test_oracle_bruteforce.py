@@ -1,0 +1,82 @@
+"""Brute-force pin of the float64 oracle: the whole step evaluated with mpmath
+at 50 significant digits on tiny inputs.
+
+The mpmath side is written directly from the node formulas of the
+"Qwen3-0.6B" Model Spec page ("Compute-graph nodes": attn.qk_norm,
+attn.rope, attn.core) with plain loops, independently of the oracle's
+vectorised NumPy.  The oracle must agree to ~1e-13 relative; a wrong index,
+sign or normaliser would show up at 1e-6 or worse ("Model conformance" page,
+note on typical error sizes).
+"""
+import numpy as np
+import pytest
+
+mpmath = pytest.importorskip("mpmath")
+from mpmath import mp, mpf  # noqa: E402
+
+from oracle import decode_attention as O  # noqa: E402
+
+
+def _mp_norm_rope(x, w, eps, pos, theta):
+    """One head: RMSNorm over 128 dims, then rotate pairs (i, i+64)."""
+    d = len(x)
+    ms = sum(xi * xi for xi in x) / d
+    inv = 1 / mp.sqrt(ms + eps)
+    y = [x[i] * inv * w[i] for i in range(d)]
+    out = list(y)
+    for i in range(d // 2):
+        ang = pos * mp.power(theta, mpf(-2 * i) / d)
+        c, s = mp.cos(ang), mp.sin(ang)
+        out[i] = y[i] * c - y[i + d // 2] * s
+        out[i + d // 2] = y[i] * s + y[i + d // 2] * c
+    return out
+
+
+def _mp_decode(qh, ks, vs):
+    d = len(qh)
+    scale = 1 / mp.sqrt(d)
+    z = [sum(qh[j] * k[j] for j in range(d)) * scale for k in ks]
+    m = max(z)
+    e = [mp.exp(zi - m) for zi in z]
+    tot = sum(e)
+    return [sum(e[s] * vs[s][j] for s in range(len(ks))) / tot for j in range(d)]
+
+
+@pytest.mark.parametrize("seq_len,seed", [(1, 0), (5, 1), (17, 2), (33, 3)])
+def test_step_matches_50_digit_brute_force(seq_len, seed):
+    mp.dps = 50
+    r = np.random.default_rng([99, seed])
+    q = r.standard_normal((1, 16, 128))
+    kn = r.standard_normal((1, 8, 128)) * 2
+    vn = r.standard_normal((1, 8, 128))
+    wq = 1 + 0.1 * r.standard_normal(128)
+    wk = 1 + 0.1 * r.standard_normal(128)
+    npages = -(-seq_len // 16)
+    pool_k = r.standard_normal((npages + 2, 8, 16, 128)).astype(np.float32)
+    pool_v = r.standard_normal((npages + 2, 8, 16, 128)).astype(np.float32)
+    table = r.permutation(npages + 2)[:npages].astype(np.int32)[None]
+    eps, theta = 1e-6, 1e6
+    res = O.decode_step(q, kn, vn, wq, wk, pool_k, pool_v, table, np.array([seq_len]), "f32",
+                        eps=eps, theta=theta)
+
+    pos = seq_len - 1
+    to_mp = lambda a: [mpf(float(t)) for t in a]  # noqa: E731
+    wq_m, wk_m = to_mp(wq), to_mp(wk)
+    q_rot = [_mp_norm_rope(to_mp(q[0, h]), wq_m, mpf(eps), pos, mpf(theta)) for h in range(16)]
+    k_rot = [_mp_norm_rope(to_mp(kn[0, g]), wk_m, mpf(eps), pos, mpf(theta)) for g in range(8)]
+    for h in range(16):
+        got = res["q_out"][0, h]
+        want = np.array([float(t) for t in q_rot[h]])
+        assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want))
+    for h in range(16):
+        g = h // 2
+        ks, vs = [], []
+        for s in range(seq_len):
+            if s == pos:
+                ks.append(k_rot[g]); vs.append(to_mp(vn[0, g]))
+            else:
+                page, slot = table[0, s // 16], s % 16
+                ks.append(to_mp(pool_k[page, g, slot])); vs.append(to_mp(pool_v[page, g, slot]))
+        want = np.array([float(t) for t in _mp_decode(q_rot[h], ks, vs)])
+        got = res["o"][0, h]
+        assert np.max(np.abs(got - want)) <= 1e-13 * max(1.0, np.max(np.abs(want))), h
