@@ -1,0 +1,216 @@
+"""Benchmark of the decode-attention block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b256_s2048]
+
+A step is one pass of the whole hot path over the batch: qk_norm + RoPE +
+cache append (qk_norm_rope_append), then split-S decodeGQA with its
+log-sum-exp combine (paged_decode_gqa) -- exactly the launches
+decode_attn_step issues, made as its two calls so that HIP events can
+bracket the decode launch.  Inputs are synthetic, seeded and resident in HBM
+before timing starts.
+
+The JSON line reports
+  value           KV-read throughput, GB/s = (sum of seq_lens * 4096 B) / step time
+  roofline        the decode launch (dominant kernel): algorithmic KV bytes per
+                  launch / its average duration measured with HIP events on the
+                  launch stream, against MI355X's 8 TB/s HBM peak
+  cpu_baseline    the float64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from inputs import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_head_amd", "csrc", "dah_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_b256_s2048_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="b256_s2048", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = planner's choice")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time paged_decode_gqa alone (profiling aid)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_val or m_src.group(1) != source_digest():
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(w, t, seq_lens, table, budget_s):
+    """Time the oracle's decode step, one sequence at a time, until the
+    budget is spent.  Host copies of each sequence's pages are made before
+    its timer starts."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import decode_attention as O
+    from dah_testlib import host_snapshot
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    order = np.random.default_rng(7).permutation(len(seq_lens))
+    done, elapsed, kv_bytes = 0, 0.0, 0
+    for b in order:
+        snap = host_snapshot(t, seq_lens, table, [int(b)])
+        t0 = time.perf_counter()
+        O.decode_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"],
+                      snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
+                      w.cache_dtype)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        kv_bytes += W.algorithmic_kv_bytes(seq_lens[[int(b)]], w.cache_dtype)
+        if elapsed >= budget_s:
+            break
+    return {
+        "value": kv_bytes / elapsed / 1e9,
+        "unit": "GB/s",
+        "seqs_per_s": done / elapsed,
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(seq_lens)} sequences of {w.name}, full decode step each "
+                  f"(float64 NumPy, {elapsed:.1f} s)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decode_attention_head_amd as dah
+
+    w = W.WORKLOADS[args.workload]
+    if w.num_layers != 1:
+        sys.exit(f"{w.name} has {w.num_layers} layers; the bench times one-layer workloads")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    seq_lens = W.make_seq_lens(w)
+    table, num_pages = W.make_block_table(w, seq_lens)
+    t = W.make_layer(w, 0, dev, table=table, num_pages=num_pages, seq_lens=seq_lens)
+    B = w.batch
+    L = int(seq_lens.max())
+    splits, pps = dah.plan_splits(B, L, args.num_splits)
+    ws_bytes = dah.workspace_bytes(B, L, args.num_splits)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    q_out = torch.empty_like(t["q"])
+    o = torch.empty_like(t["q"])
+    stream = torch.cuda.current_stream(dev)
+
+    def append():
+        dah.qk_norm_rope_append(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                q_out=q_out)
+
+    def decode():
+        dah.paged_decode_gqa(q_out, t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L,
+                             num_splits=args.num_splits, o=o, workspace=ws)
+
+    for _ in range(args.warmup):
+        if not args.decode_only:
+            append()
+        decode()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.decode_only:
+            append()
+        starts[i].record(stream)
+        decode()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    decode_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+
+    kv_bytes = W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)
+    gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
+    traffic = read_traffic() if (w.name == "b256_s2048" and args.num_splits == 0) else None
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, t, seq_lens, table, args.cpu_seconds)
+
+    line = {
+        "metric": "paged GQA decode KV-read GB/s (% of HBM peak) and seqs/s at B=256",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 KV, f32 compute" if w.cache_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) q/k/v, gains 1+N(0,0.1), random block table)",
+        "config": {
+            "workload": w.name,
+            "batch": B,
+            "seq_len": "fixed 2048" if w.name == "b256_s2048" else f"max {L}",
+            "heads": "16 q / 8 kv, D=128, page 16",
+            "kv_bytes_per_step": kv_bytes,
+            "splits": splits,
+            "pages_per_split": pps,
+            "step": "decode only" if args.decode_only else "norm+rope+append, decode+combine",
+        },
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(B / (ms_step * 1e-3), 1),
+        "roofline": {
+            "kernel": "paged_decode_gqa (decode_split_kernel" + (" + combine)" if splits > 1 else ")"),
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(decode_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+"""Qwen3-0.6B decode-attention block on AMD MI355X (gfx950): thin Python binding.
+
+The three calls mirror the C ABI in include/dah.h and only marshal arguments:
+they check torch dtypes, shapes, devices and contiguity, then pass raw device
+pointers and the current HIP stream to libdah.so.  Every step of the
+computation runs in the library's HIP kernels.
+
+    qk_norm_rope_append  nodes attn.qk_norm + attn.rope and the cache store
+    paged_decode_gqa     node attn.core (decodeGQA) over the paged cache
+    decode_attn_step     both, in order, on one stream
+
+(Node names from the "Qwen3-0.6B" Model Spec page, "Compute-graph nodes".)
+
+Cache layout: k_cache / v_cache are [num_pages, 8, 16, 128] tensors of
+float32 or bfloat16 (page, KV head, slot, dim); block_table is int32
+[B, max_pages_per_seq]; seq_lens is int32 [B] and counts the new token.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._native import DAH_BF16, DAH_F32, DahError, LIB_PATH, check, lib
+
+__all__ = [
+    "qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step", "plan_splits",
+    "workspace_bytes", "DahError", "LIB_PATH", "NUM_HEADS", "NUM_KV_HEADS", "HEAD_DIM",
+    "PAGE_SIZE",
+]
+
+NUM_HEADS = 16
+NUM_KV_HEADS = 8
+HEAD_DIM = 128
+PAGE_SIZE = 16
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _require(t, name, dtype, shape=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _cache_dtype(k_cache, v_cache) -> int:
+    torch = _torch()
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache must share a dtype")
+    if k_cache.dtype == torch.bfloat16:
+        return DAH_BF16
+    if k_cache.dtype == torch.float32:
+        return DAH_F32
+    raise TypeError(f"cache dtype must be float32 or bfloat16, got {k_cache.dtype}")
+
+
+def _check_cache(k_cache, v_cache, block_table, seq_lens, B, device):
+    torch = _torch()
+    dt = _cache_dtype(k_cache, v_cache)
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM):
+        raise ValueError(f"k_cache must be [num_pages, 8, 16, 128], got {tuple(k_cache.shape)}")
+    _require(k_cache, "k_cache", k_cache.dtype, device=device)
+    _require(v_cache, "v_cache", k_cache.dtype, tuple(k_cache.shape), device)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, max_pages_per_seq]")
+    _require(block_table, "block_table", torch.int32, device=device)
+    _require(seq_lens, "seq_lens", torch.int32, (B,), device)
+    return dt
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def plan_splits(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | None = None):
+    """(splits, pages_per_split) the planner picks; num_cus defaults to the
+    current device's compute-unit count."""
+    if num_cus is None:
+        torch = _torch()
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    s, p = ctypes.c_int(), ctypes.c_int()
+    check(lib().dah_plan_splits(B, max_seq_len, num_splits, num_cus, ctypes.byref(s),
+                                ctypes.byref(p)), "dah_plan_splits")
+    return s.value, p.value
+
+
+def workspace_bytes(B: int, max_seq_len: int, num_splits: int = 0,
+                    num_cus: int | None = None) -> int:
+    if num_cus is None:
+        return int(lib().dah_workspace_bytes(B, max_seq_len, num_splits))
+    return int(lib().dah_workspace_bytes_for(B, max_seq_len, num_splits, num_cus))
+
+
+def _workspace(workspace, B, max_seq_len, num_splits, device):
+    torch = _torch()
+    need = workspace_bytes(B, max_seq_len, num_splits)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _require(workspace, "workspace", workspace.dtype, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def qk_norm_rope_append(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_table,
+                        seq_lens, *, eps: float = 1e-6, rope_theta: float = 1e6, q_out=None,
+                        stream=None):
+    """Norm and rotate q and the new k at pos = seq_lens - 1, store k and v
+    in the cache.  Returns q_out [B,16,128] float32 (q_out may be q)."""
+    torch = _torch()
+    B = q.shape[0]
+    dev = q.device
+    _require(q, "q", torch.float32, (B, NUM_HEADS, HEAD_DIM))
+    _require(k_new, "k_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(v_new, "v_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(q_gain, "q_gain", torch.float32, (HEAD_DIM,), dev)
+    _require(k_gain, "k_gain", torch.float32, (HEAD_DIM,), dev)
+    dt = _check_cache(k_cache, v_cache, block_table, seq_lens, B, dev)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _require(q_out, "q_out", torch.float32, (B, NUM_HEADS, HEAD_DIM), dev)
+    st = lib().qk_norm_rope_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
+        _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, _ptr(q_out), _stream(dev, stream))
+    check(st, "qk_norm_rope_append")
+    return q_out
+
+
+def paged_decode_gqa(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, *,
+                     num_splits: int = 0, o=None, workspace=None, stream=None):
+    """decodeGQA over the paged cache.  q is already normed and roped.
+    max_seq_len bounds every seq_lens[b] (host value, for the planner).
+    Returns o [B,16,128] float32."""
+    torch = _torch()
+    B = q.shape[0]
+    dev = q.device
+    _require(q, "q", torch.float32, (B, NUM_HEADS, HEAD_DIM))
+    dt = _check_cache(k_cache, v_cache, block_table, seq_lens, B, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    _require(o, "o", torch.float32, (B, NUM_HEADS, HEAD_DIM), dev)
+    ws, ws_bytes = _workspace(workspace, B, max_seq_len, num_splits, dev)
+    st = lib().paged_decode_gqa(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, int(max_seq_len), int(num_splits), _ptr(o),
+        None if ws is None else _ptr(ws), ws_bytes, _stream(dev, stream))
+    check(st, "paged_decode_gqa")
+    return o
+
+
+def decode_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_table, seq_lens,
+                     max_seq_len: int, *, eps: float = 1e-6, rope_theta: float = 1e6,
+                     num_splits: int = 0, q_out=None, o=None, workspace=None, stream=None):
+    """One decode step of one layer: norm, RoPE, cache append, decodeGQA.
+    Returns (q_out, o)."""
+    torch = _torch()
+    B = q.shape[0]
+    dev = q.device
+    _require(q, "q", torch.float32, (B, NUM_HEADS, HEAD_DIM))
+    _require(k_new, "k_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(v_new, "v_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(q_gain, "q_gain", torch.float32, (HEAD_DIM,), dev)
+    _require(k_gain, "k_gain", torch.float32, (HEAD_DIM,), dev)
+    dt = _check_cache(k_cache, v_cache, block_table, seq_lens, B, dev)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if o is None:
+        o = torch.empty_like(q)
+    _require(q_out, "q_out", torch.float32, (B, NUM_HEADS, HEAD_DIM), dev)
+    _require(o, "o", torch.float32, (B, NUM_HEADS, HEAD_DIM), dev)
+    ws, ws_bytes = _workspace(workspace, B, max_seq_len, num_splits, dev)
+    st = lib().decode_attn_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
+        _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, int(max_seq_len), int(num_splits), _ptr(q_out),
+        _ptr(o), None if ws is None else _ptr(ws), ws_bytes, _stream(dev, stream))
+    check(st, "decode_attn_step")
+    return q_out, o

@@ -1,0 +1,70 @@
+"""ctypes view of libdah.so: the C ABI of include/dah.h, function by function.
+
+Loading fails loudly when the library has not been built; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdah.so")
+
+DAH_F32 = 0
+DAH_BF16 = 1
+
+STATUS_NAMES = {
+    0: "DAH_OK", 1: "DAH_ERR_NULL", 2: "DAH_ERR_SHAPE", 3: "DAH_ERR_DTYPE",
+    4: "DAH_ERR_ALIGN", 5: "DAH_ERR_WORKSPACE", 6: "DAH_ERR_HIP",
+}
+
+_c_int, _c_float, _c_i64, _c_size, _vp = (ctypes.c_int, ctypes.c_float, ctypes.c_int64,
+                                           ctypes.c_size_t, ctypes.c_void_p)
+
+# name -> (restype, argtypes), in the order of include/dah.h
+SIGNATURES = {
+    "qk_norm_rope_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_float, _c_float, _vp, _vp, _c_int,
+                                     _c_i64, _vp, _c_int, _vp, _c_int, _vp, _vp]),
+    "paged_decode_gqa": (_c_int, [_vp, _vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int, _c_int,
+                                  _c_int, _vp, _vp, _c_size, _vp]),
+    "decode_attn_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_float, _c_float, _vp, _vp, _c_int,
+                                  _c_i64, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                  _c_size, _vp]),
+    "dah_plan_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
+                                 ctypes.POINTER(_c_int)]),
+    "dah_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "dah_workspace_bytes_for": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "dah_status_string": (ctypes.c_char_p, [_c_int]),
+    "dah_last_error": (ctypes.c_char_p, []),
+}
+
+_LIB = None
+
+
+class DahError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {detail}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded once)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m decode_attention_head_amd.build` "
+                "(hipcc, gfx950). There is no fallback implementation.")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def check(status: int, where: str) -> None:
+    if status != 0:
+        detail = lib().dah_last_error().decode(errors="replace")
+        raise DahError(status, where, detail)

@@ -1,0 +1,44 @@
+// Host-side helpers of the decode-attention library: argument validation, the
+// split planner and error reporting.  Nothing here touches the HIP runtime, so
+// it builds and runs without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dah {
+
+constexpr int kHeads = 16;     // query heads
+constexpr int kKvHeads = 8;    // key/value heads; query head h reads KV head h / 2
+constexpr int kHeadDim = 128;  // head dimension
+constexpr int kPage = 16;      // positions per cache page
+
+// Records `msg` (printf-style) as this thread's last error and returns status.
+int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+struct Plan {
+  int splits;           // split ranges per sequence
+  int pages_per_split;  // pages per split range
+  size_t workspace;     // bytes of partial results (0 when splits == 1)
+};
+
+// Split planner: pure integer policy from the batch size, the longest
+// sequence and the compute-unit count.  Returns a dah_status.
+int plan_splits(int B, int max_seq_len, int num_splits, int num_cus, Plan* out);
+
+// Workspace bytes for a plan: per (sequence, query head, split) 128 floats of
+// weighted V plus (running max, sum).
+size_t workspace_bytes(int B, int splits);
+
+int validate_append(const void* q, const void* k_new, const void* v_new, const void* q_gain,
+                    const void* k_gain, float eps, float rope_theta, const void* k_cache,
+                    const void* v_cache, int cache_dtype, int64_t num_pages,
+                    const void* block_table, int max_pages_per_seq, const void* seq_lens, int B,
+                    const void* q_out);
+
+int validate_decode(const void* q, const void* k_cache, const void* v_cache, int cache_dtype,
+                    int64_t num_pages, const void* block_table, int max_pages_per_seq,
+                    const void* seq_lens, int B, int max_seq_len, int num_splits, const void* o);
+
+}  // namespace dah

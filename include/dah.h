@@ -1,0 +1,189 @@
+/*
+ * dah.h -- C ABI of the Qwen3-0.6B decode-attention block on AMD MI355X (gfx950).
+ *
+ * One decode step of one attention layer, as the "Qwen3-0.6B" Model Spec page
+ * defines it in its "Compute-graph nodes" table:
+ *
+ *   attn.qk_norm  y = x / sqrt(sum_j x_j^2 / 128 + eps) * w, per head, one gain
+ *                 vector shared by all 16 query heads and one by all 8 key heads
+ *                 (also the nnterp qwen3 page, "The Notes")
+ *   attn.rope     pairs (i, i+64), i < 64, rotated by pos * theta^(-2i/128)
+ *   attn.core     decodeGQA: o[b,h] = sum_{s < seq_lens[b]}
+ *                   softmax_s(<q[b,h], k[b,s,h/2]> / sqrt(128)) * v[b,s,h/2]
+ *
+ * plus the write of the new token's key and value into a paged KV cache with
+ * page size 16 (shape domain in "At a glance"; the "Supported models" page,
+ * "What every spec covers", states decode attention over seq_lens[b] cached
+ * positions).
+ *
+ * Fixed sizes (spec constants): 16 query heads, 8 KV heads, head dim 128,
+ * page size 16.  Query head h reads KV head h / 2.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked [device] are GPU global-memory pointers; tensors are dense
+ *    and row-major in the order given.  The caller owns every buffer; the
+ *    library never allocates, frees or synchronises.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *    stream).  Results are valid once that stream has reached the call.
+ *  - The return value is a dah_status.  Nothing throws or aborts.  Argument
+ *    problems visible on the host return DAH_ERR_* before anything is
+ *    launched; a failed launch returns DAH_ERR_HIP.  dah_last_error() gives a
+ *    one-line description of the last non-OK return on the calling thread.
+ *  - Device-resident values cannot be checked without a synchronisation, so
+ *    they are preconditions, with a defined fault-free result when violated:
+ *      seq_lens[b] <= 0               o[b] = 0, nothing appended, q_out[b] is
+ *                                     the normed query rotated at pos 0
+ *      seq_lens[b] > max_seq_len, or > max_pages_per_seq * 16,
+ *      or a needed block_table entry outside [0, num_pages)
+ *                                     o[b] = NaN, nothing appended for b
+ *    The new token's page must not be shared with another sequence.
+ *
+ * KV cache layout
+ * ---------------
+ *  k_cache and v_cache are pools of pages, each [num_pages][8][16][128]
+ *  = (physical page, KV head, slot, dim), elements float32 (DAH_F32) or
+ *  bfloat16 (DAH_BF16).  One (page, KV head) tile of 16 positions is
+ *  contiguous (4 KiB in bfloat16).  block_table is int32
+ *  [B][max_pages_per_seq]: block_table[b][j] is the physical page of logical
+ *  page j of sequence b, so position s of sequence b lives at
+ *  (block_table[b][s / 16], slot s % 16).  Only the first
+ *  ceil(seq_lens[b] / 16) entries of a row are read.
+ *
+ *  Stores into a bfloat16 cache round float32 to nearest, ties to even.
+ *  All arithmetic is float32; RoPE angles are formed and reduced in float64.
+ */
+#ifndef DAH_H
+#define DAH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DAH_NUM_HEADS 16
+#define DAH_NUM_KV_HEADS 8
+#define DAH_HEAD_DIM 128
+#define DAH_PAGE_SIZE 16
+
+typedef enum {
+  DAH_F32 = 0,  /* float32 cache */
+  DAH_BF16 = 1  /* bfloat16 cache */
+} dah_dtype;
+
+typedef enum {
+  DAH_OK = 0,
+  DAH_ERR_NULL = 1,      /* a required pointer is NULL */
+  DAH_ERR_SHAPE = 2,     /* a size is out of range or sizes disagree */
+  DAH_ERR_DTYPE = 3,     /* unknown cache dtype */
+  DAH_ERR_ALIGN = 4,     /* a pointer lacks the alignment stated below */
+  DAH_ERR_WORKSPACE = 5, /* workspace missing or smaller than dah_workspace_bytes */
+  DAH_ERR_HIP = 6        /* the HIP runtime reported an error (no device, launch failure) */
+} dah_status;
+
+/*
+ * qk_norm_rope_append -- nodes attn.qk_norm and attn.rope of the
+ * "Qwen3-0.6B" Model Spec page ("Compute-graph nodes"; tensors in "Tensors of
+ * the main nodes"), followed by the store of the new token into the cache.
+ *
+ * For every sequence b, with pos = seq_lens[b] - 1 (seq_lens counts the new
+ * token):
+ *   q_out[b,h] = rope(qk_norm(q[b,h], q_gain), pos)          h < 16
+ *   k_cache at (block_table[b][pos/16], g, pos%16) = rope(qk_norm(k_new[b,g], k_gain), pos)
+ *   v_cache at the same place                      = v_new[b,g]  (no norm)
+ *
+ *   q, q_out     [device] float32 [B][16][128], 16-byte aligned; q_out may equal q
+ *   k_new, v_new [device] float32 [B][8][128], 16-byte aligned
+ *   q_gain, k_gain [device] float32 [128]
+ *   eps          RMSNorm epsilon (1e-6 for Qwen3-0.6B), added to the mean square
+ *   rope_theta   RoPE base (1e6 for Qwen3-0.6B)
+ *   k_cache, v_cache [device] pools as described above, 16-byte aligned
+ *   cache_dtype  DAH_F32 or DAH_BF16
+ *   num_pages    pages in each pool (>= 1)
+ *   block_table  [device] int32 [B][max_pages_per_seq]
+ *   seq_lens     [device] int32 [B]
+ *   B            sequences (>= 1)
+ */
+int qk_norm_rope_append(const float* q, const float* k_new, const float* v_new,
+                        const float* q_gain, const float* k_gain, float eps, float rope_theta,
+                        void* k_cache, void* v_cache, int cache_dtype, int64_t num_pages,
+                        const int32_t* block_table, int max_pages_per_seq,
+                        const int32_t* seq_lens, int B, float* q_out, void* stream);
+
+/*
+ * paged_decode_gqa -- node attn.core (decodeGQA) of the "Qwen3-0.6B" Model
+ * Spec page ("Compute-graph nodes"), over the paged cache:
+ *
+ *   o[b,h] = sum_{s < seq_lens[b]} softmax_s(<q[b,h], K[b,s,h/2]> / sqrt(128)) V[b,s,h/2]
+ *
+ * computed as split-S flash decoding: the positions of a sequence are cut
+ * into `splits` contiguous ranges whose partial (max, sum, weighted V) are
+ * merged with a log-sum-exp combine.  The "Supported models" page ("Facts
+ * proved about the specs": flashAttn_eq, softmax_shift) states that this
+ * equals the spec's attention for any partition.
+ *
+ *   q            [device] float32 [B][16][128], already normed and roped, 16-byte aligned
+ *   k_cache, v_cache [device] pools, 16-byte aligned; cache_dtype DAH_F32 or DAH_BF16
+ *   num_pages, block_table, max_pages_per_seq, seq_lens, B  as above
+ *   max_seq_len  host-side bound on every seq_lens[b] (>= 1, <= max_pages_per_seq*16);
+ *                the split planner uses it
+ *   num_splits   0 = let the planner choose; n > 0 asks for at most n splits
+ *                (the planner may use fewer so that no split is empty)
+ *   o            [device] float32 [B][16][128], 16-byte aligned
+ *   workspace    [device] scratch of at least
+ *                dah_workspace_bytes(B, max_seq_len, num_splits) bytes,
+ *                256-byte aligned; may be NULL when that size is 0.  Its
+ *                contents need no initialisation and are garbage afterwards.
+ */
+int paged_decode_gqa(const float* q, const void* k_cache, const void* v_cache, int cache_dtype,
+                     int64_t num_pages, const int32_t* block_table, int max_pages_per_seq,
+                     const int32_t* seq_lens, int B, int max_seq_len, int num_splits,
+                     float* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * decode_attn_step -- the whole decode-attention block for one layer:
+ * qk_norm_rope_append followed, on the same stream, by paged_decode_gqa on
+ * q_out.  The attention reads the position appended by this call.
+ * Arguments are those of the two calls; q_out is required (it may equal q).
+ */
+int decode_attn_step(const float* q, const float* k_new, const float* v_new,
+                     const float* q_gain, const float* k_gain, float eps, float rope_theta,
+                     void* k_cache, void* v_cache, int cache_dtype, int64_t num_pages,
+                     const int32_t* block_table, int max_pages_per_seq,
+                     const int32_t* seq_lens, int B, int max_seq_len, int num_splits,
+                     float* q_out, float* o, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/*
+ * dah_plan_splits -- the split planner, on the host, for a device with
+ * num_cus compute units.  Writes the number of splits and the split length in
+ * pages (every split but the last of the longest sequence covers exactly
+ * that many pages).  num_splits as in paged_decode_gqa.  Returns a dah_status.
+ */
+int dah_plan_splits(int B, int max_seq_len, int num_splits, int num_cus,
+                    int* splits_out, int* pages_per_split_out);
+
+/*
+ * dah_workspace_bytes -- workspace paged_decode_gqa and decode_attn_step need
+ * on the current device for these arguments (0 when one split suffices).
+ * Returns 0 as well for invalid arguments; the entry points then report the
+ * problem.  Queries the current device's compute-unit count once per device.
+ */
+size_t dah_workspace_bytes(int B, int max_seq_len, int num_splits);
+
+/* dah_workspace_bytes_for -- the same for an explicit compute-unit count (no device query). */
+size_t dah_workspace_bytes_for(int B, int max_seq_len, int num_splits, int num_cus);
+
+/* Static name of a dah_status value ("DAH_OK", ...); "unknown status" otherwise. */
+const char* dah_status_string(int status);
+
+/* Detail of the last non-OK return on this thread ("" if none).  Valid until the next call. */
+const char* dah_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAH_H */

@@ -178,11 +178,12 @@ def gather_sequence(pool: np.ndarray, block_table_row: np.ndarray, seq_len: int,
 
     ``pool`` is [num_pages, 8, 16, 128]: K[s, g, :] = pool[block_table_row[s // 16], g, s % 16, :].
     """
-    out = np.empty((seq_len, NUM_KV_HEADS, HEAD_DIM), dtype=np.float64)
-    for s in range(seq_len):
-        page, slot = cache_location(block_table_row, s)
-        out[s] = cache_to_f64(pool[page, :, slot, :], cache_dtype)
-    return out
+    s = np.arange(seq_len)
+    pages = np.asarray(block_table_row)[s // PAGE_SIZE]
+    slots = s % PAGE_SIZE
+    # advanced indices on axes 0 and 2, separated by a slice: the result is
+    # [seq_len, 8, 128] with the position axis first
+    return cache_to_f64(pool[pages, :, slots, :], cache_dtype)
 
 
 # ---------------------------------------------------------------------------

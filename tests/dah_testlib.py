@@ -1,0 +1,153 @@
+"""Helpers shared by the GPU tests: build workloads on the device, copy the
+pages a sampled set of sequences needs to the host (before the GPU step
+modifies the cache), and compare GPU results with the oracle.
+
+Only input marshalling lives here: every expected value is computed by the
+oracle from host copies of the generated inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from inputs import workloads as W
+from oracle import decode_attention as O
+
+
+def cuda_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def build_layer(w: W.Workload, layer: int = 0, device="cuda", seq_lens=None):
+    """Workload tensors on the device plus host-side structure."""
+    seq_lens = W.make_seq_lens(w) if seq_lens is None else np.asarray(seq_lens, np.int32)
+    table, num_pages = W.make_block_table(w, seq_lens)
+    t = W.make_layer(w, layer, device, table=table, num_pages=num_pages, seq_lens=seq_lens)
+    return t, seq_lens, table, num_pages
+
+
+def pool_to_numpy(t):
+    import torch
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def host_snapshot(t: dict, seq_lens, table, batch_indices):
+    """Host copies of what the oracle needs for the sampled sequences: their
+    pages (as a compact pool with a remapped block table) and the small
+    per-sequence tensors."""
+    import torch
+    pages, rows = [], []
+    at = 0
+    for b in batch_indices:
+        n = W.pages_for(int(seq_lens[b]))
+        pages.append(table[b, :n])
+        rows.append(np.arange(at, at + n))
+        at += n
+    idx = torch.from_numpy(np.concatenate(pages).astype(np.int64)).to(t["k_pool"].device)
+    mpp = max(len(r) for r in rows)
+    mini_table = np.zeros((len(batch_indices), mpp), np.int32)
+    for i, r in enumerate(rows):
+        mini_table[i, :len(r)] = r
+    sel = torch.as_tensor(list(batch_indices), device=t["q"].device, dtype=torch.int64)
+    snap = {
+        "k_pool": pool_to_numpy(t["k_pool"].index_select(0, idx)),
+        "v_pool": pool_to_numpy(t["v_pool"].index_select(0, idx)),
+        "block_table": mini_table,
+        "seq_lens": np.asarray(seq_lens)[list(batch_indices)].astype(np.int64),
+        "q": t["q"].index_select(0, sel).cpu().numpy(),
+        "k_new": t["k_new"].index_select(0, sel).cpu().numpy(),
+        "v_new": t["v_new"].index_select(0, sel).cpu().numpy(),
+        "q_gain": t["q_gain"].cpu().numpy(),
+        "k_gain": t["k_gain"].cpu().numpy(),
+    }
+    return snap
+
+
+def sample_batch(seq_lens, k: int, seed: int = 0):
+    """Up to k sequence indices: the shortest, the longest and a seeded rest."""
+    B = len(seq_lens)
+    if B <= k:
+        return list(range(B))
+    rng = np.random.default_rng([seed, B])
+    pick = {int(np.argmin(seq_lens)), int(np.argmax(seq_lens))}
+    for b in rng.permutation(B):
+        if len(pick) >= k:
+            break
+        pick.add(int(b))
+    return sorted(pick)
+
+
+def oracle_decode(snap, cache_dtype):
+    return O.paged_decode_gqa(snap["q"], snap["k_pool"], snap["v_pool"], snap["block_table"],
+                              snap["seq_lens"], cache_dtype)
+
+
+def oracle_step(snap, cache_dtype, eps=W.RMS_EPS, theta=W.ROPE_THETA):
+    return O.decode_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"],
+                         snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
+                         cache_dtype, eps=eps, theta=theta)
+
+
+def read_slots(t, seq_lens, table, batch_indices):
+    """The K and V entries the step wrote (position seq_len - 1), as float64 [n,8,128]."""
+    import torch
+    ks, vs = [], []
+    for b in batch_indices:
+        pos = int(seq_lens[b]) - 1
+        page = int(table[b, pos // W.PAGE_SIZE])
+        slot = pos % W.PAGE_SIZE
+        ks.append(t["k_pool"][page, :, slot, :].to(torch.float64).cpu().numpy())
+        vs.append(t["v_pool"][page, :, slot, :].to(torch.float64).cpu().numpy())
+    return np.stack(ks), np.stack(vs)
+
+
+def bf16_spacing(x: np.ndarray) -> np.ndarray:
+    """Distance between adjacent bfloat16 values around |x| (normal range)."""
+    _, ex = np.frexp(np.abs(x))
+    return np.ldexp(1.0, np.maximum(ex - 1, -126) - 7)
+
+
+def check_rounded(stored: np.ndarray, exact: np.ndarray, fp32_rel: float = 4e-6):
+    """A bfloat16 store of a float32 result: either the round-to-nearest of
+    the exact value, or its neighbour when the exact value lies within the
+    float32 computation error of a rounding midpoint."""
+    bound = 0.5 * bf16_spacing(exact) + fp32_rel * np.abs(exact)
+    err = np.abs(stored - exact)
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} stored values off by more than half a bf16 step; "
+                           f"worst {float(err.max()):.3g}")
+    exact_rne = O.round_to_bf16(exact)
+    return float(np.mean(stored != exact_rne))
+
+
+def gates(o_gpu, o_ref, v_mean_dev, tol_abs, tol_rel=1e-4, label=""):
+    """The parity gates on o: max abs error <= tol_abs; relative-to-max error
+    <= tol_rel; and the error under 1% of the distance to the trivial
+    'uniform attention' answer (so a kernel that drops pages cannot pass)."""
+    e_abs = O.max_abs_err(o_gpu, o_ref)
+    e_rel = O.rel_to_max_err(o_gpu, o_ref)
+    assert np.all(np.isfinite(o_gpu)), f"{label}: non-finite output"
+    assert e_abs <= tol_abs, f"{label}: max abs err {e_abs:.3g} > {tol_abs}"
+    assert e_rel <= tol_rel, f"{label}: max rel-to-max err {e_rel:.3g} > {tol_rel}"
+    if v_mean_dev is not None and v_mean_dev > 0:
+        assert e_abs <= 0.01 * v_mean_dev, \
+            f"{label}: err {e_abs:.3g} not under 1% of distance to uniform ({v_mean_dev:.3g})"
+    return e_abs, e_rel
+
+
+def distance_to_uniform(o_ref, snap, cache_dtype):
+    """max |o_ref - mean_s v| over the sampled sequences and heads."""
+    worst = 0.0
+    for i in range(o_ref.shape[0]):
+        n = int(snap["seq_lens"][i])
+        v = O.gather_sequence(snap["v_pool"], snap["block_table"][i], n, cache_dtype)
+        mean = v.mean(axis=0)                                 # [8,128]
+        for h in range(16):
+            worst = max(worst, float(np.max(np.abs(o_ref[i, h] - mean[h // 2]))))
+    return worst

@@ -1,0 +1,193 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/dah.h declares, and rejects bad host-visible arguments with the
+documented status before touching the GPU.  The split planner is pure host
+code and is checked here too.  No kernel is launched by these tests.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dah.h")
+
+native = pytest.importorskip("decode_attention_head_amd._native")
+
+
+def _lib():
+    if not os.path.exists(native.LIB_PATH):
+        pytest.fail("libdah.so is not built: run `python -m decode_attention_head_amd.build`")
+    return native.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_entry_points():
+    decl = _declared_functions()
+    for name in ("qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step"):
+        assert name in decl
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libdah.so does not export {name}"
+    assert sorted(native.SIGNATURES) == _declared_functions()
+
+
+def test_header_constants_match_spec_fixture():
+    import json
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (DAH_\w+) (\d+)", text))
+    with open(os.path.join(ROOT, "tests", "golden", "qwen3_0_6b_constants.json")) as f:
+        c = json.load(f)
+    assert int(consts["DAH_NUM_HEADS"]) == c["num_attention_heads"]["value"]
+    assert int(consts["DAH_NUM_KV_HEADS"]) == c["num_key_value_heads"]["value"]
+    assert int(consts["DAH_HEAD_DIM"]) == c["head_dim"]["value"]
+    assert int(consts["DAH_PAGE_SIZE"]) == c["page_size"]["value"]
+
+
+def test_status_strings():
+    lib = _lib()
+    for code, name in native.STATUS_NAMES.items():
+        assert lib.dah_status_string(code).decode() == name
+    assert lib.dah_status_string(99).decode() == "unknown status"
+
+
+def _plan(B, L, n=0, cus=256):
+    lib = _lib()
+    s, p = ctypes.c_int(), ctypes.c_int()
+    st = lib.dah_plan_splits(B, L, n, cus, ctypes.byref(s), ctypes.byref(p))
+    return st, s.value, p.value
+
+
+@pytest.mark.parametrize("B,L", [(1, 1), (2, 12), (32, 4096), (256, 2048), (4, 40960),
+                                 (128, 16384), (256, 40960), (1, 17), (7, 999)])
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 7, 16, 1000])
+def test_planner_covers_every_page_with_no_empty_split(B, L, n):
+    st, splits, pps = _plan(B, L, n)
+    assert st == 0
+    pages = -(-L // 16)
+    assert splits >= 1 and pps >= 1
+    assert splits * pps >= pages            # every page of the longest sequence is covered
+    assert (splits - 1) * pps < pages       # the last split is not empty
+    if n > 0:
+        assert splits <= n
+    lib = _lib()
+    ws = lib.dah_workspace_bytes_for(B, L, n, 256)
+    assert ws == (0 if splits == 1 else B * 16 * splits * 130 * 4)
+
+
+def test_planner_choices_for_the_measured_shapes():
+    # enough waves for 256 compute units at B=256, S=2048, and many splits at B=4
+    assert _plan(256, 2048)[1:] == (2, 64)
+    st, splits, pps = _plan(4, 40960)
+    assert st == 0 and splits >= 64
+    assert _plan(2, 12)[1:] == (1, 1)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 10, 0, 256), 2), ((1, 0, 0, 256), 2), ((1, 10, -1, 256), 2), ((1, 10, 0, 0), 2),
+])
+def test_planner_rejects_bad_arguments(args, status):
+    lib = _lib()
+    s, p = ctypes.c_int(), ctypes.c_int()
+    assert lib.dah_plan_splits(*args, ctypes.byref(s), ctypes.byref(p)) == status
+    assert lib.dah_last_error().decode() != ""
+
+
+# Fake, aligned addresses: every call below must fail validation before any
+# pointer is used, so nothing is dereferenced.
+A = 0x100000
+
+
+def _decode(**kw):
+    lib = _lib()
+    a = dict(q=A, k=A, v=A, dt=1, num_pages=16, bt=A, mpps=4, sl=A, B=2, max_len=64, ns=0, o=A,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.paged_decode_gqa(a["q"], a["k"], a["v"], a["dt"], a["num_pages"], a["bt"], a["mpps"],
+                                a["sl"], a["B"], a["max_len"], a["ns"], a["o"], a["ws"],
+                                a["ws_bytes"], a["stream"])
+
+
+def _append(**kw):
+    lib = _lib()
+    a = dict(q=A, kn=A, vn=A, qg=A, kg=A, eps=1e-6, theta=1e6, k=A, v=A, dt=1, num_pages=16,
+             bt=A, mpps=4, sl=A, B=2, qo=A, stream=None)
+    a.update(kw)
+    return lib.qk_norm_rope_append(a["q"], a["kn"], a["vn"], a["qg"], a["kg"], a["eps"], a["theta"],
+                                   a["k"], a["v"], a["dt"], a["num_pages"], a["bt"], a["mpps"],
+                                   a["sl"], a["B"], a["qo"], a["stream"])
+
+
+def _step(**kw):
+    lib = _lib()
+    a = dict(q=A, kn=A, vn=A, qg=A, kg=A, eps=1e-6, theta=1e6, k=A, v=A, dt=1, num_pages=16,
+             bt=A, mpps=4, sl=A, B=2, max_len=64, ns=0, qo=A, o=A, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib.decode_attn_step(a["q"], a["kn"], a["vn"], a["qg"], a["kg"], a["eps"], a["theta"],
+                                a["k"], a["v"], a["dt"], a["num_pages"], a["bt"], a["mpps"],
+                                a["sl"], a["B"], a["max_len"], a["ns"], a["qo"], a["o"], a["ws"],
+                                a["ws_bytes"], a["stream"])
+
+
+BAD_DECODE = [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(bt=None), 1),
+    (dict(sl=None), 1), (dict(o=None), 1),
+    (dict(dt=2), 3), (dict(dt=-1), 3),
+    (dict(B=0), 2), (dict(B=-5), 2), (dict(num_pages=0), 2), (dict(num_pages=2 ** 31), 2),
+    (dict(mpps=0), 2), (dict(max_len=0), 2), (dict(max_len=65), 2), (dict(ns=-1), 2),
+    (dict(q=A + 4), 4), (dict(o=A + 8), 4), (dict(k=A + 2), 4), (dict(bt=A + 2), 4),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_DECODE)
+def test_paged_decode_rejects(kw, status):
+    assert _decode(**kw) == status
+    assert _lib().dah_last_error().decode() != ""
+
+
+BAD_APPEND = [
+    (dict(q=None), 1), (dict(kn=None), 1), (dict(vn=None), 1), (dict(qg=None), 1),
+    (dict(kg=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(bt=None), 1),
+    (dict(sl=None), 1), (dict(qo=None), 1),
+    (dict(dt=7), 3), (dict(B=0), 2), (dict(num_pages=0), 2), (dict(mpps=0), 2),
+    (dict(eps=-1.0), 2), (dict(theta=0.0), 2), (dict(eps=float("nan")), 2),
+    (dict(q=A + 4), 4), (dict(qo=A + 4), 4), (dict(kn=A + 8), 4), (dict(v=A + 2), 4),
+    (dict(sl=A + 1), 4),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_APPEND)
+def test_append_rejects(kw, status):
+    assert _append(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", BAD_APPEND + [(dict(max_len=65), 2), (dict(o=None), 1),
+                                                    (dict(ns=-2), 2), (dict(max_len=0), 2)])
+def test_step_rejects(kw, status):
+    assert _step(**kw) == status
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="valid arguments would launch on a real GPU")
+def test_valid_arguments_without_gpu_report_hip_error():
+    # With no GPU the call passes validation and fails on the device query.
+    assert _decode() == 6
+    assert "hip" in _lib().dah_last_error().decode().lower() or _lib().dah_last_error()
+    assert _lib().dah_workspace_bytes(2, 64, 0) == 0

@@ -1,0 +1,286 @@
+"""GPU checks of properties the pages state, on the HIP path through the C ABI:
+
+  * flash decoding equals the spec for any split (theorem flashAttn_eq,
+    "Supported models" page, "Facts proved about the specs"): results for
+    forced split counts agree with each other and with the oracle;
+  * causality / locality (forward_causal, attnHead_local): cache entries at or
+    past seq_len, and unused pages, never influence o, even as NaN;
+  * one cached position gives o = v; identical keys give the mean of v
+    (attnWeights_distribution);
+  * KV head j reaches only query heads 2j and 2j+1 (nnterp qwen3 page,
+    "The Notes");
+  * batch independence, idempotent re-append, the defined results for
+    out-of-domain device values, and the workspace check;
+  * edge shapes: B = 1, seq_len 1, 15, 16, 17, page-aligned and ragged
+    tails, and the domain's maximum (B = 256, S = 40,960) on sampled outputs.
+"""
+import numpy as np
+import pytest
+
+from dah_testlib import (build_layer, cuda_available, gates, host_snapshot, oracle_decode,
+                         oracle_step, sample_batch)
+from inputs import workloads as W
+from oracle import decode_attention as O
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not cuda_available(), reason="needs a GPU")]
+
+
+def _dah():
+    import decode_attention_head_amd as dah
+    return dah
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _custom(batch, lens, dtype="bf16", pool_pages=None, seed=11, outlier=None):
+    return W.Workload(f"custom_{seed}", batch=batch, cache_dtype=dtype, seed=seed,
+                      lens_kind="list", lens_args=tuple(int(x) for x in lens),
+                      pool_pages=pool_pages, key_outlier=outlier)
+
+
+def _decode(t, L, **kw):
+    dah = _dah()
+    return dah.paged_decode_gqa(t["q"], t["k_pool"], t["v_pool"], t["block_table"],
+                                t["seq_lens"], L, **kw)
+
+
+def test_split_count_invariance():
+    import torch
+    lens = [1, 15, 16, 17, 100, 257, 1024, 3000, 4096, 513]
+    w = _custom(len(lens), lens, seed=21)
+    _print("[splits] building")
+    t, seq_lens, table, _ = build_layer(w)
+    snap = host_snapshot(t, seq_lens, table, range(len(lens)))
+    ref = oracle_decode(snap, "bf16")
+    L = int(max(lens))
+    outs = {}
+    for n in (1, 2, 3, 7, 16, 64, 256):
+        _print(f"[splits] num_splits={n}")
+        o = _decode(t, L, num_splits=n)
+        torch.cuda.synchronize()
+        outs[n] = o.cpu().numpy().astype(np.float64)
+        gates(outs[n], ref, None, 2e-2, label=f"splits={n}")
+    base = outs[1]
+    for n, o in outs.items():
+        assert np.max(np.abs(o - base)) <= 1e-6, f"splits={n} differs from 1 split"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nan_poison_outside_prefix(dtype):
+    import torch
+    lens = [1, 7, 16, 17, 31, 33, 200]
+    w = _custom(len(lens), lens, dtype=dtype, pool_pages=64, seed=22)
+    t, seq_lens, table, _ = build_layer(w)
+    L = int(max(lens))
+    clean = {n: _decode(t, L, num_splits=n).clone() for n in (1, 3)}
+    W.poison_unused(t, seq_lens, table, value=float("nan"))
+    for n in (1, 3):
+        poisoned = _decode(t, L, num_splits=n)
+        torch.cuda.synchronize()
+        assert torch.equal(poisoned, clean[n]), f"poisoned tail changed o (splits={n})"
+    W.poison_unused(t, seq_lens, table, value=float("inf"))
+    assert torch.equal(_decode(t, L, num_splits=1), clean[1])
+
+
+def test_step_into_poisoned_slot():
+    """The step writes the new token over a NaN slot and reads only what it wrote."""
+    import torch
+    dah = _dah()
+    lens = [1, 2, 16, 17, 40]
+    w = _custom(len(lens), lens, dtype="bf16", pool_pages=32, seed=23)
+    t, seq_lens, table, _ = build_layer(w)
+    snap = host_snapshot(t, seq_lens, table, range(len(lens)))
+    W.poison_unused(t, seq_lens, table, include_new_slot=True)
+    q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    int(max(lens)))
+    torch.cuda.synchronize()
+    ref = oracle_step(snap, "bf16")
+    gates(o.cpu().numpy().astype(np.float64), ref["o"], None, 2e-2, label="poisoned step")
+
+
+def test_single_position_returns_v_exactly():
+    import torch
+    lens = [1] * 9
+    w = _custom(9, lens, dtype="f32", pool_pages=16, seed=24)
+    t, seq_lens, table, _ = build_layer(w)
+    o = _decode(t, 1)
+    torch.cuda.synchronize()
+    for b in range(9):
+        page = int(table[b, 0])
+        for h in range(16):
+            assert torch.equal(o[b, h], t["v_pool"][page, h // 2, 0]), (b, h)
+
+
+def test_identical_keys_give_mean_of_v():
+    import torch
+    lens = [100, 2048, 777]
+    w = _custom(3, lens, dtype="bf16", seed=25)
+    t, seq_lens, table, _ = build_layer(w)
+    t["k_pool"][:] = t["k_pool"][0, :, 0:1, :]           # every position holds the same keys
+    snap = host_snapshot(t, seq_lens, table, range(3))
+    o = _decode(t, max(lens), num_splits=4)
+    torch.cuda.synchronize()
+    for i in range(3):
+        v = O.gather_sequence(snap["v_pool"], snap["block_table"][i], lens[i], "bf16")
+        mean = v.mean(axis=0)
+        for h in range(16):
+            assert np.max(np.abs(o[i, h].cpu().numpy() - mean[h // 2])) <= 2e-6
+
+
+def test_head_mapping():
+    import torch
+    lens = [300, 45]
+    w = _custom(2, lens, dtype="bf16", seed=26)
+    t, seq_lens, table, _ = build_layer(w)
+    base = _decode(t, 300).clone()
+    for j in (0, 3, 7):
+        vp = t["v_pool"].clone()
+        t["v_pool"][:, j] *= 2.0
+        o = _decode(t, 300)
+        torch.cuda.synchronize()
+        diff = (o != base).any(dim=2).cpu().numpy()           # [B,16]
+        assert set(np.nonzero(diff.any(axis=0))[0]) == {2 * j, 2 * j + 1}
+        assert torch.equal(o[:, 2 * j:2 * j + 2], 2.0 * base[:, 2 * j:2 * j + 2])
+        t["v_pool"] = vp
+
+
+def test_batch_permutation():
+    import torch
+    lens = [5, 600, 1234, 16, 4000, 33]
+    w = _custom(len(lens), lens, dtype="bf16", seed=27)
+    t, seq_lens, table, _ = build_layer(w)
+    L = max(lens)
+    o = _decode(t, L, num_splits=1)
+    perm = torch.tensor([3, 0, 5, 1, 4, 2], device="cuda")
+    t2 = dict(t)
+    t2["q"] = t["q"][perm].contiguous()
+    t2["block_table"] = t["block_table"][perm].contiguous()
+    t2["seq_lens"] = t["seq_lens"][perm].contiguous()
+    o2 = _decode(t2, L, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o[perm])
+
+
+def test_step_is_idempotent():
+    import torch
+    dah = _dah()
+    lens = [9, 64, 65, 1000]
+    w = _custom(4, lens, dtype="bf16", seed=28)
+    t, seq_lens, table, _ = build_layer(w)
+    args = (t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"], t["k_pool"], t["v_pool"],
+            t["block_table"], t["seq_lens"], 1000)
+    q1, o1 = dah.decode_attn_step(*args)
+    k1, v1 = t["k_pool"].clone(), t["v_pool"].clone()
+    q2, o2 = dah.decode_attn_step(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(o1, o2)
+    assert torch.equal(k1, t["k_pool"]) and torch.equal(v1, t["v_pool"])
+
+
+def test_append_touches_only_the_new_slot():
+    import torch
+    dah = _dah()
+    lens = [3, 16, 17, 48]
+    w = _custom(4, lens, dtype="bf16", pool_pages=16, seed=29)
+    t, seq_lens, table, _ = build_layer(w)
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    dah.qk_norm_rope_append(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                            t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"])
+    torch.cuda.synchronize()
+    changed = (t["k_pool"] != k0).any(dim=3) | (t["v_pool"] != v0).any(dim=3)   # [P,8,16]
+    want = torch.zeros_like(changed)
+    for b, n in enumerate(lens):
+        want[int(table[b, (n - 1) // 16]), :, (n - 1) % 16] = True
+    assert torch.equal(changed, want)
+
+
+def test_out_of_domain_device_values():
+    """seq_len <= 0: o = 0 and no append; seq_len > max_seq_len or a page id
+    outside the pool: o = NaN and no append.  No fault in any case."""
+    import torch
+    dah = _dah()
+    lens = [20, 20, 20, 20, 20]
+    w = _custom(5, lens, dtype="bf16", pool_pages=16, seed=30)
+    t, seq_lens, table, num_pages = build_layer(w)
+    sl = t["seq_lens"]
+    sl[1] = 0
+    sl[2] = -3
+    sl[3] = 33                       # above max_seq_len = 32 below
+    t["block_table"][4, 1] = num_pages + 5
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    for n in (1, 2):
+        q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                        t["k_pool"], t["v_pool"], t["block_table"], sl, 32,
+                                        num_splits=n)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o[0]).all()
+        assert torch.equal(o[1], torch.zeros_like(o[1])) and torch.equal(o[2], torch.zeros_like(o[2]))
+        assert torch.isnan(o[3]).all() and torch.isnan(o[4]).all()
+    # only sequence 0's slot may have changed
+    changed = (t["k_pool"] != k0).any(dim=3) | (t["v_pool"] != v0).any(dim=3)
+    assert int(changed.sum()) == 8 and bool(changed[int(table[0, 1]), :, 3].all())
+
+
+def test_workspace_too_small_is_rejected():
+    import torch
+    dah = _dah()
+    lens = [4096] * 4
+    w = _custom(4, lens, dtype="bf16", seed=31)
+    t, seq_lens, table, _ = build_layer(w)
+    need = dah.workspace_bytes(4, 4096)
+    assert need > 0
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dah.DahError) as e:
+        _decode(t, 4096, workspace=small)
+    assert e.value.status == 5
+
+
+def test_large_gain_peaked_softmax():
+    """Gains of the trained model's magnitude (k_norm up to 96.5, q_norm up to
+    11.8, nnterp qwen3 page) give scores of O(1e3) and a sharply peaked
+    softmax; a sink key at position 0 aligned with the query."""
+    import torch
+    dah = _dah()
+    lens = [2048, 517, 40]
+    w = _custom(3, lens, dtype="bf16", seed=32)
+    t, seq_lens, table, _ = build_layer(w)
+    t["q_gain"] *= 11.8
+    t["k_gain"] *= 96.5
+    # a sink at position 0: the key equals a scaled copy of the (normed) query direction
+    for b in range(3):
+        p0 = int(table[b, 0])
+        t["k_pool"][p0, :, 0, :] = (t["q"][b, ::2, :] * 4.0).to(torch.bfloat16)
+    snap = host_snapshot(t, seq_lens, table, range(3))
+    for n in (1, 5):
+        k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+        q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                        t["k_pool"], t["v_pool"], t["block_table"],
+                                        t["seq_lens"], 2048, num_splits=n)
+        torch.cuda.synchronize()
+        ref = oracle_step(snap, "bf16")
+        e_abs, e_rel = gates(o.cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
+                             tol_rel=5e-4, label=f"large gains splits={n}")
+        _print(f"  large gains splits={n}: max abs {e_abs:.3g} rel {e_rel:.3g}")
+        t["k_pool"], t["v_pool"] = k0, v0
+
+
+def test_domain_maximum_sampled():
+    """B = 256 sequences of S = 40,960 positions (the shape domain's corners,
+    "At a glance"), checked on sampled sequences."""
+    import torch
+    w = W.Workload("max_b256_s40960", batch=256, cache_dtype="bf16", seed=33,
+                   lens_kind="fixed", lens_args=(40960,))
+    _print("[max] building 256 x 40960")
+    t, seq_lens, table, _ = build_layer(w)
+    sample = sample_batch(seq_lens, 3, seed=5)
+    snap = host_snapshot(t, seq_lens, table, sample)
+    o = _decode(t, 40960)
+    torch.cuda.synchronize()
+    ref = oracle_decode(snap, "bf16")
+    e_abs, e_rel = gates(o[sample].cpu().numpy().astype(np.float64), ref, None, 2e-2, label="max")
+    _print(f"  max shape: max abs {e_abs:.3g} rel {e_rel:.3g}")
+    assert torch.isfinite(o).all()
