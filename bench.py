@@ -49,6 +49,9 @@ def parse():
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time paged_decode_gqa alone (profiling aid)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after timing, run 3 plain device copies of this many MiB (a kernel of "
+                         "known traffic, to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -161,6 +164,15 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
     decode_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+
+    if args.copy_probe > 0:
+        from decode_attention_head_amd.probes import probe_copy
+        src = torch.ones(args.copy_probe * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            probe_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     kv_bytes = W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9

@@ -9,6 +9,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdah.so")
+PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdah_probe.so")
 
 DAH_F32 = 0
 DAH_BF16 = 1
@@ -38,7 +39,14 @@ SIGNATURES = {
     "dah_last_error": (ctypes.c_char_p, []),
 }
 
+# include/dah_probe.h (benchmark probes, separate library)
+PROBE_SIGNATURES = {
+    "dah_probe_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
+    "dah_probe_read": (_c_int, [_vp, _c_size, _vp, _c_int, _vp]),
+}
+
 _LIB = None
+_PROBE_LIB = None
 
 
 class DahError(RuntimeError):
@@ -62,6 +70,22 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
         _LIB = handle
     return _LIB
+
+
+def probe_lib() -> ctypes.CDLL:
+    """The benchmark's memory-probe library (loaded once)."""
+    global _PROBE_LIB
+    if _PROBE_LIB is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise ImportError(f"{PROBE_LIB_PATH} is missing: build it with "
+                              "`python -m decode_attention_head_amd.build`")
+        handle = ctypes.CDLL(PROBE_LIB_PATH)
+        for name, (res, args) in PROBE_SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _PROBE_LIB = handle
+    return _PROBE_LIB
 
 
 def check(status: int, where: str) -> None:

@@ -17,8 +17,13 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libdah.so")
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libdah_probe.so")
 
-SOURCES = ["dah_kernels.hip", "dah_host.cpp"]
+# (output, sources): the attention library and the benchmark's memory probes
+TARGETS = [
+    (LIB_PATH, ["dah_kernels.hip", "dah_host.cpp"]),
+    (PROBE_LIB_PATH, ["dah_probe.hip"]),
+]
 
 # Packed FP32 instructions are disabled for all device code (the compiler
 # would otherwise form v_pk_* from float code).
@@ -36,9 +41,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def build(verbose: bool = False) -> str:
+def _compile(out: str, sources: list, verbose: bool) -> None:
     cmd = [hipcc(), *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB_PATH + ".tmp"]
+           *[os.path.join(CSRC, s) for s in sources], "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -48,7 +53,12 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs))
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False) -> str:
+    for out, sources in TARGETS:
+        _compile(out, sources, verbose)
     return LIB_PATH
 
 

@@ -14,11 +14,14 @@ thread_local char g_last_error[512] = "";
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Target resident waves per compute unit (4 SIMDs x 4 waves) and the
-// shortest split worth a launch slot; both from measurements of the decode
-// kernel on MI355X.
-constexpr int kTargetWavesPerCu = 16;
+// Split policy, from split-count sweeps of the decode kernel on MI355X
+// (256 compute units): aim for 8 resident waves per compute unit (2 per
+// SIMD: the kernel's register use allows 3), never cut a split below 4
+// pages, and never leave a split longer than 128 pages, so that a batch
+// whose lengths are ragged still spreads its longest sequences.
+constexpr int kTargetWavesPerCu = 8;
 constexpr int kMinPagesPerSplit = 4;
+constexpr int kMaxPagesPerSplit = 128;
 }  // namespace
 
 int set_error(int status, const char* fmt, ...) {
@@ -60,6 +63,8 @@ int plan_splits(int B, int max_seq_len, int num_splits, int num_cus, Plan* out) 
     long long cap = max_pages / kMinPagesPerSplit;
     if (cap < 1) cap = 1;
     if (w > cap) w = cap;
+    const long long floor_splits = (max_pages + kMaxPagesPerSplit - 1) / kMaxPagesPerSplit;
+    if (w < floor_splits) w = floor_splits;
     want = static_cast<int>(w < 1 ? 1 : w);
   }
   if (want > max_pages) want = max_pages;

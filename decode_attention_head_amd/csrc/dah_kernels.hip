@@ -37,7 +37,7 @@ using dah::kKvHeads;
 using dah::kPage;
 
 constexpr int kWave = 64;
-constexpr int kDecodeWavesPerBlock = 4;
+constexpr int kDecodeWavesPerBlock = 8;  // the 8 KV heads of one (sequence, split)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------ lane utilities

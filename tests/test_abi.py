@@ -21,8 +21,8 @@ def _lib():
     return native.lib()
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("if", "defined")))
@@ -39,6 +39,28 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), f"libdah.so does not export {name}"
     assert sorted(native.SIGNATURES) == _declared_functions()
+
+
+def test_every_header_in_include_is_covered():
+    import glob
+    headers = sorted(os.path.basename(h) for h in glob.glob(os.path.join(ROOT, "include", "*.h")))
+    assert headers == ["dah.h", "dah_probe.h"]
+
+
+def test_probe_library_exports_every_declared_symbol():
+    if not os.path.exists(native.PROBE_LIB_PATH):
+        pytest.fail("libdah_probe.so is not built")
+    plib = native.probe_lib()
+    declared = _declared_functions(os.path.join(ROOT, "include", "dah_probe.h"))
+    assert sorted(native.PROBE_SIGNATURES) == declared
+    for name in declared:
+        assert hasattr(plib, name)
+    # argument checks happen before any launch
+    assert plib.dah_probe_copy(None, A, 16, None) == 1
+    assert plib.dah_probe_copy(A, A, 15, None) == 2
+    assert plib.dah_probe_copy(A + 4, A, 16, None) == 4
+    assert plib.dah_probe_read(A, 0, A, 1, None) == 2
+    assert plib.dah_probe_read(A, 16, A, 0, None) == 2
 
 
 def test_header_constants_match_spec_fixture():
@@ -85,11 +107,19 @@ def test_planner_covers_every_page_with_no_empty_split(B, L, n):
 
 
 def test_planner_choices_for_the_measured_shapes():
-    # enough waves for 256 compute units at B=256, S=2048, and many splits at B=4
-    assert _plan(256, 2048)[1:] == (2, 64)
-    st, splits, pps = _plan(4, 40960)
-    assert st == 0 and splits >= 64
+    # the split counts that measured fastest on MI355X (256 compute units)
+    assert _plan(256, 2048)[1:] == (1, 128)      # 2048 waves already fill the chip
+    assert _plan(32, 4096)[1:] == (8, 32)
+    assert _plan(4, 40960)[1:] == (64, 40)
+    assert _plan(128, 14464)[1:] == (8, 113)     # ragged batch: split the longest sequence
     assert _plan(2, 12)[1:] == (1, 1)
+
+
+def test_planner_never_leaves_long_splits():
+    for B in (1, 8, 64, 256):
+        for L in (2048, 4096, 16384, 40960):
+            st, splits, pps = _plan(B, L)
+            assert st == 0 and pps <= 128
 
 
 @pytest.mark.parametrize("args,status", [
@@ -191,3 +221,13 @@ def test_valid_arguments_without_gpu_report_hip_error():
     assert _decode() == 6
     assert "hip" in _lib().dah_last_error().decode().lower() or _lib().dah_last_error()
     assert _lib().dah_workspace_bytes(2, 64, 0) == 0
+
+
+def test_probe_wrappers_refuse_host_tensors():
+    torch = pytest.importorskip("torch")
+    from decode_attention_head_amd.probes import probe_copy, probe_read
+    a = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        probe_copy(a, a.clone())
+    with pytest.raises(ValueError):
+        probe_read(a, torch.zeros(4, dtype=torch.int32), 1)
