@@ -239,7 +239,10 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8], float sc
 template <int kDtype>
 __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int unit = blockIdx.x * kDecodeWavesPerBlock + (threadIdx.x >> 6);
+  // The wave index is uniform across the wave; saying so keeps everything
+  // derived from it (sequence, page range, page addresses) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * kDecodeWavesPerBlock + wave;
   const int g = unit & (kKvHeads - 1);
   const int bs = unit >> 3;  // b + B * split
   if (bs >= a.B * a.splits) return;
@@ -287,55 +290,76 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   A.init();
   Bs.init();
 
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages_per_seq;
-  const int64_t head_off = (int64_t)g * Tile<kDtype>::kTileBytes;
+  // The block table is read-only for the whole launch: reading it through the
+  // constant address space makes every (uniform) read a scalar load, counted
+  // apart from the vector loads of the cache tiles.
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+  const ConstI32 bt = (ConstI32)(a.block_table + (size_t)b * a.max_pages_per_seq);
+  const char* kbase = a.k_cache + (int64_t)g * Tile<kDtype>::kTileBytes;
+  const char* vbase = a.v_cache + (int64_t)g * Tile<kDtype>::kTileBytes;
   const int64_t page_bytes = (int64_t)kKvHeads * Tile<kDtype>::kTileBytes;
   const int tail = seq_len - (npages - 1) * kPage;  // valid slots in the sequence's last page
+  const int last = p1 - 1;                           // last page of this wave's range
+  const bool last_masked = (last == npages - 1) && tail < kPage;
   bool bad_page = false;
 
-  // Page ids for this wave's range: lane i holds the id of page p0 + 64t + i.
-  int chunk_base = p0;
-  int ids = (p0 + lane < p1) ? bt[p0 + lane] : 0;
-
-  auto page_offset = [&](int p) -> int64_t {
-    if (p - chunk_base >= kWave) {
-      chunk_base += kWave;
-      ids = (chunk_base + lane < p1) ? bt[chunk_base + lane] : 0;
-    }
-    int id = __builtin_amdgcn_readlane(ids, p - chunk_base);
+  // Physical page ids come from scalar loads issued two pages before the
+  // tile they address; an id is range-checked only when its tile is loaded.
+  // An id outside the pool is replaced by page 0 and flags the sequence (its
+  // output becomes NaN).
+  auto offset_of = [&](int id) -> int64_t {
     const bool ok = id >= 0 && id < a.num_pages;
     bad_page |= !ok;
-    id = ok ? id : 0;
-    return (int64_t)id * page_bytes + head_off;
+    return (int64_t)(ok ? id : 0) * page_bytes;
   };
 
+  // Software pipeline over the pages: the tile of page p+1 is in flight while
+  // page p is consumed.  In the steady-state loop both following pages exist,
+  // so every load is unconditional; the scheduling barriers keep each tile's
+  // eight loads together and ahead of the math on the other tile, so the wait
+  // before a tile covers only its own loads.  The last one or two pages (the
+  // only place a partial page can be) are finished after the loop.
   Tile<kDtype> K0, V0, K1, V1;
+  int id1 = bt[min(p0 + 1, last)];
+  int id2 = bt[min(p0 + 2, last)];
   {
-    const int64_t off = page_offset(p0);
-    K0.load(a.k_cache + off, lane);
-    V0.load(a.v_cache + off, lane);
+    const int64_t off0 = offset_of(bt[p0]);
+    K0.load(kbase + off0, lane);
+    V0.load(vbase + off0, lane);
   }
-  for (int p = p0; p < p1; p += 2) {
-    const bool has1 = p + 1 < p1;
-    if (has1) {
-      const int64_t off = page_offset(p + 1);
-      K1.load(a.k_cache + off, lane);
-      V1.load(a.v_cache + off, lane);
-    }
-    if (p == npages - 1 && tail < kPage)
-      attend_tile<kDtype, true>(K0, V0, qa, qb, A, Bs, row, tail);
-    else
-      attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
-    if (!has1) break;
-    if (p + 2 < p1) {
-      const int64_t off = page_offset(p + 2);
-      K0.load(a.k_cache + off, lane);
-      V0.load(a.v_cache + off, lane);
-    }
-    if (p + 1 == npages - 1 && tail < kPage)
+  int p = p0;
+  for (; p + 2 <= last; p += 2) {
+    const int64_t off1 = offset_of(id1);
+    K1.load(kbase + off1, lane);
+    V1.load(vbase + off1, lane);
+    const int id3 = bt[min(p + 3, last)];
+    __builtin_amdgcn_sched_barrier(0);
+    attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t off2 = offset_of(id2);
+    K0.load(kbase + off2, lane);
+    V0.load(vbase + off2, lane);
+    const int id4 = bt[min(p + 4, last)];
+    __builtin_amdgcn_sched_barrier(0);
+    attend_tile<kDtype, false>(K1, V1, qa, qb, A, Bs, row, kPage);
+    __builtin_amdgcn_sched_barrier(0);
+    id1 = id3;
+    id2 = id4;
+  }
+  if (p + 1 <= last) {
+    const int64_t off1 = offset_of(id1);
+    K1.load(kbase + off1, lane);
+    V1.load(vbase + off1, lane);
+    attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
+    if (last_masked)
       attend_tile<kDtype, true>(K1, V1, qa, qb, A, Bs, row, tail);
     else
       attend_tile<kDtype, false>(K1, V1, qa, qb, A, Bs, row, kPage);
+  } else {
+    if (last_masked)
+      attend_tile<kDtype, true>(K0, V0, qa, qb, A, Bs, row, tail);
+    else
+      attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
   }
 
   merge_rows(A);
@@ -367,7 +391,7 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(const float* __rest
                                                              int pages_per_split,
                                                              float* __restrict__ o) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (unit >= B * kHeads) return;
   const int b = unit / kHeads;
   const int seq_len = seq_lens[b];
@@ -448,7 +472,7 @@ template <int kDtype>
 __global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
   __shared__ float2 cs[64];
   const int b = blockIdx.x;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & (kWave - 1);
   const int seq_len = a.seq_lens[b];
   const int pos = seq_len >= 1 ? seq_len - 1 : 0;

@@ -1,0 +1,126 @@
+"""Condense rocprofv3 CSV output of the benchmark into the short text
+summaries kept under profiles/.
+
+    python -m decode_attention_head_amd.rocprof_summary trace DIR --out FILE --cmd "..."
+    python -m decode_attention_head_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \
+        --copy-mib 1024 --out FILE --cmd "..."
+
+`trace` lists per-kernel call counts and durations from a --kernel-trace
+--stats run.  `traffic` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
+two separate --pmc runs) into HBM bytes per decode launch, each counter
+scaled by what it reads for the probe copy kernel, whose traffic is known
+exactly (copy-mib MiB read and the same written).  The summary records a
+digest of the kernel source, so a reader can tell whether the counters
+still describe the current kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(PKG, "csrc", "dah_kernels.hip")
+DECODE_KERNEL = "decode_split_kernel"
+COPY_KERNEL = "probe_copy_kernel"
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _one(pattern: str) -> str:
+    hits = glob.glob(pattern, recursive=True)
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def _short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    return name if len(name) <= 70 else name[:67] + "..."
+
+
+def trace_summary(d: str) -> str:
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
+    out = [f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in rows:
+        out.append(f"{_short(r['Name']):70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                   f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                   f"{float(r['Percentage']):6.2f}")
+    return "\n".join(out)
+
+
+def _counter_means(d: str, counter: str):
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+    agg = collections.defaultdict(list)
+    for r in rows:
+        if r["Counter_Name"] == counter:
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def _pick(means: dict, key: str) -> float:
+    hits = [v for k, v in means.items() if key in k]
+    if len(hits) != 1:
+        raise ValueError(f"expected one kernel matching {key!r}, found {len(hits)}")
+    return hits[0]
+
+
+def traffic_summary(fetch_dir: str, write_dir: str, copy_mib: int) -> str:
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    f_scale = copy_kib / _pick(fetch, COPY_KERNEL)
+    w_scale = copy_kib / _pick(write, COPY_KERNEL)
+    d_fetch = _pick(fetch, DECODE_KERNEL)
+    d_write = _pick(write, DECODE_KERNEL)
+    hbm = (d_fetch * f_scale + d_write * w_scale) * 1024.0
+    lines = [
+        f"kernel_source_sha256_16: {source_digest()}",
+        f"copy_probe_bytes_each_way: {copy_mib * 1024 * 1024}",
+        f"copy_probe_FETCH_SIZE_KiB: {_pick(fetch, COPY_KERNEL):.3f}",
+        f"copy_probe_WRITE_SIZE_KiB: {_pick(write, COPY_KERNEL):.3f}",
+        f"fetch_scale: {f_scale:.6f}",
+        f"write_scale: {w_scale:.6f}",
+        f"decode_FETCH_SIZE_KiB_per_launch: {d_fetch:.3f}",
+        f"decode_WRITE_SIZE_KiB_per_launch: {d_write:.3f}",
+        f"decode_fetch_bytes_per_launch: {d_fetch * f_scale * 1024.0:.0f}",
+        f"decode_write_bytes_per_launch: {d_write * w_scale * 1024.0:.0f}",
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+    ]
+    return "\n".join(lines)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    c = sub.add_parser("traffic")
+    c.add_argument("fetch_dir")
+    c.add_argument("write_dir")
+    c.add_argument("--copy-mib", type=int, required=True)
+    for p in (t, c):
+        p.add_argument("--out", required=True)
+        p.add_argument("--cmd", action="append", default=[],
+                       help="command that produced the data (repeatable)")
+        p.add_argument("--note", default="")
+    a = ap.parse_args()
+    body = trace_summary(a.dir) if a.mode == "trace" else \
+        traffic_summary(a.fetch_dir, a.write_dir, a.copy_mib)
+    head = [f"# rocprofv3 {a.mode} summary"]
+    head += [f"# command: {c}" for c in a.cmd]
+    if a.note:
+        head.append(f"# {a.note}")
+    with open(a.out, "w") as f:
+        f.write("\n".join(head) + "\n" + body + "\n")
+    print(open(a.out).read())
+
+
+if __name__ == "__main__":
+    main()
