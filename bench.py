@@ -2,18 +2,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload b256_s2048]
 
-A step is one pass of the whole hot path over the batch: qk_norm + RoPE +
-cache append (qk_norm_rope_append), then split-S decodeGQA with its
-log-sum-exp combine (paged_decode_gqa) -- exactly the launches
-decode_attn_step issues, made as its two calls so that HIP events can
-bracket the decode launch.  Inputs are synthetic, seeded and resident in HBM
-before timing starts.
+A step is one pass of the whole hot path over the batch: one call of
+decode_attn_step (q/k RMSNorm, RoPE, cache append and split-S decodeGQA, in
+one kernel launch when one split suffices, plus the log-sum-exp combine
+otherwise).  HIP events recorded on the launch stream bracket every step.
+Inputs are synthetic, seeded and resident in HBM before timing starts.
 
 The JSON line reports
   value           KV-read throughput, GB/s = (sum of seq_lens * 4096 B) / step time
-  roofline        the decode launch (dominant kernel): algorithmic KV bytes per
-                  launch / its average duration measured with HIP events on the
-                  launch stream, against MI355X's 8 TB/s HBM peak
+  roofline        the step's decode kernel (dominant kernel): algorithmic KV
+                  bytes per launch / its average duration measured with HIP
+                  events on the launch stream, against MI355X's 8 TB/s HBM peak
   cpu_baseline    the float64 CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -135,19 +134,20 @@ def main():
     o = torch.empty_like(t["q"])
     stream = torch.cuda.current_stream(dev)
 
-    def append():
-        dah.qk_norm_rope_append(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
-                                t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
-                                q_out=q_out)
+    def step():
+        dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                             t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L,
+                             num_splits=args.num_splits, q_out=q_out, o=o, workspace=ws)
 
     def decode():
         dah.paged_decode_gqa(q_out, t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L,
                              num_splits=args.num_splits, o=o, workspace=ws)
 
+    run = decode if args.decode_only else step
+    if args.decode_only:
+        step()
     for _ in range(args.warmup):
-        if not args.decode_only:
-            append()
-        decode()
+        run()
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -155,15 +155,13 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if not args.decode_only:
-            append()
         starts[i].record(stream)
-        decode()
+        run()
         ends[i].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    decode_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    launch_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
 
     if args.copy_probe > 0:
         from decode_attention_head_amd.probes import probe_copy
@@ -176,7 +174,7 @@ def main():
 
     kv_bytes = W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
+    achieved = kv_bytes / (launch_ms * 1e-3) / 1e9
     traffic = read_traffic() if (w.name == "b256_s2048" and args.num_splits == 0) else None
 
     cpu = None
@@ -204,19 +202,20 @@ def main():
             "kv_bytes_per_step": kv_bytes,
             "splits": splits,
             "pages_per_split": pps,
-            "step": "decode only" if args.decode_only else "norm+rope+append, decode+combine",
+            "step": "paged_decode_gqa" if args.decode_only else "decode_attn_step",
         },
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(B / (ms_step * 1e-3), 1),
         "roofline": {
-            "kernel": "paged_decode_gqa (decode_split_kernel" + (" + combine)" if splits > 1 else ")"),
+            "kernel": ("decode_split_kernel" + ("" if args.decode_only else " (fused step)") +
+                       (" + combine_splits_kernel" if splits > 1 else "")),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "avg_launch_us": round(decode_ms * 1e3, 2),
+            "avg_launch_us": round(launch_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": kv_bytes,
         },
         "cpu_baseline": cpu,

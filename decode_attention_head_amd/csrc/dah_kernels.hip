@@ -28,6 +28,7 @@
 
 #include "dah.h"
 #include "dah_host.h"
+#include "dah_rope.h"
 
 namespace {
 
@@ -118,6 +119,47 @@ struct Tile<DAH_F32> {
   }
 };
 
+// Words of one cached position for one lane (8 dims) in the cache's dtype.
+template <int kDtype>
+struct SlotWords {
+  static constexpr int kWords = kDtype == DAH_BF16 ? 1 : 2;
+  u32x4 w[kWords];
+};
+
+template <int kDtype>
+__device__ __forceinline__ void unpack_slot(const SlotWords<kDtype>& s, float (&x)[8]) {
+  if constexpr (kDtype == DAH_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(s.w[0][i]);
+      x[2 * i + 1] = bf16_hi(s.w[0][i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = __uint_as_float(s.w[0][i]);
+      x[4 + i] = __uint_as_float(s.w[1][i]);
+    }
+  }
+}
+
+template <int kDtype>
+__device__ __forceinline__ SlotWords<kDtype> pack_slot(const float (&x)[8]) {
+  SlotWords<kDtype> s;
+  if constexpr (kDtype == DAH_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s.w[0][i] = (uint32_t)to_bf16(x[2 * i]) | ((uint32_t)to_bf16(x[2 * i + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s.w[0][i] = __float_as_uint(x[i]);
+      s.w[1][i] = __float_as_uint(x[4 + i]);
+    }
+  }
+  return s;
+}
+
 // Online-softmax state of one query head in one row of the wave: running
 // max (log2 units), running sum of weights, and this lane's 8 accumulators.
 struct HeadState {
@@ -193,6 +235,19 @@ __device__ __forceinline__ void attend_tile(const Tile<kDtype>& K, Tile<kDtype>&
   }
 }
 
+// Online-softmax update with one position (score s in log2 units, this
+// lane's 8 dims of v); rows that do not own the position pass s = -inf.
+__device__ __forceinline__ void attend_one(HeadState& st, float s, const float (&v)[8]) {
+  const float mn = fmaxf(st.m, s);
+  const float mu = mn == -INFINITY ? 0.0f : mn;
+  const float alpha = fast_exp2(st.m - mu);
+  const float p = fast_exp2(s - mu);
+  st.l = fmaf(st.l, alpha, p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.acc[e] = fmaf(p, v[e], st.acc[e] * alpha);
+  st.m = mn;
+}
+
 // Merge the four rows' states of a head; afterwards every row holds the total.
 __device__ __forceinline__ void merge_rows(HeadState& st) {
   float M = fmaxf(st.m, __shfl_xor(st.m, 16));
@@ -213,6 +268,60 @@ __device__ __forceinline__ void merge_rows(HeadState& st) {
   st.l = l;
 }
 
+// ---------------------------------------------------------- norm + RoPE, row layout
+//
+// In the decode layout lane (row r, column c) holds dims 8c..8c+7 of a head,
+// the same in all four rows.  The RoPE partner of dim i < 64 is dim i + 64,
+// held by column c + 8 of the same row, so pairs meet with one DPP rotation
+// of the row by 8 lanes.
+
+// cos/sin of pos * theta^(-2i/128) for this lane's eight pair indices
+// i = 8 (c mod 8) + e.  Each lane forms one of the 64 angles (dah_rope.h:
+// float64 angle, Cody-Waite reduction; a float32 angle at pos ~ 40,959 would
+// be off by ~4e-3 rad); shuffles hand every lane the eight it needs.
+__device__ __forceinline__ void rope_table(int pos, const dah::RopePowers& rp, int lane, int col,
+                                           float (&c)[8], float (&s)[8]) {
+  float cf, sf;
+  dah::rope_cos_sin((double)pos * dah::rope_inv_freq(lane, rp), &cf, &sf);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int src = 8 * (col & 7) + e;
+    c[e] = __shfl(cf, src);
+    s[e] = __shfl(sf, src);
+  }
+}
+
+// RMSNorm of one head held in the row layout (x / sqrt(sum x^2 / 128 + eps) * w,
+// the sum as a 16-lane DPP tree, which theorem rmsNormTiled_eq of the
+// "Supported models" page equates with the spec's sum), then the rotation of
+// the pairs (i, i + 64).
+__device__ __forceinline__ void norm_rope_row(float (&x)[8], const float (&w)[8], float eps,
+                                              const float (&c)[8], const float (&s)[8], int col) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+  ss = row_sum16(ss);
+  const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+  float y[8], partner[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * w[e];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)  // row_ror:8 -- column c reads column c +- 8
+    partner[e] = __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(y[e]), 0x128, 0xF, 0xF, false));
+  const bool upper = col >= 8;  // this lane holds dims i + 64
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    x[e] = upper ? partner[e] * s[e] + y[e] * c[e] : y[e] * c[e] - partner[e] * s[e];
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a0 = reinterpret_cast<const float4*>(p)[0];
+  const float4 a1 = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
+  v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+}
+
 struct DecodeArgs {
   const float* q;
   const char* k_cache;
@@ -228,6 +337,16 @@ struct DecodeArgs {
   float* o;         // written when splits == 1
   float* part_acc;  // [B][16][splits][128] when splits > 1
   float* part_ml;   // [B][16][splits][2]   when splits > 1
+  // The fused step only: q above is the raw (pre-norm) query.
+  const float* k_new;
+  const float* v_new;
+  const float* q_gain;
+  const float* k_gain;
+  float eps;
+  dah::RopePowers rope;
+  float* q_out;
+  char* k_cache_w;  // the pools again, writable (same addresses as k_cache / v_cache)
+  char* v_cache_w;
 };
 
 __device__ __forceinline__ void store8(float* dst, const float (&v)[8], float scale) {
@@ -236,7 +355,12 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8], float sc
   d[1] = make_float4(v[4] * scale, v[5] * scale, v[6] * scale, v[7] * scale);
 }
 
-template <int kDtype>
+// decodeGQA over one split of one sequence, for the 8 KV heads (one wave each).
+// kStep: the fused decode step -- q arrives raw and is normed and rotated here
+// (split 0 also writes q_out), and the workgroup holding the sequence's last
+// page norms and rotates the new key, stores the new key and value in the
+// cache and uses them for that slot directly from registers.
+template <int kDtype, bool kStep>
 __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   // The wave index is uniform across the wave; saying so keeps everything
@@ -244,7 +368,7 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * kDecodeWavesPerBlock + wave;
   const int g = unit & (kKvHeads - 1);
-  const int bs = unit >> 3;  // b + B * split
+  const int bs = unit >> 3;  // b + B * split, the same for the whole workgroup
   if (bs >= a.B * a.splits) return;
   const int b = bs % a.B;
   const int split = bs / a.B;
@@ -256,51 +380,40 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   const int npages = len_ok ? (seq_len + kPage - 1) / kPage : 0;
   const int p0 = split * a.pages_per_split;
   const int p1 = min(p0 + a.pages_per_split, npages);
+  const bool empty = p0 >= p1;
 
-  if (p0 >= p1) {
-    // Empty range.  With one split this is the whole sequence: o = 0 for
-    // seq_len <= 0, NaN for a length past max_seq_len.  With several splits
-    // the combine kernel reads only non-empty ranges.
+  // Empty range.  With one split this is the whole sequence: o = 0 for
+  // seq_len <= 0, NaN for a length past max_seq_len.  With several splits the
+  // combine kernel reads only non-empty ranges.  (In the fused step, split 0
+  // still has to write q_out first.)
+  auto fill_empty_output = [&]() {
     if (a.splits == 1 && row < 2) {
       const float fill = seq_len <= 0 ? 0.0f : NAN;
       const float z[8] = {fill, fill, fill, fill, fill, fill, fill, fill};
       store8(a.o + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col, z, 1.0f);
     }
+  };
+  if (empty && !(kStep && split == 0)) {
+    fill_empty_output();
     return;
   }
-
-  // Query rows 2g and 2g+1, this lane's 8 dims, pre-scaled by log2(e)/sqrt(128)
-  // so that scores come out in log2 units for exp2.
-  const float qscale = kLog2e * 0.08838834764831845f;  // 1/sqrt(128)
-  float qa[8], qb[8];
-  {
-    const float4* qp = reinterpret_cast<const float4*>(a.q + ((size_t)b * kHeads + 2 * g) * kHeadDim + 8 * col);
-    const float4 a0 = qp[0], a1 = qp[1];
-    const float4 b0 = qp[kHeadDim / 4], b1 = qp[kHeadDim / 4 + 1];
-    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qa[e] = av[e] * qscale;
-      qb[e] = bv[e] * qscale;
-    }
-  }
-
-  HeadState A, Bs;
-  A.init();
-  Bs.init();
 
   // The block table is read-only for the whole launch: reading it through the
   // constant address space makes every (uniform) read a scalar load, counted
   // apart from the vector loads of the cache tiles.
   typedef const __attribute__((address_space(4))) int32_t* ConstI32;
   const ConstI32 bt = (ConstI32)(a.block_table + (size_t)b * a.max_pages_per_seq);
-  const char* kbase = a.k_cache + (int64_t)g * Tile<kDtype>::kTileBytes;
-  const char* vbase = a.v_cache + (int64_t)g * Tile<kDtype>::kTileBytes;
   const int64_t page_bytes = (int64_t)kKvHeads * Tile<kDtype>::kTileBytes;
+  const int64_t head_bytes = (int64_t)g * Tile<kDtype>::kTileBytes;
+  const char* kbase = a.k_cache + head_bytes;
+  const char* vbase = a.v_cache + head_bytes;
   const int tail = seq_len - (npages - 1) * kPage;  // valid slots in the sequence's last page
   const int last = p1 - 1;                           // last page of this wave's range
-  const bool last_masked = (last == npages - 1) && tail < kPage;
+  // In the fused step the last page's final slot is the new token, which is
+  // taken from registers, so only tail - 1 of its slots are read from the cache.
+  const bool step_last = kStep && p1 == npages && !empty;
+  const int last_valid = step_last ? tail - 1 : tail;
+  const bool last_masked = (last == npages - 1) && last_valid < kPage;
   bool bad_page = false;
 
   // Physical page ids come from scalar loads issued two pages before the
@@ -313,20 +426,93 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
     return (int64_t)(ok ? id : 0) * page_bytes;
   };
 
+  // The small per-wave loads go first: vector loads complete in order, so the
+  // prologue's wait for them must not also wait for the first tile.
+  // Query rows 2g and 2g+1, this lane's 8 dims (raw in the fused step).
+  float qa[8], qb[8];
+  load8(a.q + ((size_t)b * kHeads + 2 * g) * kHeadDim + 8 * col, qa);
+  load8(a.q + ((size_t)b * kHeads + 2 * g + 1) * kHeadDim + 8 * col, qb);
+  const bool holds_last = step_last;
+  float qw[8], kx[8], vx[8], kw8[8];
+  if constexpr (kStep) {
+    load8(a.q_gain + 8 * col, qw);
+    if (holds_last) {
+      load8(a.k_new + ((size_t)b * kKvHeads + g) * kHeadDim + 8 * col, kx);
+      load8(a.v_new + ((size_t)b * kKvHeads + g) * kHeadDim + 8 * col, vx);
+      load8(a.k_gain + 8 * col, kw8);
+    }
+  }
+
+  // First tile in flight before the prologue's arithmetic.
+  Tile<kDtype> K0, V0, K1, V1;
+  int id1 = 0, id2 = 0;
+  if (!empty) {
+    id1 = bt[min(p0 + 1, last)];
+    id2 = bt[min(p0 + 2, last)];
+    const int64_t off0 = offset_of(bt[p0]);
+    K0.load(kbase + off0, lane);
+    V0.load(vbase + off0, lane);
+  }
+
+  // The fused step's outputs besides o -- q_out rows and the new token's key
+  // and value in the cache dtype -- wait in LDS (per wave, written and read
+  // by that wave only) and go to memory after the page loop: one counter
+  // tracks vector loads and stores in issue order, so a store issued early
+  // would hold up the waits for the first tiles.
+  __shared__ u32x4 stash[kDecodeWavesPerBlock][2][2][16];   // [wave][k|v][word][column]
+  __shared__ float4 qstash[kDecodeWavesPerBlock][2][2][16];  // [wave][head][half][column]
+  if constexpr (kStep) {
+    const int pos = seq_len >= 1 ? seq_len - 1 : 0;
+    float cr[8], sr[8];
+    rope_table(pos, a.rope, lane, col, cr, sr);
+    norm_rope_row(qa, qw, a.eps, cr, sr, col);
+    norm_rope_row(qb, qw, a.eps, cr, sr, col);
+    if (split == 0 && row < 2) {
+      const float (&q)[8] = row == 0 ? qa : qb;
+      qstash[wave][row][0][col] = make_float4(q[0], q[1], q[2], q[3]);
+      qstash[wave][row][1][col] = make_float4(q[4], q[5], q[6], q[7]);
+    }
+    if (empty) {
+      if (split == 0 && row < 2) {
+        float* qo = a.q_out + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col;
+        reinterpret_cast<float4*>(qo)[0] = qstash[wave][row][0][col];
+        reinterpret_cast<float4*>(qo)[1] = qstash[wave][row][1][col];
+      }
+      fill_empty_output();
+      return;
+    }
+    if (holds_last) {
+      norm_rope_row(kx, kw8, a.eps, cr, sr, col);
+      const SlotWords<kDtype> kw = pack_slot<kDtype>(kx);
+      const SlotWords<kDtype> vw = pack_slot<kDtype>(vx);
+      if (row == 0) {
+#pragma unroll
+        for (int i = 0; i < SlotWords<kDtype>::kWords; ++i) {
+          stash[wave][0][i][col] = kw.w[i];
+          stash[wave][1][i][col] = vw.w[i];
+        }
+      }
+    }
+  }
+  // Pre-scale by log2(e)/sqrt(128) so that scores come out in log2 units for exp2.
+  const float qscale = kLog2e * 0.08838834764831845f;  // 1/sqrt(128)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    qa[e] *= qscale;
+    qb[e] *= qscale;
+  }
+
+  HeadState A, Bs;
+  A.init();
+  Bs.init();
+
   // Software pipeline over the pages: the tile of page p+1 is in flight while
   // page p is consumed.  In the steady-state loop both following pages exist,
   // so every load is unconditional; the scheduling barriers keep each tile's
   // eight loads together and ahead of the math on the other tile, so the wait
   // before a tile covers only its own loads.  The last one or two pages (the
-  // only place a partial page can be) are finished after the loop.
-  Tile<kDtype> K0, V0, K1, V1;
-  int id1 = bt[min(p0 + 1, last)];
-  int id2 = bt[min(p0 + 2, last)];
-  {
-    const int64_t off0 = offset_of(bt[p0]);
-    K0.load(kbase + off0, lane);
-    V0.load(vbase + off0, lane);
-  }
+  // only place a partial page, or the new token, can be) are finished after
+  // the loop.
   int p = p0;
   for (; p + 2 <= last; p += 2) {
     const int64_t off1 = offset_of(id1);
@@ -350,16 +536,45 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
     const int64_t off1 = offset_of(id1);
     K1.load(kbase + off1, lane);
     V1.load(vbase + off1, lane);
+    __builtin_amdgcn_sched_barrier(0);
     attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
+    __builtin_amdgcn_sched_barrier(0);
     if (last_masked)
-      attend_tile<kDtype, true>(K1, V1, qa, qb, A, Bs, row, tail);
+      attend_tile<kDtype, true>(K1, V1, qa, qb, A, Bs, row, last_valid);
     else
       attend_tile<kDtype, false>(K1, V1, qa, qb, A, Bs, row, kPage);
   } else {
     if (last_masked)
-      attend_tile<kDtype, true>(K0, V0, qa, qb, A, Bs, row, tail);
+      attend_tile<kDtype, true>(K0, V0, qa, qb, A, Bs, row, last_valid);
     else
       attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
+  }
+  if constexpr (kStep) {
+    // The new token (slot tail - 1 of the last page, read from the cache
+    // above as masked) enters from the stash: the values just stored, in the
+    // cache's dtype, owned by the row of that slot.
+    if (holds_last) {
+      SlotWords<kDtype> kw, vw;
+#pragma unroll
+      for (int i = 0; i < SlotWords<kDtype>::kWords; ++i) {
+        kw.w[i] = stash[wave][0][i][col];
+        vw.w[i] = stash[wave][1][i][col];
+      }
+      float kf[8], vf[8];
+      unpack_slot<kDtype>(kw, kf);
+      unpack_slot<kDtype>(vw, vf);
+      float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sa = fmaf(qa[e], kf[e], sa);
+        sb = fmaf(qb[e], kf[e], sb);
+      }
+      sa = row_sum16(sa);
+      sb = row_sum16(sb);
+      const bool mine = row == ((tail - 1) & 3);
+      attend_one(A, mine ? sa : -INFINITY, vf);
+      attend_one(Bs, mine ? sb : -INFINITY, vf);
+    }
   }
 
   merge_rows(A);
@@ -378,6 +593,28 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
       const size_t part = ((size_t)b * kHeads + h) * a.splits + split;
       store8(a.part_acc + part * kHeadDim + 8 * col, st.acc, bad_page ? NAN : 1.0f);
       if (col == 0) reinterpret_cast<float2*>(a.part_ml)[part] = make_float2(st.m, st.l);
+    }
+  }
+  if constexpr (kStep) {
+    if (split == 0 && row < 2) {
+      float* qo = a.q_out + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col;
+      reinterpret_cast<float4*>(qo)[0] = qstash[wave][row][0][col];
+      reinterpret_cast<float4*>(qo)[1] = qstash[wave][row][1][col];
+    }
+    if (holds_last && row == 0) {
+      // The new token's slot: page block_table[b][npages-1], slot tail - 1.
+      const int id = bt[npages - 1];
+      if (id >= 0 && id < a.num_pages) {
+        const int64_t slot_off = (int64_t)id * page_bytes + head_bytes +
+                                 (int64_t)(tail - 1) * (Tile<kDtype>::kTileBytes / kPage);
+        u32x4* kd = reinterpret_cast<u32x4*>(a.k_cache_w + slot_off) + SlotWords<kDtype>::kWords * col;
+        u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache_w + slot_off) + SlotWords<kDtype>::kWords * col;
+#pragma unroll
+        for (int i = 0; i < SlotWords<kDtype>::kWords; ++i) {
+          kd[i] = stash[wave][0][i][col];
+          vd[i] = stash[wave][1][i][col];
+        }
+      }
     }
   }
 }
@@ -437,7 +674,7 @@ struct AppendArgs {
   const float* q_gain;
   const float* k_gain;
   float eps;
-  double log2_theta;
+  dah::RopePowers rope;
   char* k_cache;
   char* v_cache;
   int num_pages;
@@ -477,12 +714,11 @@ __global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
   const int seq_len = a.seq_lens[b];
   const int pos = seq_len >= 1 ? seq_len - 1 : 0;
   if (w == 0) {
-    // Angle pos * theta^(-2i/128) and its cos/sin in float64 (at pos near
-    // 40,960 a float32 angle would be off by ~4e-3 rad).
-    const double inv_freq = exp2(-(double)lane / 64.0 * a.log2_theta);
-    double sn, cn;
-    sincos((double)pos * inv_freq, &sn, &cn);
-    cs[lane] = make_float2((float)cn, (float)sn);
+    // cos/sin of pos * theta^(-2i/128), angle formed in float64 (at pos near
+    // 40,960 a float32 angle would be off by ~4e-3 rad); see dah_rope.h.
+    float cn, sn;
+    dah::rope_cos_sin((double)pos * dah::rope_inv_freq(lane, a.rope), &cn, &sn);
+    cs[lane] = make_float2(cn, sn);
   }
   // Load while wave 0 computes the angles.
   const size_t qbase0 = ((size_t)b * kHeads + w) * kHeadDim;
@@ -570,7 +806,7 @@ int launch_append(const float* q, const float* k_new, const float* v_new, const 
   a.q_gain = q_gain;
   a.k_gain = k_gain;
   a.eps = eps;
-  a.log2_theta = log2((double)rope_theta);
+  a.rope = dah::rope_powers((double)rope_theta);
   a.k_cache = static_cast<char*>(k_cache);
   a.v_cache = static_cast<char*>(v_cache);
   a.num_pages = static_cast<int>(num_pages);
@@ -586,26 +822,46 @@ int launch_append(const float* q, const float* k_new, const float* v_new, const 
   return check_launch("norm_rope_append_kernel");
 }
 
-int launch_decode(const float* q, const void* k_cache, const void* v_cache, int cache_dtype,
-                  int64_t num_pages, const int32_t* block_table, int max_pages_per_seq,
-                  const int32_t* seq_lens, int B, int max_seq_len, int num_splits, float* o,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// The extra inputs of the fused decode step.
+struct StepInputs {
+  const float* k_new;
+  const float* v_new;
+  const float* q_gain;
+  const float* k_gain;
+  float eps;
+  float rope_theta;
+  float* q_out;
+  void* k_cache;
+  void* v_cache;
+};
+
+int plan_for(int B, int max_seq_len, int num_splits, void* workspace, size_t workspace_bytes,
+             dah::Plan* plan) {
   int cus = 0;
   int st = device_cu_count(&cus);
   if (st != DAH_OK) return st;
-  dah::Plan plan;
-  st = dah::plan_splits(B, max_seq_len, num_splits, cus, &plan);
+  st = dah::plan_splits(B, max_seq_len, num_splits, cus, plan);
   if (st != DAH_OK) return st;
-  if (plan.workspace > 0) {
-    if (workspace == nullptr || workspace_bytes < plan.workspace)
+  if (plan->workspace > 0) {
+    if (workspace == nullptr || workspace_bytes < plan->workspace)
       return dah::set_error(DAH_ERR_WORKSPACE,
                             "workspace of %zu bytes, need %zu (B=%d, max_seq_len=%d, %d splits)",
-                            workspace == nullptr ? (size_t)0 : workspace_bytes, plan.workspace, B,
-                            max_seq_len, plan.splits);
+                            workspace == nullptr ? (size_t)0 : workspace_bytes, plan->workspace, B,
+                            max_seq_len, plan->splits);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return dah::set_error(DAH_ERR_ALIGN, "workspace needs 256-byte alignment");
   }
-  DecodeArgs a;
+  return DAH_OK;
+}
+
+// Decode (step == nullptr: q is already normed and roped) or the fused
+// decode step (q is raw; the kernel norms, rotates and appends).
+int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
+                  const void* v_cache, int cache_dtype, int64_t num_pages,
+                  const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
+                  int B, int max_seq_len, float* o, void* workspace, const StepInputs* step,
+                  hipStream_t stream) {
+  DecodeArgs a = {};
   a.q = q;
   a.k_cache = static_cast<const char*>(k_cache);
   a.v_cache = static_cast<const char*>(v_cache);
@@ -622,15 +878,34 @@ int launch_decode(const float* q, const void* k_cache, const void* v_cache, int 
   const size_t parts = (size_t)B * kHeads * plan.splits;
   a.part_acc = plan.splits > 1 ? ws : nullptr;
   a.part_ml = plan.splits > 1 ? ws + parts * kHeadDim : nullptr;
+  if (step != nullptr) {
+    a.k_new = step->k_new;
+    a.v_new = step->v_new;
+    a.q_gain = step->q_gain;
+    a.k_gain = step->k_gain;
+    a.eps = step->eps;
+    a.rope = dah::rope_powers((double)step->rope_theta);
+    a.q_out = step->q_out;
+    a.k_cache_w = static_cast<char*>(step->k_cache);
+    a.v_cache_w = static_cast<char*>(step->v_cache);
+  }
 
-  const long long waves = (long long)B * kKvHeads * plan.splits;
-  const long long blocks = (waves + kDecodeWavesPerBlock - 1) / kDecodeWavesPerBlock;
+  const long long blocks = (long long)B * plan.splits;  // one workgroup per (sequence, split)
   if (blocks > INT32_MAX) return dah::set_error(DAH_ERR_SHAPE, "grid too large");
-  if (cache_dtype == DAH_BF16)
-    decode_split_kernel<DAH_BF16><<<(unsigned)blocks, kWave * kDecodeWavesPerBlock, 0, stream>>>(a);
-  else
-    decode_split_kernel<DAH_F32><<<(unsigned)blocks, kWave * kDecodeWavesPerBlock, 0, stream>>>(a);
-  st = check_launch("decode_split_kernel");
+  const dim3 grid((unsigned)blocks), block(kWave * kDecodeWavesPerBlock);
+  const bool bf16 = cache_dtype == DAH_BF16;
+  if (step == nullptr) {
+    if (bf16)
+      decode_split_kernel<DAH_BF16, false><<<grid, block, 0, stream>>>(a);
+    else
+      decode_split_kernel<DAH_F32, false><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (bf16)
+      decode_split_kernel<DAH_BF16, true><<<grid, block, 0, stream>>>(a);
+    else
+      decode_split_kernel<DAH_F32, true><<<grid, block, 0, stream>>>(a);
+  }
+  int st = check_launch("decode_split_kernel");
   if (st != DAH_OK || plan.splits == 1) return st;
   const int cblocks = (B * kHeads + 3) / 4;
   combine_splits_kernel<<<cblocks, 256, 0, stream>>>(a.part_acc, a.part_ml, seq_lens, B,
@@ -666,9 +941,12 @@ int paged_decode_gqa(const float* q, const void* k_cache, const void* v_cache, i
   int st = dah::validate_decode(q, k_cache, v_cache, cache_dtype, num_pages, block_table,
                                 max_pages_per_seq, seq_lens, B, max_seq_len, num_splits, o);
   if (st != DAH_OK) return st;
-  return launch_decode(q, k_cache, v_cache, cache_dtype, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, B, max_seq_len, num_splits, o, workspace,
-                       workspace_bytes, static_cast<hipStream_t>(stream));
+  dah::Plan plan;
+  st = plan_for(B, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
+  if (st != DAH_OK) return st;
+  return launch_decode(plan, q, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                       max_pages_per_seq, seq_lens, B, max_seq_len, o, workspace, nullptr,
+                       static_cast<hipStream_t>(stream));
 }
 
 int decode_attn_step(const float* q, const float* k_new, const float* v_new,
@@ -685,27 +963,27 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
   st = dah::validate_decode(q_out, k_cache, v_cache, cache_dtype, num_pages, block_table,
                             max_pages_per_seq, seq_lens, B, max_seq_len, num_splits, o);
   if (st != DAH_OK) return st;
-  // Check the workspace before anything is launched, so that a failing call
-  // leaves the cache untouched.
-  int cus = 0;
-  st = device_cu_count(&cus);
-  if (st != DAH_OK) return st;
+  // Plan and check the workspace before anything is launched, so that a
+  // failing call leaves the cache untouched.
   dah::Plan plan;
-  st = dah::plan_splits(B, max_seq_len, num_splits, cus, &plan);
+  st = plan_for(B, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
   if (st != DAH_OK) return st;
-  if (plan.workspace > 0 && (workspace == nullptr || workspace_bytes < plan.workspace))
-    return dah::set_error(DAH_ERR_WORKSPACE, "workspace of %zu bytes, need %zu",
-                          workspace == nullptr ? (size_t)0 : workspace_bytes, plan.workspace);
-  if (plan.workspace > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return dah::set_error(DAH_ERR_ALIGN, "workspace needs 256-byte alignment");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launch_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
-                     cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
-                     max_seq_len, q_out, s);
-  if (st != DAH_OK) return st;
-  return launch_decode(q_out, k_cache, v_cache, cache_dtype, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, B, max_seq_len, num_splits, o, workspace,
-                       workspace_bytes, s);
+  if (q_out == q && plan.splits > 1) {
+    // In place with several splits: the workgroups of one sequence would read
+    // q while another overwrites it, so norm and rotate first, then decode.
+    st = launch_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
+                       cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
+                       max_seq_len, q_out, s);
+    if (st != DAH_OK) return st;
+    return launch_decode(plan, q_out, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                         max_pages_per_seq, seq_lens, B, max_seq_len, o, workspace, nullptr, s);
+  }
+  // One launch: the decode kernel norms and rotates q, writes q_out, and
+  // appends the new key and value (see decode_split_kernel).
+  const StepInputs step = {k_new, v_new, q_gain, k_gain, eps, rope_theta, q_out, k_cache, v_cache};
+  return launch_decode(plan, q, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                       max_pages_per_seq, seq_lens, B, max_seq_len, o, workspace, &step, s);
 }
 
 size_t dah_workspace_bytes(int B, int max_seq_len, int num_splits) {

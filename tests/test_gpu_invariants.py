@@ -284,3 +284,80 @@ def test_domain_maximum_sampled():
     e_abs, e_rel = gates(o[sample].cpu().numpy().astype(np.float64), ref, None, 2e-2, label="max")
     _print(f"  max shape: max abs {e_abs:.3g} rel {e_rel:.3g}")
     assert torch.isfinite(o).all()
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_step_in_place_query(splits):
+    """q_out may be q: the in-place call gives the same q_out, o and cache as
+    a call with a separate q_out."""
+    import torch
+    dah = _dah()
+    lens = [1, 16, 17, 250, 1000]
+    w = _custom(len(lens), lens, dtype="bf16", seed=34)
+    t, seq_lens, table, _ = build_layer(w)
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    q_sep, o_sep = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                        t["k_pool"], t["v_pool"], t["block_table"],
+                                        t["seq_lens"], 1000, num_splits=splits)
+    k1, v1 = t["k_pool"].clone(), t["v_pool"].clone()
+    t["k_pool"].copy_(k0)
+    t["v_pool"].copy_(v0)
+    q = t["q"].clone()
+    q_in, o_in = dah.decode_attn_step(q, t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                      t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                      1000, num_splits=splits, q_out=q)
+    torch.cuda.synchronize()
+    assert q_in.data_ptr() == q.data_ptr()
+    assert torch.allclose(q_in, q_sep, atol=1e-6, rtol=0)
+    assert torch.allclose(o_in, o_sep, atol=1e-6, rtol=0)
+    bf16_step = 2.0 ** -7 * t["k_pool"].float().abs().clamp(min=1e-30)
+    assert bool(((t["k_pool"].float() - k1.float()).abs() <= bf16_step).all())
+    assert torch.equal(t["v_pool"], v1)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_fused_step_matches_two_calls(splits):
+    """decode_attn_step (one fused launch) against qk_norm_rope_append followed
+    by paged_decode_gqa: same q_out and o to float32 rounding, same stored v,
+    stored k within one bf16 step (the two kernels sum the norm in different
+    orders, which may flip a rounding decision)."""
+    import torch
+    dah = _dah()
+    lens = [1, 2, 15, 16, 17, 33, 700, 2048]
+    w = _custom(len(lens), lens, dtype="bf16", seed=35)
+    t, seq_lens, table, _ = build_layer(w)
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    q_f, o_f = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    2048, num_splits=splits)
+    kf, vf = t["k_pool"].clone(), t["v_pool"].clone()
+    t["k_pool"].copy_(k0)
+    t["v_pool"].copy_(v0)
+    q_2 = dah.qk_norm_rope_append(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                  t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"])
+    o_2 = dah.paged_decode_gqa(q_2, t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                               2048, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.allclose(q_f, q_2, atol=2e-6, rtol=0)
+    assert torch.allclose(o_f, o_2, atol=2e-5, rtol=0)
+    assert torch.equal(vf, t["v_pool"])
+    step = 2.0 ** -7 * t["k_pool"].float().abs()
+    assert bool(((kf.float() - t["k_pool"].float()).abs() <= step).all())
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_step_touches_only_the_new_slot(splits):
+    import torch
+    dah = _dah()
+    lens = [1, 3, 16, 17, 48, 95]
+    w = _custom(len(lens), lens, dtype="bf16", pool_pages=24, seed=36)
+    t, seq_lens, table, _ = build_layer(w)
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"], t["k_pool"],
+                         t["v_pool"], t["block_table"], t["seq_lens"], 95, num_splits=splits)
+    torch.cuda.synchronize()
+    changed = (t["k_pool"] != k0).any(dim=3) | (t["v_pool"] != v0).any(dim=3)   # [P,8,16]
+    want = torch.zeros_like(changed)
+    for b, n in enumerate(lens):
+        want[int(table[b, (n - 1) // 16]), :, (n - 1) % 16] = True
+    assert torch.equal(changed, want)
