@@ -48,6 +48,8 @@ def parse():
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time paged_decode_gqa alone (profiling aid)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the streaming-read probe (practical bandwidth ceiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 plain device copies of this many MiB (a kernel of "
                          "known traffic, to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -172,6 +174,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    probe_gbs = None
+    if not args.no_read_probe:
+        # Practical ceiling: the K pool streamed by a plain non-temporal read
+        # kernel; the best of a few grid sizes.
+        from decode_attention_head_amd.probes import probe_read
+        src = t["k_pool"].view(torch.uint8).reshape(-1)
+        sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+        best = 0.0
+        for blocks in (512, 2048, 16384):
+            for _ in range(2):
+                probe_read(src, sink, blocks)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(10):
+                probe_read(src, sink, blocks)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            best = max(best, 10 * src.numel() / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9)
+        probe_gbs = round(best, 1)
+
     kv_bytes = W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (launch_ms * 1e-3) / 1e9
@@ -216,6 +238,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(launch_ms * 1e3, 2),
+            "probe_read_gbs": probe_gbs,
+            "frac_of_probe_read": None if not probe_gbs else round(achieved / probe_gbs, 4),
             "algorithmic_bytes_per_launch": kv_bytes,
         },
         "cpu_baseline": cpu,
