@@ -129,7 +129,7 @@ def main():
     t = W.make_layer(w, 0, dev, table=table, num_pages=num_pages, seq_lens=seq_lens)
     B = w.batch
     L = int(seq_lens.max())
-    splits, pps = dah.plan_splits(B, L, args.num_splits)
+    plan = dah.plan_decode(B, L, args.num_splits)
     ws_bytes = dah.workspace_bytes(B, L, args.num_splits)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     q_out = torch.empty_like(t["q"])
@@ -222,15 +222,15 @@ def main():
             "seq_len": "fixed 2048" if w.name == "b256_s2048" else f"max {L}",
             "heads": "16 q / 8 kv, D=128, page 16",
             "kv_bytes_per_step": kv_bytes,
-            "splits": splits,
-            "pages_per_split": pps,
+            "plan": plan["mode"],
+            "workgroups": plan["workgroups"],
             "step": "paged_decode_gqa" if args.decode_only else "decode_attn_step",
         },
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(B / (ms_step * 1e-3), 1),
         "roofline": {
             "kernel": ("decode_split_kernel" + ("" if args.decode_only else " (fused step)") +
-                       (" + combine_splits_kernel" if splits > 1 else "")),
+                       ("" if plan["mode"] == "per_sequence" else " + combine")),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

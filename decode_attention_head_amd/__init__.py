@@ -22,7 +22,7 @@ import ctypes
 from ._native import DAH_BF16, DAH_F32, DahError, LIB_PATH, check, lib
 
 __all__ = [
-    "qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step", "plan_splits",
+    "qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step", "plan_decode",
     "workspace_bytes", "DahError", "LIB_PATH", "NUM_HEADS", "NUM_KV_HEADS", "HEAD_DIM",
     "PAGE_SIZE",
 ]
@@ -89,16 +89,20 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def plan_splits(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | None = None):
-    """(splits, pages_per_split) the planner picks; num_cus defaults to the
-    current device's compute-unit count."""
+def plan_decode(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | None = None) -> dict:
+    """How the decode will cut the work (dah_plan_decode): a dict with mode
+    ("per_sequence", "split" or "balanced"), splits, pages_per_split,
+    workgroups and workspace_bytes.  num_cus defaults to the current device's
+    compute-unit count."""
+    from ._native import PLAN_MODES, DecodePlan
     if num_cus is None:
         torch = _torch()
         num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    s, p = ctypes.c_int(), ctypes.c_int()
-    check(lib().dah_plan_splits(B, max_seq_len, num_splits, num_cus, ctypes.byref(s),
-                                ctypes.byref(p)), "dah_plan_splits")
-    return s.value, p.value
+    p = DecodePlan()
+    check(lib().dah_plan_decode(B, max_seq_len, num_splits, num_cus, ctypes.byref(p)),
+          "dah_plan_decode")
+    return {"mode": PLAN_MODES[p.mode], "splits": p.splits, "pages_per_split": p.pages_per_split,
+            "workgroups": p.workgroups, "workspace_bytes": int(p.workspace_bytes)}
 
 
 def workspace_bytes(B: int, max_seq_len: int, num_splits: int = 0,

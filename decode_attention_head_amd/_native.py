@@ -31,8 +31,7 @@ SIGNATURES = {
     "decode_attn_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_float, _c_float, _vp, _vp, _c_int,
                                   _c_i64, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp,
                                   _c_size, _vp]),
-    "dah_plan_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
-                                 ctypes.POINTER(_c_int)]),
+    "dah_plan_decode": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.c_void_p]),
     "dah_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "dah_workspace_bytes_for": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "dah_status_string": (ctypes.c_char_p, [_c_int]),
@@ -47,6 +46,15 @@ PROBE_SIGNATURES = {
 
 _LIB = None
 _PROBE_LIB = None
+
+PLAN_MODES = {0: "per_sequence", 1: "split", 2: "balanced"}
+
+
+class DecodePlan(ctypes.Structure):
+    """dah_decode_plan of include/dah.h."""
+    _fields_ = [("mode", ctypes.c_int), ("splits", ctypes.c_int),
+                ("pages_per_split", ctypes.c_int), ("workgroups", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class DahError(RuntimeError):

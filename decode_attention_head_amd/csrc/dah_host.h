@@ -17,19 +17,20 @@ constexpr int kPage = 16;      // positions per cache page
 int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
+constexpr int kMaxBalancedBatch = 4096;  // sequences the balanced decode's LDS scan holds
+
 struct Plan {
-  int splits;           // split ranges per sequence
-  int pages_per_split;  // pages per split range
-  size_t workspace;     // bytes of partial results (0 when splits == 1)
+  int mode;             // dah_plan_mode
+  int splits;           // splits per sequence (1 per sequence, 0 balanced)
+  int pages_per_split;  // pages per split (0 balanced)
+  int grid_splits;      // DAH_PLAN_SPLIT: splits padded to a multiple of 8 for the XCD mapping
+  int workgroups;       // grid of the decode launch
+  size_t workspace;     // bytes of partial results
 };
 
-// Split planner: pure integer policy from the batch size, the longest
-// sequence and the compute-unit count.  Returns a dah_status.
-int plan_splits(int B, int max_seq_len, int num_splits, int num_cus, Plan* out);
-
-// Workspace bytes for a plan: per (sequence, query head, split) 128 floats of
-// weighted V plus (running max, sum).
-size_t workspace_bytes(int B, int splits);
+// Planner: pure integer policy from the batch size, the longest sequence and
+// the compute-unit count.  Returns a dah_status.
+int plan_decode(int B, int max_seq_len, int num_splits, int num_cus, Plan* out);
 
 int validate_append(const void* q, const void* k_new, const void* v_new, const void* q_gain,
                     const void* k_gain, float eps, float rope_theta, const void* k_cache,

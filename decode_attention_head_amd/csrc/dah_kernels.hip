@@ -39,6 +39,9 @@ using dah::kPage;
 
 constexpr int kWave = 64;
 constexpr int kDecodeWavesPerBlock = 8;  // the 8 KV heads of one (sequence, split)
+static_assert(dah::kMaxBalancedBatch == 8 * kWave * kDecodeWavesPerBlock,
+              "the balanced decode's scan gives each thread 8 sequences");
+using dah::kMaxBalancedBatch;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------ lane utilities
@@ -333,10 +336,14 @@ struct DecodeArgs {
   int B;
   int max_seq_len;
   int splits;
+  int grid_splits;  // splits rounded up to a multiple of 8 (1 when splits == 1)
   int pages_per_split;
-  float* o;         // written when splits == 1
-  float* part_acc;  // [B][16][splits][128] when splits > 1
-  float* part_ml;   // [B][16][splits][2]   when splits > 1
+  float* o;
+  // Partial results: DAH_PLAN_SPLIT slot (b*16 + h)*splits + split,
+  // DAH_PLAN_BALANCED slot (b + workgroup)*16 + h; 128 floats of weighted V
+  // sum each, then one float2 (running max in log2 units, sum) each.
+  float* part_acc;
+  float* part_ml;
   // The fused step only: q above is the raw (pre-norm) query.
   const float* k_new;
   const float* v_new;
@@ -355,48 +362,45 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8], float sc
   d[1] = make_float4(v[4] * scale, v[5] * scale, v[6] * scale, v[7] * scale);
 }
 
-// decodeGQA over one split of one sequence, for the 8 KV heads (one wave each).
-// kStep: the fused decode step -- q arrives raw and is normed and rotated here
-// (split 0 also writes q_out), and the workgroup holding the sequence's last
-// page norms and rotates the new key, stores the new key and value in the
-// cache and uses them for that slot directly from registers.
+// LDS a workgroup of the fused step uses to hold outputs until the end of a
+// range (see decode_range).
+struct StepStash {
+  u32x4 kv[kDecodeWavesPerBlock][2][2][16];  // [wave][k|v][word][column]
+  float4 q[kDecodeWavesPerBlock][2][2][16];  // [wave][head][half][column]
+};
+
+// The fused step for a sequence with nothing to attend to (seq_len out of
+// range): q_out is still the normed query, rotated at pos = seq_len - 1 (or 0).
+template <int kDtype>
+__device__ void step_q_out_only(const DecodeArgs& a, int b, int seq_len, int g, int lane) {
+  const int row = lane >> 4, col = lane & 15;
+  float qa[8], qb[8], qw[8], cr[8], sr[8];
+  load8(a.q + ((size_t)b * kHeads + 2 * g) * kHeadDim + 8 * col, qa);
+  load8(a.q + ((size_t)b * kHeads + 2 * g + 1) * kHeadDim + 8 * col, qb);
+  load8(a.q_gain + 8 * col, qw);
+  rope_table(seq_len >= 1 ? seq_len - 1 : 0, a.rope, lane, col, cr, sr);
+  norm_rope_row(qa, qw, a.eps, cr, sr, col);
+  norm_rope_row(qb, qw, a.eps, cr, sr, col);
+  if (row < 2) store8(a.q_out + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col,
+                      row == 0 ? qa : qb, 1.0f);
+}
+
+// decodeGQA of one KV head (this wave: g) and its query heads 2g, 2g+1 over
+// pages [p0, p1) of sequence b (p0 < p1 <= npages).  The result goes to o
+// when the range is the whole sequence (to_o), else to the partial slots
+// part_base + h * part_stride as (weighted V sum, running max, sum).
+// kStep, the fused decode step: q arrives raw and is normed and rotated here
+// (write_q: this range also writes q_out), and the range holding the
+// sequence's last page norms and rotates the new key, folds the new token in
+// from registers and stores the new key and value in the cache.
 template <int kDtype, bool kStep>
-__global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  // The wave index is uniform across the wave; saying so keeps everything
-  // derived from it (sequence, page range, page addresses) in scalar registers.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kDecodeWavesPerBlock + wave;
-  const int g = unit & (kKvHeads - 1);
-  const int bs = unit >> 3;  // b + B * split, the same for the whole workgroup
-  if (bs >= a.B * a.splits) return;
-  const int b = bs % a.B;
-  const int split = bs / a.B;
+__device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq_len, int npages,
+                                             int p0, int p1, bool write_q, bool to_o,
+                                             size_t part_base, int part_stride, int g, int lane,
+                                             StepStash& stash) {
+  const int wave = g;
   const int row = lane >> 4;
   const int col = lane & 15;
-
-  const int seq_len = a.seq_lens[b];
-  const bool len_ok = seq_len >= 1 && seq_len <= a.max_seq_len;
-  const int npages = len_ok ? (seq_len + kPage - 1) / kPage : 0;
-  const int p0 = split * a.pages_per_split;
-  const int p1 = min(p0 + a.pages_per_split, npages);
-  const bool empty = p0 >= p1;
-
-  // Empty range.  With one split this is the whole sequence: o = 0 for
-  // seq_len <= 0, NaN for a length past max_seq_len.  With several splits the
-  // combine kernel reads only non-empty ranges.  (In the fused step, split 0
-  // still has to write q_out first.)
-  auto fill_empty_output = [&]() {
-    if (a.splits == 1 && row < 2) {
-      const float fill = seq_len <= 0 ? 0.0f : NAN;
-      const float z[8] = {fill, fill, fill, fill, fill, fill, fill, fill};
-      store8(a.o + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col, z, 1.0f);
-    }
-  };
-  if (empty && !(kStep && split == 0)) {
-    fill_empty_output();
-    return;
-  }
 
   // The block table is read-only for the whole launch: reading it through the
   // constant address space makes every (uniform) read a scalar load, counted
@@ -408,11 +412,11 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   const char* kbase = a.k_cache + head_bytes;
   const char* vbase = a.v_cache + head_bytes;
   const int tail = seq_len - (npages - 1) * kPage;  // valid slots in the sequence's last page
-  const int last = p1 - 1;                           // last page of this wave's range
+  const int last = p1 - 1;                           // last page of this range
   // In the fused step the last page's final slot is the new token, which is
   // taken from registers, so only tail - 1 of its slots are read from the cache.
-  const bool step_last = kStep && p1 == npages && !empty;
-  const int last_valid = step_last ? tail - 1 : tail;
+  const bool holds_last = kStep && p1 == npages;
+  const int last_valid = holds_last ? tail - 1 : tail;
   const bool last_masked = (last == npages - 1) && last_valid < kPage;
   bool bad_page = false;
 
@@ -432,7 +436,6 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   float qa[8], qb[8];
   load8(a.q + ((size_t)b * kHeads + 2 * g) * kHeadDim + 8 * col, qa);
   load8(a.q + ((size_t)b * kHeads + 2 * g + 1) * kHeadDim + 8 * col, qb);
-  const bool holds_last = step_last;
   float qw[8], kx[8], vx[8], kw8[8];
   if constexpr (kStep) {
     load8(a.q_gain + 8 * col, qw);
@@ -445,10 +448,9 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
 
   // First tile in flight before the prologue's arithmetic.
   Tile<kDtype> K0, V0, K1, V1;
-  int id1 = 0, id2 = 0;
-  if (!empty) {
-    id1 = bt[min(p0 + 1, last)];
-    id2 = bt[min(p0 + 2, last)];
+  int id1 = bt[min(p0 + 1, last)];
+  int id2 = bt[min(p0 + 2, last)];
+  {
     const int64_t off0 = offset_of(bt[p0]);
     K0.load(kbase + off0, lane);
     V0.load(vbase + off0, lane);
@@ -459,27 +461,16 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   // by that wave only) and go to memory after the page loop: one counter
   // tracks vector loads and stores in issue order, so a store issued early
   // would hold up the waits for the first tiles.
-  __shared__ u32x4 stash[kDecodeWavesPerBlock][2][2][16];   // [wave][k|v][word][column]
-  __shared__ float4 qstash[kDecodeWavesPerBlock][2][2][16];  // [wave][head][half][column]
   if constexpr (kStep) {
-    const int pos = seq_len >= 1 ? seq_len - 1 : 0;
+    const int pos = seq_len - 1;
     float cr[8], sr[8];
     rope_table(pos, a.rope, lane, col, cr, sr);
     norm_rope_row(qa, qw, a.eps, cr, sr, col);
     norm_rope_row(qb, qw, a.eps, cr, sr, col);
-    if (split == 0 && row < 2) {
+    if (write_q && row < 2) {
       const float (&q)[8] = row == 0 ? qa : qb;
-      qstash[wave][row][0][col] = make_float4(q[0], q[1], q[2], q[3]);
-      qstash[wave][row][1][col] = make_float4(q[4], q[5], q[6], q[7]);
-    }
-    if (empty) {
-      if (split == 0 && row < 2) {
-        float* qo = a.q_out + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col;
-        reinterpret_cast<float4*>(qo)[0] = qstash[wave][row][0][col];
-        reinterpret_cast<float4*>(qo)[1] = qstash[wave][row][1][col];
-      }
-      fill_empty_output();
-      return;
+      stash.q[wave][row][0][col] = make_float4(q[0], q[1], q[2], q[3]);
+      stash.q[wave][row][1][col] = make_float4(q[4], q[5], q[6], q[7]);
     }
     if (holds_last) {
       norm_rope_row(kx, kw8, a.eps, cr, sr, col);
@@ -488,8 +479,8 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
       if (row == 0) {
 #pragma unroll
         for (int i = 0; i < SlotWords<kDtype>::kWords; ++i) {
-          stash[wave][0][i][col] = kw.w[i];
-          stash[wave][1][i][col] = vw.w[i];
+          stash.kv[wave][0][i][col] = kw.w[i];
+          stash.kv[wave][1][i][col] = vw.w[i];
         }
       }
     }
@@ -551,14 +542,14 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   }
   if constexpr (kStep) {
     // The new token (slot tail - 1 of the last page, read from the cache
-    // above as masked) enters from the stash: the values just stored, in the
-    // cache's dtype, owned by the row of that slot.
+    // above as masked) enters from the stash: the values just computed, in
+    // the cache's dtype, owned by the row of that slot.
     if (holds_last) {
       SlotWords<kDtype> kw, vw;
 #pragma unroll
       for (int i = 0; i < SlotWords<kDtype>::kWords; ++i) {
-        kw.w[i] = stash[wave][0][i][col];
-        vw.w[i] = stash[wave][1][i][col];
+        kw.w[i] = stash.kv[wave][0][i][col];
+        vw.w[i] = stash.kv[wave][1][i][col];
       }
       float kf[8], vf[8];
       unpack_slot<kDtype>(kw, kf);
@@ -587,19 +578,19 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   if (row < 2) {
     const HeadState& st = row == 0 ? A : Bs;
     const int h = 2 * g + row;
-    if (a.splits == 1) {
+    if (to_o) {
       store8(a.o + ((size_t)b * kHeads + h) * kHeadDim + 8 * col, st.acc, 1.0f / st.l);
     } else {
-      const size_t part = ((size_t)b * kHeads + h) * a.splits + split;
+      const size_t part = part_base + (size_t)h * part_stride;
       store8(a.part_acc + part * kHeadDim + 8 * col, st.acc, bad_page ? NAN : 1.0f);
       if (col == 0) reinterpret_cast<float2*>(a.part_ml)[part] = make_float2(st.m, st.l);
     }
   }
   if constexpr (kStep) {
-    if (split == 0 && row < 2) {
+    if (write_q && row < 2) {
       float* qo = a.q_out + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col;
-      reinterpret_cast<float4*>(qo)[0] = qstash[wave][row][0][col];
-      reinterpret_cast<float4*>(qo)[1] = qstash[wave][row][1][col];
+      reinterpret_cast<float4*>(qo)[0] = stash.q[wave][row][0][col];
+      reinterpret_cast<float4*>(qo)[1] = stash.q[wave][row][1][col];
     }
     if (holds_last && row == 0) {
       // The new token's slot: page block_table[b][npages-1], slot tail - 1.
@@ -611,58 +602,309 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
         u32x4* vd = reinterpret_cast<u32x4*>(a.v_cache_w + slot_off) + SlotWords<kDtype>::kWords * col;
 #pragma unroll
         for (int i = 0; i < SlotWords<kDtype>::kWords; ++i) {
-          kd[i] = stash[wave][0][i][col];
-          vd[i] = stash[wave][1][i][col];
+          kd[i] = stash.kv[wave][0][i][col];
+          vd[i] = stash.kv[wave][1][i][col];
         }
       }
     }
   }
 }
 
-// One wave per (sequence, query head): merge the non-empty split ranges.
-//   M = max_s m_s,  w_s = 2^(m_s - M),  o = sum_s w_s acc_s / sum_s w_s l_s
-__global__ __launch_bounds__(256) void combine_splits_kernel(const float* __restrict__ part_acc,
-                                                             const float* __restrict__ part_ml,
-                                                             const int32_t* __restrict__ seq_lens,
-                                                             int B, int max_seq_len, int splits,
-                                                             int pages_per_split,
-                                                             float* __restrict__ o) {
+__device__ __forceinline__ int pages_of(int seq_len, int max_seq_len) {
+  return (seq_len >= 1 && seq_len <= max_seq_len) ? (seq_len + kPage - 1) / kPage : 0;
+}
+
+// Empty sequence (seq_len <= 0: o = 0; past max_seq_len: o = NaN).
+__device__ __forceinline__ void fill_o(const DecodeArgs& a, int b, int seq_len, int g, int lane) {
+  const int row = lane >> 4, col = lane & 15;
+  if (row < 2) {
+    const float fill = seq_len <= 0 ? 0.0f : NAN;
+    const float z[8] = {fill, fill, fill, fill, fill, fill, fill, fill};
+    store8(a.o + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col, z, 1.0f);
+  }
+}
+
+// One workgroup (8 waves = 8 KV heads) per (sequence, split), each split
+// `pages_per_split` pages; splits == 1 writes o directly, otherwise
+// combine_splits_kernel merges the partials.
+template <int kDtype, bool kStep>
+__global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (unit >= B * kHeads) return;
+  // The wave index is uniform across the wave; saying so keeps everything
+  // derived from it (sequence, page range, page addresses) in scalar registers.
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head
+  // Workgroup -> (sequence, split).  Workgroups are handed to the 8 XCDs
+  // (each with its own L2 and 1/8 of the chip's bandwidth) round-robin by
+  // blockIdx.  With several splits the grid is padded to a multiple of 8
+  // splits and split s of sequence b goes to XCD (s + b) mod 8, so every XCD
+  // gets an eighth of each long sequence.
+  int b, split;
+  if (a.splits == 1) {
+    b = blockIdx.x;
+    split = 0;
+  } else {
+    const int xcd = blockIdx.x & 7;
+    const int local = blockIdx.x >> 3;
+    const int per = a.grid_splits >> 3;  // padded splits per XCD and sequence
+    b = local / per;
+    split = 8 * (local - b * per) + ((xcd - b) & 7);
+  }
+  if (b >= a.B) return;
+  const int seq_len = a.seq_lens[b];
+  const int npages = pages_of(seq_len, a.max_seq_len);
+  const int p0 = split * a.pages_per_split;  // splits past a.splits are padding: empty
+  const int p1 = min(p0 + a.pages_per_split, npages);
+  if (p0 >= p1 || split >= a.splits) {
+    // Nothing to attend to.  With one split this is the whole sequence; with
+    // several, the combine kernel reads only non-empty ranges.
+    if (kStep && split == 0) step_q_out_only<kDtype>(a, b, seq_len, g, lane);
+    if (a.splits == 1) fill_o(a, b, seq_len, g, lane);
+    return;
+  }
+  __shared__ StepStash stash;
+  decode_range<kDtype, kStep>(a, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
+                              ((size_t)b * kHeads) * a.splits + split, a.splits, g, lane, stash);
+}
+
+// Balanced decode: the batch's pages, in sequence order, are cut into
+// gridDim.x equal ranges, one per workgroup, regardless of where sequences
+// begin and end.  A workgroup walks the sequence segments inside its range;
+// a segment that is a whole sequence writes o, any other writes partial slot
+// b + k (k = workgroup), which combine_balanced_kernel merges.  Consecutive
+// workgroups go to different XCDs, so every XCD gets an equal share of the
+// pages however ragged the lengths are, and no workgroup is empty.
+template <int kDtype, bool kStep>
+__global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head
+  __shared__ int prefix[kMaxBalancedBatch + 1];  // prefix[b] = pages of sequences < b
+  __shared__ int wave_total[kDecodeWavesPerBlock];
+  __shared__ StepStash stash;
+
+  // Block-wide exclusive scan of the page counts; thread t owns sequences
+  // 8t .. 8t+7.
+  const int t = threadIdx.x;
+  int own[8], tot = 0;
+  // Eight independent loads (clamped index, masked afterwards) so that they
+  // are in flight together.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) own[i] = a.seq_lens[min(8 * t + i, a.B - 1)];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    own[i] = 8 * t + i < a.B ? pages_of(own[i], a.max_seq_len) : 0;
+    tot += own[i];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wave_total[g] = incl;
+  __syncthreads();
+  int run = incl - tot;
+  for (int w = 0; w < g; ++w) run += wave_total[w];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int bb = 8 * t + i;
+    if (bb < a.B) prefix[bb] = run;
+    run += own[i];
+    if (bb == a.B - 1) prefix[a.B] = run;
+  }
+  __syncthreads();
+
+  if constexpr (kStep) {
+    // Sequences with nothing to attend to still get q_out (workgroup 0).
+    if (blockIdx.x == 0)
+      for (int bb = 0; bb < a.B; ++bb)
+        if (prefix[bb + 1] == prefix[bb]) step_q_out_only<kDtype>(a, bb, a.seq_lens[bb], g, lane);
+  }
+
+  const long long T = prefix[a.B];
+  const long long G = gridDim.x, k = blockIdx.x;
+  int s = (int)(k * T / G);
+  const int e = (int)((k + 1) * T / G);
+  if (s >= e) return;
+  // The sequence holding page s: the largest b with prefix[b] <= s.
+  int lo = 0, hi = a.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= s) lo = mid; else hi = mid;
+  }
+  int b = lo;
+  for (;;) {
+    b = __builtin_amdgcn_readfirstlane(b);
+    const int base = __builtin_amdgcn_readfirstlane(prefix[b]);
+    const int next = __builtin_amdgcn_readfirstlane(prefix[b + 1]);
+    const int seg_end = min(e, next);
+    const int npages = next - base;
+    const int p0 = s - base, p1 = seg_end - base;
+    const bool whole = p0 == 0 && p1 == npages;
+    decode_range<kDtype, kStep>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
+                                (size_t)(b + k) * kHeads, 1, g, lane, stash);
+    s = seg_end;
+    if (s >= e) break;
+    do { ++b; } while (prefix[b + 1] == prefix[b]);  // next sequence with pages
+  }
+}
+
+// ------------------------------------------------------------ log-sum-exp merge
+//
+// One workgroup of 256 threads per (sequence, query head) merges that row's
+// partial results (weighted V sum acc_s, running max m_s in log2 units, sum
+// l_s):  M = max_s m_s,  w_s = 2^(m_s - M),  o = sum_s w_s acc_s / sum_s w_s l_s.
+// Thread t owns dims 4(t mod 32) .. +3 and every 8th partial starting at
+// t / 32, so 8 partials are read in parallel for each dim; LDS merges the 8
+// groups.  The partials' lists are independent loads, so a long list costs
+// bandwidth, not a chain of latencies.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineGroups = kCombineThreads / 32;
+
+// Partial i of a row: split layout (row-major splits, all present).
+struct SplitParts {
+  size_t base;  // (b * 16 + h) * splits
+  __device__ size_t slot(int i) const { return base + i; }
+  __device__ bool present(int) const { return true; }
+};
+
+// Partial i of a row: balanced layout, slot (b + k0 + i) * 16 + h; a
+// workgroup whose page range was empty wrote nothing.
+struct BalancedParts {
+  int b, h, k0;
+  long long T, G;
+  __device__ size_t slot(int i) const { return (size_t)(b + k0 + i) * kHeads + h; }
+  __device__ bool present(int i) const {
+    const long long k = k0 + i;
+    return T >= G || k * T / G < (k + 1) * T / G;
+  }
+};
+
+template <class Parts>
+__device__ __forceinline__ void merge_parts(const float* __restrict__ part_acc,
+                                            const float* __restrict__ part_ml, const Parts& parts,
+                                            int n, float* __restrict__ out_row) {
+  __shared__ float red_m[kCombineThreads / kWave];
+  __shared__ float4 red_acc[kCombineGroups][32];
+  __shared__ float red_l[kCombineGroups];
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int grp = t >> 5, dim4 = t & 31;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml);
+
+  float M = -INFINITY;
+  for (int i = t; i < n; i += kCombineThreads)
+    if (parts.present(i)) M = fmaxf(M, ml[parts.slot(i)].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red_m[t >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float L = 0.0f;
+#pragma unroll 4
+  for (int i = grp; i < n; i += kCombineGroups) {
+    if (!parts.present(i)) continue;
+    const size_t slot = parts.slot(i);
+    const float2 m_l = ml[slot];
+    const float4 v = reinterpret_cast<const float4*>(part_acc + slot * kHeadDim)[dim4];
+    const float w = fast_exp2(m_l.x - M);
+    L = fmaf(w, m_l.y, L);
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  red_acc[grp][dim4] = acc;
+  if (dim4 == 0) red_l[grp] = L;
+  __syncthreads();
+  if (grp == 0) {
+    float4 sum = red_acc[0][dim4];
+    float Ls = red_l[0];
+#pragma unroll
+    for (int g = 1; g < kCombineGroups; ++g) {
+      const float4 v = red_acc[g][dim4];
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+      Ls += red_l[g];
+    }
+    const float inv = 1.0f / Ls;
+    reinterpret_cast<float4*>(out_row)[dim4] =
+        make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+  }
+}
+
+// Empty sequence: o = 0 for seq_len <= 0, NaN for a length past max_seq_len.
+__device__ __forceinline__ void fill_row(float* out_row, int seq_len) {
+  if (threadIdx.x < 32) {
+    const float fill = seq_len < 1 ? 0.0f : NAN;
+    reinterpret_cast<float4*>(out_row)[threadIdx.x] = make_float4(fill, fill, fill, fill);
+  }
+}
+
+// DAH_PLAN_SPLIT: the non-empty splits of each (sequence, head).
+__global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
+    const float* __restrict__ part_acc, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_lens, int B, int max_seq_len, int splits, int pages_per_split,
+    float* __restrict__ o) {
+  const int unit = blockIdx.x;  // b * 16 + h
   const int b = unit / kHeads;
   const int seq_len = seq_lens[b];
-  float2* out = reinterpret_cast<float2*>(o + (size_t)unit * kHeadDim) + lane;
+  float* out_row = o + (size_t)unit * kHeadDim;
   if (seq_len < 1 || seq_len > max_seq_len) {
-    const float fill = seq_len < 1 ? 0.0f : NAN;
-    *out = make_float2(fill, fill);
+    fill_row(out_row, seq_len);
     return;
   }
   const int npages = (seq_len + kPage - 1) / kPage;
   const int nsplit = (npages + pages_per_split - 1) / pages_per_split;
-  const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)unit * splits;
-  const float2* acc = reinterpret_cast<const float2*>(part_acc + (size_t)unit * splits * kHeadDim) + lane;
+  merge_parts(part_acc, part_ml, SplitParts{(size_t)unit * splits}, nsplit, out_row);
+}
 
-  float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += kWave) M = fmaxf(M, ml[s].x);
-  M = fmaxf(M, __shfl_xor(M, 1));
-  M = fmaxf(M, __shfl_xor(M, 2));
-  M = fmaxf(M, __shfl_xor(M, 4));
-  M = fmaxf(M, __shfl_xor(M, 8));
-  M = fmaxf(M, __shfl_xor(M, 16));
-  M = fmaxf(M, __shfl_xor(M, 32));
-
-  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 m_l = ml[s];
-    const float w = fast_exp2(m_l.x - M);
-    const float2 v = acc[(size_t)s * (kHeadDim / 2)];
-    L = fmaf(w, m_l.y, L);
-    o0 = fmaf(w, v.x, o0);
-    o1 = fmaf(w, v.y, o1);
+// DAH_PLAN_BALANCED: sequence b owns pages [P_b, P_b + n_b) of the batch and
+// workgroup k of G owns [floor(kT/G), floor((k+1)T/G)), so the workgroups
+// that saw b are owner(P_b) .. owner(P_b + n_b - 1) with
+// owner(x) = floor(((x+1)G - 1)/T), their partials in slots b + k.  A
+// sequence seen by one workgroup was written to o directly.
+__global__ __launch_bounds__(kCombineThreads) void combine_balanced_kernel(
+    const float* __restrict__ part_acc, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_lens, int B, int max_seq_len, int G, float* __restrict__ o) {
+  __shared__ int red[2][kCombineThreads / kWave];
+  const int unit = blockIdx.x;  // b * 16 + h
+  const int b = unit / kHeads;
+  const int h = unit - b * kHeads;
+  const int seq_len = seq_lens[b];
+  float* out_row = o + (size_t)unit * kHeadDim;
+  if (seq_len < 1 || seq_len > max_seq_len) {
+    fill_row(out_row, seq_len);
+    return;
   }
-  const float inv = 1.0f / L;
-  *out = make_float2(o0 * inv, o1 * inv);
+  // P_b and T: page counts summed across the workgroup.
+  int before = 0, total = 0;
+  for (int i = threadIdx.x; i < B; i += kCombineThreads) {
+    const int n = seq_lens[i];
+    const int np = (n >= 1 && n <= max_seq_len) ? (n + kPage - 1) / kPage : 0;
+    total += np;
+    before += i < b ? np : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    before += __shfl_xor(before, off);
+    total += __shfl_xor(total, off);
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    red[0][threadIdx.x >> 6] = before;
+    red[1][threadIdx.x >> 6] = total;
+  }
+  __syncthreads();
+  const long long P = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  const long long T = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const long long last = P + (seq_len + kPage - 1) / kPage - 1;
+  const int k0 = (int)(((P + 1) * G - 1) / T);
+  const int k1 = (int)(((last + 1) * G - 1) / T);
+  if (k0 == k1) return;
+  merge_parts(part_acc, part_ml, BalancedParts{b, h, k0, T, (long long)G}, k1 - k0 + 1, out_row);
 }
 
 // ------------------------------------------------------------ norm + RoPE + append
@@ -840,18 +1082,35 @@ int plan_for(int B, int max_seq_len, int num_splits, void* workspace, size_t wor
   int cus = 0;
   int st = device_cu_count(&cus);
   if (st != DAH_OK) return st;
-  st = dah::plan_splits(B, max_seq_len, num_splits, cus, plan);
+  st = dah::plan_decode(B, max_seq_len, num_splits, cus, plan);
   if (st != DAH_OK) return st;
   if (plan->workspace > 0) {
     if (workspace == nullptr || workspace_bytes < plan->workspace)
       return dah::set_error(DAH_ERR_WORKSPACE,
-                            "workspace of %zu bytes, need %zu (B=%d, max_seq_len=%d, %d splits)",
+                            "workspace of %zu bytes, need %zu (B=%d, max_seq_len=%d)",
                             workspace == nullptr ? (size_t)0 : workspace_bytes, plan->workspace, B,
-                            max_seq_len, plan->splits);
+                            max_seq_len);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return dah::set_error(DAH_ERR_ALIGN, "workspace needs 256-byte alignment");
   }
   return DAH_OK;
+}
+
+template <bool kStep>
+void launch_decode_kernel(const dah::Plan& plan, bool bf16, const DecodeArgs& a,
+                          hipStream_t stream) {
+  const dim3 grid((unsigned)plan.workgroups), block(kWave * kDecodeWavesPerBlock);
+  if (plan.mode == DAH_PLAN_BALANCED) {
+    if (bf16)
+      decode_balanced_kernel<DAH_BF16, kStep><<<grid, block, 0, stream>>>(a);
+    else
+      decode_balanced_kernel<DAH_F32, kStep><<<grid, block, 0, stream>>>(a);
+  } else {
+    if (bf16)
+      decode_split_kernel<DAH_BF16, kStep><<<grid, block, 0, stream>>>(a);
+    else
+      decode_split_kernel<DAH_F32, kStep><<<grid, block, 0, stream>>>(a);
+  }
 }
 
 // Decode (step == nullptr: q is already normed and roped) or the fused
@@ -871,13 +1130,14 @@ int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
   a.seq_lens = seq_lens;
   a.B = B;
   a.max_seq_len = max_seq_len;
-  a.splits = plan.splits;
+  a.splits = plan.mode == DAH_PLAN_SPLIT ? plan.splits : 1;
+  a.grid_splits = plan.mode == DAH_PLAN_SPLIT ? plan.grid_splits : 1;
   a.pages_per_split = plan.pages_per_split;
   a.o = o;
   float* ws = static_cast<float*>(workspace);
-  const size_t parts = (size_t)B * kHeads * plan.splits;
-  a.part_acc = plan.splits > 1 ? ws : nullptr;
-  a.part_ml = plan.splits > 1 ? ws + parts * kHeadDim : nullptr;
+  const size_t slots = plan.workspace / ((kHeadDim + 2) * sizeof(float) * kHeads);
+  a.part_acc = plan.workspace > 0 ? ws : nullptr;
+  a.part_ml = plan.workspace > 0 ? ws + slots * kHeads * kHeadDim : nullptr;
   if (step != nullptr) {
     a.k_new = step->k_new;
     a.v_new = step->v_new;
@@ -889,29 +1149,21 @@ int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
     a.k_cache_w = static_cast<char*>(step->k_cache);
     a.v_cache_w = static_cast<char*>(step->v_cache);
   }
-
-  const long long blocks = (long long)B * plan.splits;  // one workgroup per (sequence, split)
-  if (blocks > INT32_MAX) return dah::set_error(DAH_ERR_SHAPE, "grid too large");
-  const dim3 grid((unsigned)blocks), block(kWave * kDecodeWavesPerBlock);
   const bool bf16 = cache_dtype == DAH_BF16;
-  if (step == nullptr) {
-    if (bf16)
-      decode_split_kernel<DAH_BF16, false><<<grid, block, 0, stream>>>(a);
-    else
-      decode_split_kernel<DAH_F32, false><<<grid, block, 0, stream>>>(a);
-  } else {
-    if (bf16)
-      decode_split_kernel<DAH_BF16, true><<<grid, block, 0, stream>>>(a);
-    else
-      decode_split_kernel<DAH_F32, true><<<grid, block, 0, stream>>>(a);
-  }
-  int st = check_launch("decode_split_kernel");
-  if (st != DAH_OK || plan.splits == 1) return st;
-  const int cblocks = (B * kHeads + 3) / 4;
-  combine_splits_kernel<<<cblocks, 256, 0, stream>>>(a.part_acc, a.part_ml, seq_lens, B,
-                                                     max_seq_len, plan.splits,
-                                                     plan.pages_per_split, o);
-  return check_launch("combine_splits_kernel");
+  if (step == nullptr)
+    launch_decode_kernel<false>(plan, bf16, a, stream);
+  else
+    launch_decode_kernel<true>(plan, bf16, a, stream);
+  int st = check_launch("decode kernel");
+  if (st != DAH_OK || plan.mode == DAH_PLAN_PER_SEQUENCE) return st;
+  const int cblocks = B * kHeads;  // one workgroup per (sequence, head)
+  if (plan.mode == DAH_PLAN_BALANCED)
+    combine_balanced_kernel<<<cblocks, kCombineThreads, 0, stream>>>(
+        a.part_acc, a.part_ml, seq_lens, B, max_seq_len, plan.workgroups, o);
+  else
+    combine_splits_kernel<<<cblocks, kCombineThreads, 0, stream>>>(
+        a.part_acc, a.part_ml, seq_lens, B, max_seq_len, plan.splits, plan.pages_per_split, o);
+  return check_launch("combine kernel");
 }
 
 }  // namespace
@@ -969,7 +1221,7 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
   st = plan_for(B, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
   if (st != DAH_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q_out == q && plan.splits > 1) {
+  if (q_out == q && plan.mode != DAH_PLAN_PER_SEQUENCE) {
     // In place with several splits: the workgroups of one sequence would read
     // q while another overwrites it, so norm and rotate first, then decode.
     st = launch_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,

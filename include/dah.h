@@ -157,13 +157,39 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
                      void* stream);
 
 /*
- * dah_plan_splits -- the split planner, on the host, for a device with
- * num_cus compute units.  Writes the number of splits and the split length in
- * pages (every split but the last of the longest sequence covers exactly
- * that many pages).  num_splits as in paged_decode_gqa.  Returns a dah_status.
+ * dah_plan_decode -- how paged_decode_gqa / decode_attn_step will cut the work
+ * on a device with num_cus compute units (host-only, no device access).
+ *
+ *   DAH_PLAN_PER_SEQUENCE  one workgroup per sequence (8 waves, one per KV head);
+ *                          chosen when the batch alone fills the device and no
+ *                          sequence exceeds 128 pages
+ *   DAH_PLAN_BALANCED      the batch's pages, in sequence order, cut into
+ *                          `workgroups` equal ranges regardless of sequence
+ *                          boundaries; sequences cut by a range boundary are
+ *                          merged by a log-sum-exp combine (flashAttn_eq on the
+ *                          "Supported models" page licenses any partition)
+ *   DAH_PLAN_SPLIT         every sequence cut into `splits` ranges of
+ *                          `pages_per_split` pages (num_splits > 1 asks for this;
+ *                          also the fallback for batches over 4096 sequences)
+ *
+ * num_splits: 0 = automatic, 1 = per sequence, n > 1 = at most n splits.
+ * Returns a dah_status.
  */
-int dah_plan_splits(int B, int max_seq_len, int num_splits, int num_cus,
-                    int* splits_out, int* pages_per_split_out);
+typedef enum {
+  DAH_PLAN_PER_SEQUENCE = 0,
+  DAH_PLAN_SPLIT = 1,
+  DAH_PLAN_BALANCED = 2
+} dah_plan_mode;
+
+typedef struct {
+  int mode;               /* dah_plan_mode */
+  int splits;             /* splits per sequence (PER_SEQUENCE: 1; BALANCED: 0) */
+  int pages_per_split;    /* pages per split (PER_SEQUENCE: the longest sequence; BALANCED: 0) */
+  int workgroups;         /* workgroups of the decode launch */
+  size_t workspace_bytes; /* workspace the call needs */
+} dah_decode_plan;
+
+int dah_plan_decode(int B, int max_seq_len, int num_splits, int num_cus, dah_decode_plan* out);
 
 /*
  * dah_workspace_bytes -- workspace paged_decode_gqa and decode_attn_step need

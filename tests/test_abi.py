@@ -84,42 +84,59 @@ def test_status_strings():
 
 def _plan(B, L, n=0, cus=256):
     lib = _lib()
-    s, p = ctypes.c_int(), ctypes.c_int()
-    st = lib.dah_plan_splits(B, L, n, cus, ctypes.byref(s), ctypes.byref(p))
-    return st, s.value, p.value
+    p = native.DecodePlan()
+    st = lib.dah_plan_decode(B, L, n, cus, ctypes.byref(p))
+    return st, p
 
 
-@pytest.mark.parametrize("B,L", [(1, 1), (2, 12), (32, 4096), (256, 2048), (4, 40960),
-                                 (128, 16384), (256, 40960), (1, 17), (7, 999)])
+SHAPES = [(1, 1), (2, 12), (32, 4096), (256, 2048), (4, 40960), (128, 16384), (256, 40960),
+          (1, 17), (7, 999), (4096, 64), (5000, 2048)]
+
+
+@pytest.mark.parametrize("B,L", SHAPES)
 @pytest.mark.parametrize("n", [0, 1, 2, 3, 7, 16, 1000])
-def test_planner_covers_every_page_with_no_empty_split(B, L, n):
-    st, splits, pps = _plan(B, L, n)
+def test_planner_is_consistent(B, L, n):
+    st, p = _plan(B, L, n)
     assert st == 0
     pages = -(-L // 16)
-    assert splits >= 1 and pps >= 1
-    assert splits * pps >= pages            # every page of the longest sequence is covered
-    assert (splits - 1) * pps < pages       # the last split is not empty
-    if n > 0:
-        assert splits <= n
-    lib = _lib()
-    ws = lib.dah_workspace_bytes_for(B, L, n, 256)
-    assert ws == (0 if splits == 1 else B * 16 * splits * 130 * 4)
+    mode = native.PLAN_MODES[p.mode]
+    slot_bytes = 16 * 130 * 4
+    if mode == "per_sequence":
+        assert p.splits == 1 and p.workgroups == B and p.workspace_bytes == 0
+        assert p.pages_per_split == pages
+    elif mode == "split":
+        assert p.splits >= 2 and p.pages_per_split >= 1
+        assert p.splits * p.pages_per_split >= pages          # every page is covered
+        assert (p.splits - 1) * p.pages_per_split < pages     # the last split is not empty
+        assert p.workgroups == B * (-(-p.splits // 8) * 8)   # padded for the XCD mapping
+        assert p.workspace_bytes == B * p.splits * slot_bytes
+    else:
+        assert mode == "balanced" and n == 0 and 64 <= B <= 4096
+        assert p.workgroups == 256
+        assert p.workspace_bytes == (B + p.workgroups - 1) * slot_bytes
+    if n == 1:
+        assert mode == "per_sequence"
+    if n > 1:
+        assert p.splits <= n and mode in ("split", "per_sequence")
+    assert _lib().dah_workspace_bytes_for(B, L, n, 256) == p.workspace_bytes
 
 
 def test_planner_choices_for_the_measured_shapes():
-    # the split counts that measured fastest on MI355X (256 compute units)
-    assert _plan(256, 2048)[1:] == (1, 128)      # 2048 waves already fill the chip
-    assert _plan(32, 4096)[1:] == (8, 32)
-    assert _plan(4, 40960)[1:] == (64, 40)
-    assert _plan(128, 14464)[1:] == (8, 113)     # ragged batch: split the longest sequence
-    assert _plan(2, 12)[1:] == (1, 1)
-
-
-def test_planner_never_leaves_long_splits():
-    for B in (1, 8, 64, 256):
-        for L in (2048, 4096, 16384, 40960):
-            st, splits, pps = _plan(B, L)
-            assert st == 0 and pps <= 128
+    # B=256, S=2048: one workgroup per sequence fills 256 compute units
+    st, p = _plan(256, 2048)
+    assert native.PLAN_MODES[p.mode] == "per_sequence"
+    # 64+ sequences that do not fill the device or run long: balanced
+    for B, L in [(128, 14464), (64, 100), (255, 2048), (256, 2064), (4096, 40960)]:
+        st, p = _plan(B, L)
+        assert native.PLAN_MODES[p.mode] == "balanced", (B, L)
+    # fewer sequences: fixed splits spread over the XCDs (measured best at
+    # B=32 up to 4096 positions: 8 splits; B=4 up to 40,960: 64 splits)
+    assert (native.PLAN_MODES[_plan(32, 4096)[1].mode], _plan(32, 4096)[1].splits) == ("split", 8)
+    assert (native.PLAN_MODES[_plan(4, 40960)[1].mode], _plan(4, 40960)[1].splits) == ("split", 64)
+    assert native.PLAN_MODES[_plan(2, 12)[1].mode] == "per_sequence"
+    # beyond the balanced scan's 4096 sequences: fixed splits
+    st, p = _plan(5000, 4096)
+    assert native.PLAN_MODES[p.mode] == "split"
 
 
 @pytest.mark.parametrize("args,status", [
@@ -127,9 +144,10 @@ def test_planner_never_leaves_long_splits():
 ])
 def test_planner_rejects_bad_arguments(args, status):
     lib = _lib()
-    s, p = ctypes.c_int(), ctypes.c_int()
-    assert lib.dah_plan_splits(*args, ctypes.byref(s), ctypes.byref(p)) == status
+    p = native.DecodePlan()
+    assert lib.dah_plan_decode(*args, ctypes.byref(p)) == status
     assert lib.dah_last_error().decode() != ""
+    assert lib.dah_plan_decode(1, 10, 0, 256, None) == 1
 
 
 # Fake, aligned addresses: every call below must fail validation before any

@@ -57,7 +57,7 @@ def test_split_count_invariance():
     ref = oracle_decode(snap, "bf16")
     L = int(max(lens))
     outs = {}
-    for n in (1, 2, 3, 7, 16, 64, 256):
+    for n in (1, 0, 2, 3, 7, 16, 64, 256):
         _print(f"[splits] num_splits={n}")
         o = _decode(t, L, num_splits=n)
         torch.cuda.synchronize()
@@ -75,9 +75,9 @@ def test_nan_poison_outside_prefix(dtype):
     w = _custom(len(lens), lens, dtype=dtype, pool_pages=64, seed=22)
     t, seq_lens, table, _ = build_layer(w)
     L = int(max(lens))
-    clean = {n: _decode(t, L, num_splits=n).clone() for n in (1, 3)}
+    clean = {n: _decode(t, L, num_splits=n).clone() for n in (0, 1, 3)}
     W.poison_unused(t, seq_lens, table, value=float("nan"))
-    for n in (1, 3):
+    for n in (0, 1, 3):
         poisoned = _decode(t, L, num_splits=n)
         torch.cuda.synchronize()
         assert torch.equal(poisoned, clean[n]), f"poisoned tail changed o (splits={n})"
@@ -212,7 +212,7 @@ def test_out_of_domain_device_values():
     sl[3] = 33                       # above max_seq_len = 32 below
     t["block_table"][4, 1] = num_pages + 5
     k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
-    for n in (1, 2):
+    for n in (1, 2, 0):
         q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
                                         t["k_pool"], t["v_pool"], t["block_table"], sl, 32,
                                         num_splits=n)
@@ -255,7 +255,7 @@ def test_large_gain_peaked_softmax():
         p0 = int(table[b, 0])
         t["k_pool"][p0, :, 0, :] = (t["q"][b, ::2, :] * 4.0).to(torch.bfloat16)
     snap = host_snapshot(t, seq_lens, table, range(3))
-    for n in (1, 5):
+    for n in (1, 5, 0):
         k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
         q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
                                         t["k_pool"], t["v_pool"], t["block_table"],
@@ -286,7 +286,7 @@ def test_domain_maximum_sampled():
     assert torch.isfinite(o).all()
 
 
-@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("splits", [1, 3, 0])
 def test_step_in_place_query(splits):
     """q_out may be q: the in-place call gives the same q_out, o and cache as
     a call with a separate q_out."""
@@ -315,7 +315,7 @@ def test_step_in_place_query(splits):
     assert torch.equal(t["v_pool"], v1)
 
 
-@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("splits", [1, 4, 0])
 def test_fused_step_matches_two_calls(splits):
     """decode_attn_step (one fused launch) against qk_norm_rope_append followed
     by paged_decode_gqa: same q_out and o to float32 rounding, same stored v,
@@ -345,7 +345,7 @@ def test_fused_step_matches_two_calls(splits):
     assert bool(((kf.float() - t["k_pool"].float()).abs() <= step).all())
 
 
-@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("splits", [1, 3, 0])
 def test_step_touches_only_the_new_slot(splits):
     import torch
     dah = _dah()
@@ -361,3 +361,49 @@ def test_step_touches_only_the_new_slot(splits):
     for b, n in enumerate(lens):
         want[int(table[b, (n - 1) // 16]), :, (n - 1) % 16] = True
     assert torch.equal(changed, want)
+
+
+def test_balanced_plan_with_more_workgroups_than_pages():
+    """Balanced decode when the batch has fewer pages than workgroups (some
+    workgroups own no page): results match the per-sequence layout."""
+    import torch
+    dah = _dah()
+    lens = list(np.random.default_rng(38).integers(1, 48, 80))
+    w = _custom(len(lens), lens, dtype="bf16", seed=37)
+    t, seq_lens, table, _ = build_layer(w)
+    L = int(max(lens))
+    plan = dah.plan_decode(len(lens), L)
+    assert plan["mode"] == "balanced" and plan["workgroups"] > sum(-(-n // 16) for n in lens)
+    o_bal = _decode(t, L, num_splits=0)
+    o_one = _decode(t, L, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o_bal).all()
+    assert torch.allclose(o_bal, o_one, atol=1e-6, rtol=0)
+    snap = host_snapshot(t, seq_lens, table, range(len(lens)))
+    gates(o_bal.cpu().numpy().astype(np.float64), oracle_decode(snap, "bf16"), None, 2e-2,
+          label="balanced, T < G")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_balanced_ragged_batch_matches_oracle(splits):
+    """A ragged batch of 96 sequences (1 .. 6000 positions, some sharing
+    workgroups, some spread over many) in every layout, with the fused step."""
+    import torch
+    dah = _dah()
+    rng = np.random.default_rng(39)
+    lens = list(np.floor(np.exp(rng.uniform(0, np.log(6000), 96))).astype(int))
+    w = _custom(len(lens), lens, dtype="bf16", seed=38)
+    t, seq_lens, table, _ = build_layer(w)
+    L = int(max(lens))
+    if splits == 0:
+        assert dah.plan_decode(len(lens), L)["mode"] == "balanced"
+    snap = host_snapshot(t, seq_lens, table, range(len(lens)))
+    q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    L, num_splits=splits)
+    torch.cuda.synchronize()
+    ref = oracle_step(snap, "bf16")
+    e_abs, e_rel = gates(o.cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
+                         label=f"ragged step, splits={splits}")
+    assert float(np.max(np.abs(q_out.cpu().numpy() - ref["q_out"]))) <= 1e-5
+    _print(f"  ragged step splits={splits}: max abs {e_abs:.3g} rel {e_rel:.3g}")
