@@ -118,19 +118,21 @@ int qk_norm_rope_append(const float* q, const float* k_new, const float* v_new,
  *
  *   o[b,h] = sum_{s < seq_lens[b]} softmax_s(<q[b,h], K[b,s,h/2]> / sqrt(128)) V[b,s,h/2]
  *
- * computed as split-S flash decoding: the positions of a sequence are cut
- * into `splits` contiguous ranges whose partial (max, sum, weighted V) are
- * merged with a log-sum-exp combine.  The "Supported models" page ("Facts
- * proved about the specs": flashAttn_eq, softmax_shift) states that this
- * equals the spec's attention for any partition.
+ * computed as flash decoding: the positions are cut into ranges (see
+ * dah_plan_decode) whose partial (max, sum, weighted V) are merged with a
+ * log-sum-exp combine.  The "Supported models" page ("Facts proved about the
+ * specs": flashAttn_eq, softmax_shift) states that this equals the spec's
+ * attention for any partition.  One launch, plus one for the merge when a
+ * sequence is cut.
  *
  *   q            [device] float32 [B][16][128], already normed and roped, 16-byte aligned
  *   k_cache, v_cache [device] pools, 16-byte aligned; cache_dtype DAH_F32 or DAH_BF16
  *   num_pages, block_table, max_pages_per_seq, seq_lens, B  as above
  *   max_seq_len  host-side bound on every seq_lens[b] (>= 1, <= max_pages_per_seq*16);
- *                the split planner uses it
- *   num_splits   0 = let the planner choose; n > 0 asks for at most n splits
- *                (the planner may use fewer so that no split is empty)
+ *                the planner uses it
+ *   num_splits   0 = let the planner choose; 1 = one workgroup per sequence;
+ *                n > 1 = every sequence in at most n equal splits (the planner
+ *                may use fewer so that no split is empty)
  *   o            [device] float32 [B][16][128], 16-byte aligned
  *   workspace    [device] scratch of at least
  *                dah_workspace_bytes(B, max_seq_len, num_splits) bytes,
@@ -143,10 +145,14 @@ int paged_decode_gqa(const float* q, const void* k_cache, const void* v_cache, i
                      float* o, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * decode_attn_step -- the whole decode-attention block for one layer:
- * qk_norm_rope_append followed, on the same stream, by paged_decode_gqa on
- * q_out.  The attention reads the position appended by this call.
- * Arguments are those of the two calls; q_out is required (it may equal q).
+ * decode_attn_step -- the whole decode-attention block for one layer: the
+ * result of qk_norm_rope_append followed by paged_decode_gqa on q_out, in one
+ * kernel launch (plus the merge when a sequence is cut): every decode
+ * workgroup norms and rotates its own query heads, and the workgroup that
+ * holds a sequence's last page norms, rotates and stores the new key and
+ * value and attends to them.  Arguments are those of the two calls; q_out is
+ * required and may equal q (in place with a cut sequence, the call makes the
+ * two launches instead).
  */
 int decode_attn_step(const float* q, const float* k_new, const float* v_new,
                      const float* q_gain, const float* k_gain, float eps, float rope_theta,
