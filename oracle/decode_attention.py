@@ -200,20 +200,33 @@ def softmax(z: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
-def decode_gqa_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
-    """One sequence: q [16,128], k/v [S,8,128] (S >= 1) -> o [16,128].
+def group_size(num_heads: int, num_kv_heads: int = NUM_KV_HEADS) -> int:
+    """Query heads per KV head.  Qwen3-0.6B has 16 over 8 (G = 2); the family's
+    other sizes are 32, 40 and 64 over 8 (nnterp qwen3 page, "Grouped-query
+    attention, with 128-wide heads on every size")."""
+    if num_heads % num_kv_heads:
+        raise ValueError(f"{num_heads} query heads do not split over {num_kv_heads} KV heads")
+    return num_heads // num_kv_heads
 
-    o[h] = sum_s softmax_s(<q[h], k[s, h // 2]> / sqrt(128)) * v[s, h // 2].
+
+def decode_gqa_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """One sequence: q [H,128], k/v [S,8,128] (S >= 1) -> o [H,128].
+
+    o[h] = sum_s softmax_s(<q[h], k[s, h // G]> / sqrt(128)) * v[s, h // G],
+    G = H / 8 query heads per KV head (G = 2 for Qwen3-0.6B: KV head j serves
+    query heads 2j and 2j+1).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     if k.shape[0] < 1:
         raise ValueError("decodeGQA needs at least one cached position (S >= 1)")
-    o = np.empty((NUM_HEADS, HEAD_DIM), dtype=np.float64)
+    H = q.shape[0]
+    G = group_size(H, k.shape[1])
+    o = np.empty((H, HEAD_DIM), dtype=np.float64)
     scale = 1.0 / math.sqrt(HEAD_DIM)
-    for h in range(NUM_HEADS):
-        g = h // 2
+    for h in range(H):
+        g = h // G
         scores = (k[:, g, :] @ q[h]) * scale
         p = softmax(scores)
         o[h] = p @ v[:, g, :]
@@ -221,19 +234,20 @@ def decode_gqa_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
 
 
 def attention_weights(q: np.ndarray, k: np.ndarray) -> np.ndarray:
-    """The softmax weights decodeGQA uses: [16, S] for one sequence."""
+    """The softmax weights decodeGQA uses: [H, S] for one sequence."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
+    G = group_size(q.shape[0], k.shape[1])
     scale = 1.0 / math.sqrt(HEAD_DIM)
-    return np.stack([softmax((k[:, h // 2, :] @ q[h]) * scale) for h in range(NUM_HEADS)])
+    return np.stack([softmax((k[:, h // G, :] @ q[h]) * scale) for h in range(q.shape[0])])
 
 
 def paged_decode_gqa(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                      block_table: np.ndarray, seq_lens: np.ndarray, cache_dtype: str,
                      batch_indices=None) -> np.ndarray:
     """decodeGQA over a paged cache, for the sequences in ``batch_indices``
-    (all by default).  q is [B,16,128] (already normed and roped).
-    Returns o [len(batch_indices),16,128] in float64."""
+    (all by default).  q is [B,H,128] (already normed and roped).
+    Returns o [len(batch_indices),H,128] in float64."""
     q = np.asarray(q, dtype=np.float64)
     idx = range(q.shape[0]) if batch_indices is None else list(batch_indices)
     out = []
@@ -242,7 +256,7 @@ def paged_decode_gqa(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         k = gather_sequence(k_pool, block_table[b], n, cache_dtype)
         v = gather_sequence(v_pool, block_table[b], n, cache_dtype)
         out.append(decode_gqa_dense(q[b], k, v))
-    return np.stack(out) if out else np.zeros((0, NUM_HEADS, HEAD_DIM))
+    return np.stack(out) if out else np.zeros((0, q.shape[1], HEAD_DIM))
 
 
 # ---------------------------------------------------------------------------
@@ -251,7 +265,7 @@ def paged_decode_gqa(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
 
 def norm_rope(q: np.ndarray, k_new: np.ndarray, q_gain: np.ndarray, k_gain: np.ndarray,
               seq_lens: np.ndarray, eps: float = RMS_EPS, theta: float = ROPE_THETA):
-    """q [B,16,128], k_new [B,8,128] -> (q_out, k_rot) at pos = seq_lens - 1."""
+    """q [B,H,128], k_new [B,8,128] -> (q_out, k_rot) at pos = seq_lens - 1."""
     pos = np.asarray(seq_lens, dtype=np.float64) - 1.0
     q_out = rope(qk_norm(q, q_gain, eps), pos, theta)
     k_rot = rope(qk_norm(k_new, k_gain, eps), pos, theta)
@@ -264,10 +278,10 @@ def decode_step(q, k_new, v_new, q_gain, k_gain, k_pool, v_pool, block_table, se
     """One decode step for the selected sequences.
 
     Returns a dict of float64 arrays, one entry per selected sequence:
-      q_out  [n,16,128]  normed and roped query
+      q_out  [n,H,128]   normed and roped query (H = 16 for Qwen3-0.6B)
       k_slot [n,8,128]   value the cache holds at pos after the append
       v_slot [n,8,128]
-      o      [n,16,128]  attention output
+      o      [n,H,128]   attention output
     The pools are read, never modified: the appended position is taken from
     the oracle's own append, every other position from the pools.
     """

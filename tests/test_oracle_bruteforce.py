@@ -42,11 +42,14 @@ def _mp_decode(qh, ks, vs):
     return [sum(e[s] * vs[s][j] for s in range(len(ks))) / tot for j in range(d)]
 
 
-@pytest.mark.parametrize("seq_len,seed", [(1, 0), (5, 1), (17, 2), (33, 3)])
-def test_step_matches_50_digit_brute_force(seq_len, seed):
+@pytest.mark.parametrize("seq_len,seed,H,theta", [(1, 0, 16, 1e6), (5, 1, 16, 1e6), (17, 2, 16, 1e6),
+                                                   (33, 3, 16, 1e6), (9, 4, 32, 5e6), (18, 5, 40, 1e6),
+                                                   (3, 6, 64, 1e6)])
+def test_step_matches_50_digit_brute_force(seq_len, seed, H, theta):
     mp.dps = 50
+    G = H // 8
     r = np.random.default_rng([99, seed])
-    q = r.standard_normal((1, 16, 128))
+    q = r.standard_normal((1, H, 128))
     kn = r.standard_normal((1, 8, 128)) * 2
     vn = r.standard_normal((1, 8, 128))
     wq = 1 + 0.1 * r.standard_normal(128)
@@ -55,21 +58,21 @@ def test_step_matches_50_digit_brute_force(seq_len, seed):
     pool_k = r.standard_normal((npages + 2, 8, 16, 128)).astype(np.float32)
     pool_v = r.standard_normal((npages + 2, 8, 16, 128)).astype(np.float32)
     table = r.permutation(npages + 2)[:npages].astype(np.int32)[None]
-    eps, theta = 1e-6, 1e6
+    eps = 1e-6
     res = O.decode_step(q, kn, vn, wq, wk, pool_k, pool_v, table, np.array([seq_len]), "f32",
                         eps=eps, theta=theta)
 
     pos = seq_len - 1
     to_mp = lambda a: [mpf(float(t)) for t in a]  # noqa: E731
     wq_m, wk_m = to_mp(wq), to_mp(wk)
-    q_rot = [_mp_norm_rope(to_mp(q[0, h]), wq_m, mpf(eps), pos, mpf(theta)) for h in range(16)]
+    q_rot = [_mp_norm_rope(to_mp(q[0, h]), wq_m, mpf(eps), pos, mpf(theta)) for h in range(H)]
     k_rot = [_mp_norm_rope(to_mp(kn[0, g]), wk_m, mpf(eps), pos, mpf(theta)) for g in range(8)]
-    for h in range(16):
+    for h in range(H):
         got = res["q_out"][0, h]
         want = np.array([float(t) for t in q_rot[h]])
         assert np.max(np.abs(got - want)) <= 1e-13 * np.max(np.abs(want))
-    for h in range(16):
-        g = h // 2
+    for h in range(H):
+        g = h // G
         ks, vs = [], []
         for s in range(seq_len):
             if s == pos:

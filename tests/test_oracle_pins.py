@@ -384,3 +384,47 @@ def test_error_metrics():
     ref = np.array([1.0, -4.0, 2.0]); imp = np.array([1.0, -3.5, 2.0])
     assert O.max_abs_err(imp, ref) == 0.5
     assert O.rel_to_max_err(imp, ref) == 0.125
+
+
+# ---------------------------------------------------------------- family sizes
+
+def test_family_sizes_fixture():
+    with open(os.path.join(GOLDEN, "qwen3_family_sizes.json")) as f:
+        c = json.load(f)
+    groups = sorted({(s["num_heads"], s["num_kv_heads"]) for s in c["sizes"]["value"]})
+    assert groups == [(16, 8), (32, 8), (40, 8), (64, 8)]
+    assert [O.group_size(h, kv) for h, kv in groups] == [2, 4, 5, 8]
+    assert c["head_dim"]["value"] == O.HEAD_DIM
+
+
+@pytest.mark.parametrize("H", [16, 32, 40, 64])
+def test_decode_head_mapping_family(H):
+    # KV head j serves query heads j*G .. j*G + G - 1 (G = H / 8): an edit to
+    # KV head j reaches exactly those heads
+    G = H // 8
+    q = _rng(50 + H).standard_normal((H, 128))
+    k, v = _kv(23, 51 + H)
+    o = O.decode_gqa_dense(q, k, v)
+    for j in (0, 3, 7):
+        v2 = v.copy(); v2[:, j] *= 3.0
+        o2 = O.decode_gqa_dense(q, k, v2)
+        changed = [h for h in range(H) if not np.array_equal(o2[h], o[h])]
+        assert changed == list(range(j * G, (j + 1) * G))
+
+
+@pytest.mark.parametrize("H", [32, 40, 64])
+def test_decode_family_single_position_and_uniform(H):
+    q = _rng(60 + H).standard_normal((H, 128))
+    k, v = _kv(1, 61 + H)
+    o = O.decode_gqa_dense(q, k, v)
+    for h in range(H):
+        assert np.array_equal(o[h], v[0, h // (H // 8)])
+    k, v = _kv(31, 62 + H)
+    o = O.decode_gqa_dense(np.zeros((H, 128)), k, v)
+    for h in range(H):
+        np.testing.assert_allclose(o[h], v[:, h // (H // 8)].mean(axis=0), atol=1e-14)
+
+
+def test_group_size_rejects_uneven_heads():
+    with pytest.raises(ValueError):
+        O.group_size(20, 8)
