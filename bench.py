@@ -93,7 +93,7 @@ def cpu_baseline(w, t, seq_lens, table, budget_s):
         t0 = time.perf_counter()
         O.decode_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"],
                       snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
-                      w.cache_dtype)
+                      w.cache_dtype, theta=w.rope_theta)
         elapsed += time.perf_counter() - t0
         done += 1
         kv_bytes += W.algorithmic_kv_bytes(seq_lens[[int(b)]], w.cache_dtype)
@@ -129,8 +129,9 @@ def main():
     t = W.make_layer(w, 0, dev, table=table, num_pages=num_pages, seq_lens=seq_lens)
     B = w.batch
     L = int(seq_lens.max())
-    plan = dah.plan_decode(B, L, args.num_splits)
-    ws_bytes = dah.workspace_bytes(B, L, args.num_splits)
+    H = w.num_heads
+    plan = dah.plan_decode(B, L, args.num_splits, num_heads=H)
+    ws_bytes = dah.workspace_bytes(B, L, args.num_splits, num_heads=H)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     q_out = torch.empty_like(t["q"])
     o = torch.empty_like(t["q"])
@@ -139,7 +140,8 @@ def main():
     def step():
         dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
                              t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L,
-                             num_splits=args.num_splits, q_out=q_out, o=o, workspace=ws)
+                             rope_theta=w.rope_theta, num_splits=args.num_splits, q_out=q_out,
+                             o=o, workspace=ws)
 
     def decode():
         dah.paged_decode_gqa(q_out, t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L,
@@ -219,8 +221,9 @@ def main():
         "config": {
             "workload": w.name,
             "batch": B,
-            "seq_len": "fixed 2048" if w.name == "b256_s2048" else f"max {L}",
-            "heads": "16 q / 8 kv, D=128, page 16",
+            "seq_len": "fixed 2048" if w.name.startswith("b256_s2048") else f"max {L}",
+            "heads": f"{H} q / 8 kv, D=128, page 16",
+            "rope_theta": w.rope_theta,
             "kv_bytes_per_step": kv_bytes,
             "plan": plan["mode"],
             "workgroups": plan["workgroups"],

@@ -14,6 +14,10 @@ computation runs in the library's HIP kernels.
 Cache layout: k_cache / v_cache are [num_pages, 8, 16, 128] tensors of
 float32 or bfloat16 (page, KV head, slot, dim); block_table is int32
 [B, max_pages_per_seq]; seq_lens is int32 [B] and counts the new token.
+
+q, q_out and o are [B, H, 128] with H = 16 (Qwen3-0.6B, the C calls without
+suffix) or another of the family's head counts 32, 40, 64 over the same 8 KV
+heads (the *_ex C calls, chosen from q's shape).
 """
 from __future__ import annotations
 
@@ -24,10 +28,11 @@ from ._native import DAH_BF16, DAH_F32, DahError, LIB_PATH, check, lib
 __all__ = [
     "qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step", "plan_decode",
     "workspace_bytes", "DahError", "LIB_PATH", "NUM_HEADS", "NUM_KV_HEADS", "HEAD_DIM",
-    "PAGE_SIZE",
+    "PAGE_SIZE", "HEAD_COUNTS",
 ]
 
 NUM_HEADS = 16
+HEAD_COUNTS = (16, 32, 40, 64)  # query heads over 8 KV heads: group sizes 2, 4, 5, 8
 NUM_KV_HEADS = 8
 HEAD_DIM = 128
 PAGE_SIZE = 16
@@ -89,7 +94,8 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def plan_decode(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | None = None) -> dict:
+def plan_decode(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | None = None,
+                num_heads: int = NUM_HEADS) -> dict:
     """How the decode will cut the work (dah_plan_decode): a dict with mode
     ("per_sequence", "split" or "balanced"), splits, pages_per_split,
     workgroups and workspace_bytes.  num_cus defaults to the current device's
@@ -99,22 +105,36 @@ def plan_decode(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | No
         torch = _torch()
         num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
     p = DecodePlan()
-    check(lib().dah_plan_decode(B, max_seq_len, num_splits, num_cus, ctypes.byref(p)),
-          "dah_plan_decode")
+    if num_heads == NUM_HEADS:
+        st = lib().dah_plan_decode(B, max_seq_len, num_splits, num_cus, ctypes.byref(p))
+    else:
+        st = lib().dah_plan_decode_ex(B, num_heads, max_seq_len, num_splits, num_cus,
+                                      ctypes.byref(p))
+    check(st, "dah_plan_decode")
     return {"mode": PLAN_MODES[p.mode], "splits": p.splits, "pages_per_split": p.pages_per_split,
             "workgroups": p.workgroups, "workspace_bytes": int(p.workspace_bytes)}
 
 
 def workspace_bytes(B: int, max_seq_len: int, num_splits: int = 0,
-                    num_cus: int | None = None) -> int:
+                    num_cus: int | None = None, num_heads: int = NUM_HEADS) -> int:
+    if num_heads != NUM_HEADS:
+        if num_cus is None:
+            return int(lib().dah_workspace_bytes_ex(B, num_heads, max_seq_len, num_splits))
+        return plan_decode(B, max_seq_len, num_splits, num_cus, num_heads)["workspace_bytes"]
     if num_cus is None:
         return int(lib().dah_workspace_bytes(B, max_seq_len, num_splits))
     return int(lib().dah_workspace_bytes_for(B, max_seq_len, num_splits, num_cus))
 
 
-def _workspace(workspace, B, max_seq_len, num_splits, device):
+def _heads(q) -> int:
+    if q.dim() != 3 or q.shape[1] not in HEAD_COUNTS or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [B, H, 128] with H in {HEAD_COUNTS}, got {tuple(q.shape)}")
+    return int(q.shape[1])
+
+
+def _workspace(workspace, B, H, max_seq_len, num_splits, device):
     torch = _torch()
-    need = workspace_bytes(B, max_seq_len, num_splits)
+    need = workspace_bytes(B, max_seq_len, num_splits, num_heads=H)
     if workspace is None:
         if need == 0:
             return None, 0
@@ -127,11 +147,11 @@ def qk_norm_rope_append(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block
                         seq_lens, *, eps: float = 1e-6, rope_theta: float = 1e6, q_out=None,
                         stream=None):
     """Norm and rotate q and the new k at pos = seq_lens - 1, store k and v
-    in the cache.  Returns q_out [B,16,128] float32 (q_out may be q)."""
+    in the cache.  Returns q_out [B,H,128] float32 (q_out may be q)."""
     torch = _torch()
-    B = q.shape[0]
+    B, H = q.shape[0], _heads(q)
     dev = q.device
-    _require(q, "q", torch.float32, (B, NUM_HEADS, HEAD_DIM))
+    _require(q, "q", torch.float32, (B, H, HEAD_DIM))
     _require(k_new, "k_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
     _require(v_new, "v_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
     _require(q_gain, "q_gain", torch.float32, (HEAD_DIM,), dev)
@@ -139,11 +159,15 @@ def qk_norm_rope_append(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block
     dt = _check_cache(k_cache, v_cache, block_table, seq_lens, B, dev)
     if q_out is None:
         q_out = torch.empty_like(q)
-    _require(q_out, "q_out", torch.float32, (B, NUM_HEADS, HEAD_DIM), dev)
-    st = lib().qk_norm_rope_append(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
-        _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
-        block_table.shape[1], _ptr(seq_lens), B, _ptr(q_out), _stream(dev, stream))
+    _require(q_out, "q_out", torch.float32, (B, H, HEAD_DIM), dev)
+    head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
+            _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), B)
+    tail = (_ptr(q_out), _stream(dev, stream))
+    if H == NUM_HEADS:
+        st = lib().qk_norm_rope_append(*head, *tail)
+    else:
+        st = lib().qk_norm_rope_append_ex(*head, H, *tail)
     check(st, "qk_norm_rope_append")
     return q_out
 
@@ -152,20 +176,24 @@ def paged_decode_gqa(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: in
                      num_splits: int = 0, o=None, workspace=None, stream=None):
     """decodeGQA over the paged cache.  q is already normed and roped.
     max_seq_len bounds every seq_lens[b] (host value, for the planner).
-    Returns o [B,16,128] float32."""
+    Returns o [B,H,128] float32."""
     torch = _torch()
-    B = q.shape[0]
+    B, H = q.shape[0], _heads(q)
     dev = q.device
-    _require(q, "q", torch.float32, (B, NUM_HEADS, HEAD_DIM))
+    _require(q, "q", torch.float32, (B, H, HEAD_DIM))
     dt = _check_cache(k_cache, v_cache, block_table, seq_lens, B, dev)
     if o is None:
         o = torch.empty_like(q)
-    _require(o, "o", torch.float32, (B, NUM_HEADS, HEAD_DIM), dev)
-    ws, ws_bytes = _workspace(workspace, B, max_seq_len, num_splits, dev)
-    st = lib().paged_decode_gqa(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
-        block_table.shape[1], _ptr(seq_lens), B, int(max_seq_len), int(num_splits), _ptr(o),
-        None if ws is None else _ptr(ws), ws_bytes, _stream(dev, stream))
+    _require(o, "o", torch.float32, (B, H, HEAD_DIM), dev)
+    ws, ws_bytes = _workspace(workspace, B, H, max_seq_len, num_splits, dev)
+    head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), B)
+    tail = (int(max_seq_len), int(num_splits), _ptr(o), None if ws is None else _ptr(ws),
+            ws_bytes, _stream(dev, stream))
+    if H == NUM_HEADS:
+        st = lib().paged_decode_gqa(*head, *tail)
+    else:
+        st = lib().paged_decode_gqa_ex(*head, H, *tail)
     check(st, "paged_decode_gqa")
     return o
 
@@ -176,9 +204,9 @@ def decode_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_ta
     """One decode step of one layer: norm, RoPE, cache append, decodeGQA.
     Returns (q_out, o)."""
     torch = _torch()
-    B = q.shape[0]
+    B, H = q.shape[0], _heads(q)
     dev = q.device
-    _require(q, "q", torch.float32, (B, NUM_HEADS, HEAD_DIM))
+    _require(q, "q", torch.float32, (B, H, HEAD_DIM))
     _require(k_new, "k_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
     _require(v_new, "v_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
     _require(q_gain, "q_gain", torch.float32, (HEAD_DIM,), dev)
@@ -188,13 +216,17 @@ def decode_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_ta
         q_out = torch.empty_like(q)
     if o is None:
         o = torch.empty_like(q)
-    _require(q_out, "q_out", torch.float32, (B, NUM_HEADS, HEAD_DIM), dev)
-    _require(o, "o", torch.float32, (B, NUM_HEADS, HEAD_DIM), dev)
-    ws, ws_bytes = _workspace(workspace, B, max_seq_len, num_splits, dev)
-    st = lib().decode_attn_step(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
-        _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
-        block_table.shape[1], _ptr(seq_lens), B, int(max_seq_len), int(num_splits), _ptr(q_out),
-        _ptr(o), None if ws is None else _ptr(ws), ws_bytes, _stream(dev, stream))
+    _require(q_out, "q_out", torch.float32, (B, H, HEAD_DIM), dev)
+    _require(o, "o", torch.float32, (B, H, HEAD_DIM), dev)
+    ws, ws_bytes = _workspace(workspace, B, H, max_seq_len, num_splits, dev)
+    head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
+            _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), B)
+    tail = (int(max_seq_len), int(num_splits), _ptr(q_out), _ptr(o),
+            None if ws is None else _ptr(ws), ws_bytes, _stream(dev, stream))
+    if H == NUM_HEADS:
+        st = lib().decode_attn_step(*head, *tail)
+    else:
+        st = lib().decode_attn_step_ex(*head, H, *tail)
     check(st, "decode_attn_step")
     return q_out, o

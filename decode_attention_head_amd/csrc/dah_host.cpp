@@ -43,14 +43,22 @@ int set_error(int status, const char* fmt, ...) {
 void clear_error() { g_last_error[0] = '\0'; }
 
 namespace {
-size_t partial_bytes(long long slots) {
-  return static_cast<size_t>(slots) * kHeads * (kHeadDim + 2) * sizeof(float);
+size_t partial_bytes(long long slots, int num_heads) {
+  return static_cast<size_t>(slots) * num_heads * (kHeadDim + 2) * sizeof(float);
+}
+
+int check_heads(int num_heads) {
+  if (!valid_heads(num_heads))
+    return set_error(DAH_ERR_SHAPE, "num_heads = %d, need 16, 32, 40 or 64 (over 8 KV heads)",
+                     num_heads);
+  return DAH_OK;
 }
 }  // namespace
 
-int plan_decode(int B, int max_seq_len, int num_splits, int num_cus, Plan* out) {
+int plan_decode(int B, int num_heads, int max_seq_len, int num_splits, int num_cus, Plan* out) {
   if (out == nullptr) return set_error(DAH_ERR_NULL, "plan_decode: output pointer is NULL");
   if (B < 1) return set_error(DAH_ERR_SHAPE, "B = %d, need B >= 1", B);
+  if (check_heads(num_heads) != DAH_OK) return DAH_ERR_SHAPE;
   if (max_seq_len < 1)
     return set_error(DAH_ERR_SHAPE, "max_seq_len = %d, need >= 1", max_seq_len);
   if (num_splits < 0)
@@ -97,7 +105,7 @@ int plan_decode(int B, int max_seq_len, int num_splits, int num_cus, Plan* out) 
       p.pages_per_split = 0;
       p.grid_splits = 0;
       p.workgroups = num_cus * kBalancedGroupsPerCu;
-      p.workspace = partial_bytes(static_cast<long long>(B) + p.workgroups - 1);
+      p.workspace = partial_bytes(static_cast<long long>(B) + p.workgroups - 1, num_heads);
       break;
     default: {
       const int pps = (max_pages + want - 1) / want;
@@ -113,7 +121,7 @@ int plan_decode(int B, int max_seq_len, int num_splits, int num_cus, Plan* out) 
         const long long wg = static_cast<long long>(B) * p.grid_splits;
         if (wg > INT32_MAX) return set_error(DAH_ERR_SHAPE, "grid of %lld workgroups too large", wg);
         p.workgroups = static_cast<int>(wg);
-        p.workspace = partial_bytes(static_cast<long long>(B) * p.splits);
+        p.workspace = partial_bytes(static_cast<long long>(B) * p.splits, num_heads);
       }
     }
   }
@@ -125,7 +133,7 @@ int validate_append(const void* q, const void* k_new, const void* v_new, const v
                     const void* k_gain, float eps, float rope_theta, const void* k_cache,
                     const void* v_cache, int cache_dtype, int64_t num_pages,
                     const void* block_table, int max_pages_per_seq, const void* seq_lens, int B,
-                    const void* q_out) {
+                    int num_heads, const void* q_out) {
   if (!q || !k_new || !v_new || !q_gain || !k_gain || !k_cache || !v_cache || !block_table ||
       !seq_lens || !q_out)
     return set_error(DAH_ERR_NULL, "qk_norm_rope_append: a required pointer is NULL");
@@ -133,6 +141,7 @@ int validate_append(const void* q, const void* k_new, const void* v_new, const v
     return set_error(DAH_ERR_DTYPE, "cache_dtype = %d, need DAH_F32 (0) or DAH_BF16 (1)",
                      cache_dtype);
   if (B < 1) return set_error(DAH_ERR_SHAPE, "B = %d, need B >= 1", B);
+  if (check_heads(num_heads) != DAH_OK) return DAH_ERR_SHAPE;
   if (num_pages < 1 || num_pages > INT32_MAX)
     return set_error(DAH_ERR_SHAPE, "num_pages = %lld, need 1 <= num_pages <= 2^31-1",
                      static_cast<long long>(num_pages));
@@ -151,13 +160,15 @@ int validate_append(const void* q, const void* k_new, const void* v_new, const v
 
 int validate_decode(const void* q, const void* k_cache, const void* v_cache, int cache_dtype,
                     int64_t num_pages, const void* block_table, int max_pages_per_seq,
-                    const void* seq_lens, int B, int max_seq_len, int num_splits, const void* o) {
+                    const void* seq_lens, int B, int num_heads, int max_seq_len, int num_splits,
+                    const void* o) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
     return set_error(DAH_ERR_NULL, "paged_decode_gqa: a required pointer is NULL");
   if (cache_dtype != DAH_F32 && cache_dtype != DAH_BF16)
     return set_error(DAH_ERR_DTYPE, "cache_dtype = %d, need DAH_F32 (0) or DAH_BF16 (1)",
                      cache_dtype);
   if (B < 1) return set_error(DAH_ERR_SHAPE, "B = %d, need B >= 1", B);
+  if (check_heads(num_heads) != DAH_OK) return DAH_ERR_SHAPE;
   if (num_pages < 1 || num_pages > INT32_MAX)
     return set_error(DAH_ERR_SHAPE, "num_pages = %lld, need 1 <= num_pages <= 2^31-1",
                      static_cast<long long>(num_pages));
@@ -183,10 +194,11 @@ int validate_decode(const void* q, const void* k_cache, const void* v_cache, int
 
 extern "C" {
 
-int dah_plan_decode(int B, int max_seq_len, int num_splits, int num_cus, dah_decode_plan* out) {
+int dah_plan_decode_ex(int B, int num_heads, int max_seq_len, int num_splits, int num_cus,
+                       dah_decode_plan* out) {
   if (!out) return dah::set_error(DAH_ERR_NULL, "dah_plan_decode: output pointer is NULL");
   dah::Plan p;
-  int st = dah::plan_decode(B, max_seq_len, num_splits, num_cus, &p);
+  int st = dah::plan_decode(B, num_heads, max_seq_len, num_splits, num_cus, &p);
   if (st != DAH_OK) return st;
   out->mode = p.mode;
   out->splits = p.splits;
@@ -196,9 +208,13 @@ int dah_plan_decode(int B, int max_seq_len, int num_splits, int num_cus, dah_dec
   return DAH_OK;
 }
 
+int dah_plan_decode(int B, int max_seq_len, int num_splits, int num_cus, dah_decode_plan* out) {
+  return dah_plan_decode_ex(B, dah::kHeads, max_seq_len, num_splits, num_cus, out);
+}
+
 size_t dah_workspace_bytes_for(int B, int max_seq_len, int num_splits, int num_cus) {
   dah::Plan p;
-  if (dah::plan_decode(B, max_seq_len, num_splits, num_cus, &p) != DAH_OK) return 0;
+  if (dah::plan_decode(B, dah::kHeads, max_seq_len, num_splits, num_cus, &p) != DAH_OK) return 0;
   return p.workspace;
 }
 

@@ -8,10 +8,14 @@
 
 namespace dah {
 
-constexpr int kHeads = 16;     // query heads
-constexpr int kKvHeads = 8;    // key/value heads; query head h reads KV head h / 2
+constexpr int kHeads = 16;     // query heads of Qwen3-0.6B (the default entry points)
+constexpr int kKvHeads = 8;    // key/value heads; query head h reads KV head h / (H / 8)
 constexpr int kHeadDim = 128;  // head dimension
 constexpr int kPage = 16;      // positions per cache page
+
+// Query-head counts the kernels are built for: the Qwen3 family's 16, 32, 40
+// and 64 heads over 8 KV heads (2, 4, 5, 8 query heads per KV head).
+inline bool valid_heads(int h) { return h == 16 || h == 32 || h == 40 || h == 64; }
 
 // Records `msg` (printf-style) as this thread's last error and returns status.
 int set_error(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -29,17 +33,19 @@ struct Plan {
 };
 
 // Planner: pure integer policy from the batch size, the longest sequence and
-// the compute-unit count.  Returns a dah_status.
-int plan_decode(int B, int max_seq_len, int num_splits, int num_cus, Plan* out);
+// the compute-unit count; the head count sizes the workspace.  Returns a
+// dah_status.
+int plan_decode(int B, int num_heads, int max_seq_len, int num_splits, int num_cus, Plan* out);
 
 int validate_append(const void* q, const void* k_new, const void* v_new, const void* q_gain,
                     const void* k_gain, float eps, float rope_theta, const void* k_cache,
                     const void* v_cache, int cache_dtype, int64_t num_pages,
                     const void* block_table, int max_pages_per_seq, const void* seq_lens, int B,
-                    const void* q_out);
+                    int num_heads, const void* q_out);
 
 int validate_decode(const void* q, const void* k_cache, const void* v_cache, int cache_dtype,
                     int64_t num_pages, const void* block_table, int max_pages_per_seq,
-                    const void* seq_lens, int B, int max_seq_len, int num_splits, const void* o);
+                    const void* seq_lens, int B, int num_heads, int max_seq_len, int num_splits,
+                    const void* o);
 
 }  // namespace dah

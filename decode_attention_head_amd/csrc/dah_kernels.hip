@@ -10,8 +10,9 @@
 // the specs").
 //
 // Decode design.  The work is HBM-bound: every cached position costs 4 KiB of
-// K and V (bf16) and ~1 flop per byte.  One wavefront owns one
-// (sequence, KV head, split) and both query heads 2g, 2g+1 of that KV head.
+// K and V (bf16) and ~G flops per byte.  One wavefront owns one
+// (sequence, KV head g, split) and all G query heads gG .. gG+G-1 of that KV
+// head (G = 2 for Qwen3-0.6B; 4, 5, 8 for the family's larger members).
 // A (page, KV head) tile is 16 positions x 128 dims, contiguous (4 KiB bf16).
 // Lane l = 16*r + c holds dims 8c..8c+7 of positions 4j+r, j = 0..3: each of
 // the four 16-byte loads per tile is a fully coalesced 1 KiB wave access.
@@ -25,6 +26,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "dah.h"
 #include "dah_host.h"
@@ -193,47 +195,50 @@ __device__ __forceinline__ float softmax_update(HeadState& st, const float (&s)[
   return alpha;
 }
 
-// Consume one (page, KV head) tile for the two query heads.
-template <int kDtype, bool kMasked>
+// Consume one (page, KV head) tile for the kG query heads of that KV head
+// (kG = 2 for Qwen3-0.6B).
+template <int kDtype, bool kMasked, int kG>
 __device__ __forceinline__ void attend_tile(const Tile<kDtype>& K, Tile<kDtype>& V,
-                                            const float (&qa)[8], const float (&qb)[8],
-                                            HeadState& A, HeadState& Bs, int row, int nvalid) {
-  float sa[4], sb[4];
+                                            const float (&q)[kG][8], HeadState (&st)[kG],
+                                            int row, int nvalid) {
+  float sc[kG][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float pa = 0.0f, pb = 0.0f;
+    float part[kG];
+#pragma unroll
+    for (int h = 0; h < kG; ++h) part[h] = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float k = K.get(j, e);
-      pa = fmaf(qa[e], k, pa);
-      pb = fmaf(qb[e], k, pb);
+#pragma unroll
+      for (int h = 0; h < kG; ++h) part[h] = fmaf(q[h][e], k, part[h]);
     }
-    sa[j] = row_sum16(pa);
-    sb[j] = row_sum16(pb);
+#pragma unroll
+    for (int h = 0; h < kG; ++h) sc[h][j] = row_sum16(part[h]);
     if (kMasked) {
       // Positions at or past seq_len may hold anything (NaN included): the
       // select keeps them out of both the scores and the V sum.
       const bool ok = (4 * j + row) < nvalid;
-      sa[j] = ok ? sa[j] : -INFINITY;
-      sb[j] = ok ? sb[j] : -INFINITY;
+#pragma unroll
+      for (int h = 0; h < kG; ++h) sc[h][j] = ok ? sc[h][j] : -INFINITY;
       if (!ok) V.clear(j);
     }
   }
-  float wa[4], wb[4];
-  const float ala = softmax_update<kMasked>(A, sa, wa);
-  const float alb = softmax_update<kMasked>(Bs, sb, wb);
+  float w[kG][4], alpha[kG];
+#pragma unroll
+  for (int h = 0; h < kG; ++h) alpha[h] = softmax_update<kMasked>(st[h], sc[h], w[h]);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    A.acc[e] *= ala;
-    Bs.acc[e] *= alb;
+#pragma unroll
+    for (int h = 0; h < kG; ++h) st[h].acc[e] *= alpha[h];
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float v = V.get(j, e);
-      A.acc[e] = fmaf(wa[j], v, A.acc[e]);
-      Bs.acc[e] = fmaf(wb[j], v, Bs.acc[e]);
+#pragma unroll
+      for (int h = 0; h < kG; ++h) st[h].acc[e] = fmaf(w[h][j], v, st[h].acc[e]);
     }
   }
 }
@@ -339,9 +344,9 @@ struct DecodeArgs {
   int grid_splits;  // splits rounded up to a multiple of 8 (1 when splits == 1)
   int pages_per_split;
   float* o;
-  // Partial results: DAH_PLAN_SPLIT slot (b*16 + h)*splits + split,
-  // DAH_PLAN_BALANCED slot (b + workgroup)*16 + h; 128 floats of weighted V
-  // sum each, then one float2 (running max in log2 units, sum) each.
+  // Partial results (H query heads): DAH_PLAN_SPLIT slot (b*H + h)*splits +
+  // split, DAH_PLAN_BALANCED slot (b + workgroup)*H + h; 128 floats of
+  // weighted V sum each, then one float2 (running max in log2 units, sum) each.
   float* part_acc;
   float* part_ml;
   // The fused step only: q above is the raw (pre-norm) query.
@@ -364,43 +369,54 @@ __device__ __forceinline__ void store8(float* dst, const float (&v)[8], float sc
 
 // LDS a workgroup of the fused step uses to hold outputs until the end of a
 // range (see decode_range).
+template <int kG>
 struct StepStash {
-  u32x4 kv[kDecodeWavesPerBlock][2][2][16];  // [wave][k|v][word][column]
-  float4 q[kDecodeWavesPerBlock][2][2][16];  // [wave][head][half][column]
+  u32x4 kv[kDecodeWavesPerBlock][2][2][16];   // [wave][k|v][word][column]
+  float4 q[kDecodeWavesPerBlock][kG][2][16];  // [wave][head][half][column]
 };
+
+// Query head h (< kG) of KV head g is written by the wave rows r with
+// r = h mod 4 (after merge_rows every row holds every head's result).
+__device__ __forceinline__ bool row_writes(int row, int h) { return row == (h & 3); }
 
 // The fused step for a sequence with nothing to attend to (seq_len out of
 // range): q_out is still the normed query, rotated at pos = seq_len - 1 (or 0).
-template <int kDtype>
+template <int kDtype, int kG>
 __device__ void step_q_out_only(const DecodeArgs& a, int b, int seq_len, int g, int lane) {
+  constexpr int kH = kG * kKvHeads;
   const int row = lane >> 4, col = lane & 15;
-  float qa[8], qb[8], qw[8], cr[8], sr[8];
-  load8(a.q + ((size_t)b * kHeads + 2 * g) * kHeadDim + 8 * col, qa);
-  load8(a.q + ((size_t)b * kHeads + 2 * g + 1) * kHeadDim + 8 * col, qb);
+  float qw[8], cr[8], sr[8];
   load8(a.q_gain + 8 * col, qw);
   rope_table(seq_len >= 1 ? seq_len - 1 : 0, a.rope, lane, col, cr, sr);
-  norm_rope_row(qa, qw, a.eps, cr, sr, col);
-  norm_rope_row(qb, qw, a.eps, cr, sr, col);
-  if (row < 2) store8(a.q_out + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col,
-                      row == 0 ? qa : qb, 1.0f);
+#pragma unroll
+  for (int h = 0; h < kG; ++h) {
+    float q[8];
+    const size_t rowoff = ((size_t)b * kH + g * kG + h) * kHeadDim + 8 * col;
+    load8(a.q + rowoff, q);
+    norm_rope_row(q, qw, a.eps, cr, sr, col);
+    if (row_writes(row, h)) store8(a.q_out + rowoff, q, 1.0f);
+  }
 }
 
-// decodeGQA of one KV head (this wave: g) and its query heads 2g, 2g+1 over
-// pages [p0, p1) of sequence b (p0 < p1 <= npages).  The result goes to o
-// when the range is the whole sequence (to_o), else to the partial slots
-// part_base + h * part_stride as (weighted V sum, running max, sum).
+// decodeGQA of one KV head (this wave: g) and its kG query heads over pages
+// [p0, p1) of sequence b (p0 < p1 <= npages).  The result goes to o when the
+// range is the whole sequence (to_o), else to the partial slots
+// part_base + h * part_stride (h = query head) as (weighted V sum, running
+// max, sum).
 // kStep, the fused decode step: q arrives raw and is normed and rotated here
 // (write_q: this range also writes q_out), and the range holding the
 // sequence's last page norms and rotates the new key, folds the new token in
 // from registers and stores the new key and value in the cache.
-template <int kDtype, bool kStep>
+template <int kDtype, bool kStep, int kG>
 __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq_len, int npages,
                                              int p0, int p1, bool write_q, bool to_o,
                                              size_t part_base, int part_stride, int g, int lane,
-                                             StepStash& stash) {
+                                             StepStash<kG>& stash) {
+  constexpr int kH = kG * kKvHeads;
   const int wave = g;
   const int row = lane >> 4;
   const int col = lane & 15;
+  const size_t qrow0 = (size_t)b * kH + g * kG;  // first query head row of this KV head
 
   // The block table is read-only for the whole launch: reading it through the
   // constant address space makes every (uniform) read a scalar load, counted
@@ -432,10 +448,10 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
 
   // The small per-wave loads go first: vector loads complete in order, so the
   // prologue's wait for them must not also wait for the first tile.
-  // Query rows 2g and 2g+1, this lane's 8 dims (raw in the fused step).
-  float qa[8], qb[8];
-  load8(a.q + ((size_t)b * kHeads + 2 * g) * kHeadDim + 8 * col, qa);
-  load8(a.q + ((size_t)b * kHeads + 2 * g + 1) * kHeadDim + 8 * col, qb);
+  // Query rows of this KV head, this lane's 8 dims (raw in the fused step).
+  float q[kG][8];
+#pragma unroll
+  for (int h = 0; h < kG; ++h) load8(a.q + (qrow0 + h) * kHeadDim + 8 * col, q[h]);
   float qw[8], kx[8], vx[8], kw8[8];
   if constexpr (kStep) {
     load8(a.q_gain + 8 * col, qw);
@@ -465,12 +481,13 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
     const int pos = seq_len - 1;
     float cr[8], sr[8];
     rope_table(pos, a.rope, lane, col, cr, sr);
-    norm_rope_row(qa, qw, a.eps, cr, sr, col);
-    norm_rope_row(qb, qw, a.eps, cr, sr, col);
-    if (write_q && row < 2) {
-      const float (&q)[8] = row == 0 ? qa : qb;
-      stash.q[wave][row][0][col] = make_float4(q[0], q[1], q[2], q[3]);
-      stash.q[wave][row][1][col] = make_float4(q[4], q[5], q[6], q[7]);
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+      norm_rope_row(q[h], qw, a.eps, cr, sr, col);
+      if (write_q && row_writes(row, h)) {
+        stash.q[wave][h][0][col] = make_float4(q[h][0], q[h][1], q[h][2], q[h][3]);
+        stash.q[wave][h][1][col] = make_float4(q[h][4], q[h][5], q[h][6], q[h][7]);
+      }
     }
     if (holds_last) {
       norm_rope_row(kx, kw8, a.eps, cr, sr, col);
@@ -488,14 +505,13 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
   // Pre-scale by log2(e)/sqrt(128) so that scores come out in log2 units for exp2.
   const float qscale = kLog2e * 0.08838834764831845f;  // 1/sqrt(128)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    qa[e] *= qscale;
-    qb[e] *= qscale;
-  }
+  for (int h = 0; h < kG; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[h][e] *= qscale;
 
-  HeadState A, Bs;
-  A.init();
-  Bs.init();
+  HeadState st[kG];
+#pragma unroll
+  for (int h = 0; h < kG; ++h) st[h].init();
 
   // Software pipeline over the pages: the tile of page p+1 is in flight while
   // page p is consumed.  In the steady-state loop both following pages exist,
@@ -511,14 +527,14 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
     V1.load(vbase + off1, lane);
     const int id3 = bt[min(p + 3, last)];
     __builtin_amdgcn_sched_barrier(0);
-    attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
+    attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
     __builtin_amdgcn_sched_barrier(0);
     const int64_t off2 = offset_of(id2);
     K0.load(kbase + off2, lane);
     V0.load(vbase + off2, lane);
     const int id4 = bt[min(p + 4, last)];
     __builtin_amdgcn_sched_barrier(0);
-    attend_tile<kDtype, false>(K1, V1, qa, qb, A, Bs, row, kPage);
+    attend_tile<kDtype, false, kG>(K1, V1, q, st, row, kPage);
     __builtin_amdgcn_sched_barrier(0);
     id1 = id3;
     id2 = id4;
@@ -528,17 +544,17 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
     K1.load(kbase + off1, lane);
     V1.load(vbase + off1, lane);
     __builtin_amdgcn_sched_barrier(0);
-    attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
+    attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
     __builtin_amdgcn_sched_barrier(0);
     if (last_masked)
-      attend_tile<kDtype, true>(K1, V1, qa, qb, A, Bs, row, last_valid);
+      attend_tile<kDtype, true, kG>(K1, V1, q, st, row, last_valid);
     else
-      attend_tile<kDtype, false>(K1, V1, qa, qb, A, Bs, row, kPage);
+      attend_tile<kDtype, false, kG>(K1, V1, q, st, row, kPage);
   } else {
     if (last_masked)
-      attend_tile<kDtype, true>(K0, V0, qa, qb, A, Bs, row, last_valid);
+      attend_tile<kDtype, true, kG>(K0, V0, q, st, row, last_valid);
     else
-      attend_tile<kDtype, false>(K0, V0, qa, qb, A, Bs, row, kPage);
+      attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
   }
   if constexpr (kStep) {
     // The new token (slot tail - 1 of the last page, read from the cache
@@ -554,43 +570,43 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
       float kf[8], vf[8];
       unpack_slot<kDtype>(kw, kf);
       unpack_slot<kDtype>(vw, vf);
-      float sa = 0.0f, sb = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sa = fmaf(qa[e], kf[e], sa);
-        sb = fmaf(qb[e], kf[e], sb);
-      }
-      sa = row_sum16(sa);
-      sb = row_sum16(sb);
       const bool mine = row == ((tail - 1) & 3);
-      attend_one(A, mine ? sa : -INFINITY, vf);
-      attend_one(Bs, mine ? sb : -INFINITY, vf);
+#pragma unroll
+      for (int h = 0; h < kG; ++h) {
+        float sc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc = fmaf(q[h][e], kf[e], sc);
+        sc = row_sum16(sc);
+        attend_one(st[h], mine ? sc : -INFINITY, vf);
+      }
     }
   }
 
-  merge_rows(A);
-  merge_rows(Bs);
-  if (bad_page) {
-    A.l = NAN;
-    Bs.l = NAN;
+#pragma unroll
+  for (int h = 0; h < kG; ++h) {
+    merge_rows(st[h]);
+    if (bad_page) st[h].l = NAN;
   }
-
-  if (row < 2) {
-    const HeadState& st = row == 0 ? A : Bs;
-    const int h = 2 * g + row;
+#pragma unroll
+  for (int h = 0; h < kG; ++h) {
+    if (!row_writes(row, h)) continue;
     if (to_o) {
-      store8(a.o + ((size_t)b * kHeads + h) * kHeadDim + 8 * col, st.acc, 1.0f / st.l);
+      store8(a.o + (qrow0 + h) * kHeadDim + 8 * col, st[h].acc, 1.0f / st[h].l);
     } else {
-      const size_t part = part_base + (size_t)h * part_stride;
-      store8(a.part_acc + part * kHeadDim + 8 * col, st.acc, bad_page ? NAN : 1.0f);
-      if (col == 0) reinterpret_cast<float2*>(a.part_ml)[part] = make_float2(st.m, st.l);
+      const size_t part = part_base + (size_t)(g * kG + h) * part_stride;
+      store8(a.part_acc + part * kHeadDim + 8 * col, st[h].acc, bad_page ? NAN : 1.0f);
+      if (col == 0) reinterpret_cast<float2*>(a.part_ml)[part] = make_float2(st[h].m, st[h].l);
     }
   }
   if constexpr (kStep) {
-    if (write_q && row < 2) {
-      float* qo = a.q_out + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col;
-      reinterpret_cast<float4*>(qo)[0] = stash.q[wave][row][0][col];
-      reinterpret_cast<float4*>(qo)[1] = stash.q[wave][row][1][col];
+    if (write_q) {
+#pragma unroll
+      for (int h = 0; h < kG; ++h) {
+        if (!row_writes(row, h)) continue;
+        float* qo = a.q_out + (qrow0 + h) * kHeadDim + 8 * col;
+        reinterpret_cast<float4*>(qo)[0] = stash.q[wave][h][0][col];
+        reinterpret_cast<float4*>(qo)[1] = stash.q[wave][h][1][col];
+      }
     }
     if (holds_last && row == 0) {
       // The new token's slot: page block_table[b][npages-1], slot tail - 1.
@@ -615,19 +631,21 @@ __device__ __forceinline__ int pages_of(int seq_len, int max_seq_len) {
 }
 
 // Empty sequence (seq_len <= 0: o = 0; past max_seq_len: o = NaN).
+template <int kG>
 __device__ __forceinline__ void fill_o(const DecodeArgs& a, int b, int seq_len, int g, int lane) {
   const int row = lane >> 4, col = lane & 15;
-  if (row < 2) {
-    const float fill = seq_len <= 0 ? 0.0f : NAN;
-    const float z[8] = {fill, fill, fill, fill, fill, fill, fill, fill};
-    store8(a.o + ((size_t)b * kHeads + 2 * g + row) * kHeadDim + 8 * col, z, 1.0f);
-  }
+  const float fill = seq_len <= 0 ? 0.0f : NAN;
+  const float z[8] = {fill, fill, fill, fill, fill, fill, fill, fill};
+#pragma unroll
+  for (int h = 0; h < kG; ++h)
+    if (row_writes(row, h))
+      store8(a.o + ((size_t)b * kG * kKvHeads + g * kG + h) * kHeadDim + 8 * col, z, 1.0f);
 }
 
 // One workgroup (8 waves = 8 KV heads) per (sequence, split), each split
 // `pages_per_split` pages; splits == 1 writes o directly, otherwise
 // combine_splits_kernel merges the partials.
-template <int kDtype, bool kStep>
+template <int kDtype, bool kStep, int kG>
 __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   // The wave index is uniform across the wave; saying so keeps everything
@@ -657,13 +675,14 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
   if (p0 >= p1 || split >= a.splits) {
     // Nothing to attend to.  With one split this is the whole sequence; with
     // several, the combine kernel reads only non-empty ranges.
-    if (kStep && split == 0) step_q_out_only<kDtype>(a, b, seq_len, g, lane);
-    if (a.splits == 1) fill_o(a, b, seq_len, g, lane);
+    if (kStep && split == 0) step_q_out_only<kDtype, kG>(a, b, seq_len, g, lane);
+    if (a.splits == 1) fill_o<kG>(a, b, seq_len, g, lane);
     return;
   }
-  __shared__ StepStash stash;
-  decode_range<kDtype, kStep>(a, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
-                              ((size_t)b * kHeads) * a.splits + split, a.splits, g, lane, stash);
+  __shared__ StepStash<kG> stash;
+  decode_range<kDtype, kStep, kG>(a, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
+                                  ((size_t)b * kG * kKvHeads) * a.splits + split, a.splits, g,
+                                  lane, stash);
 }
 
 // Balanced decode: the batch's pages, in sequence order, are cut into
@@ -673,13 +692,14 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
 // b + k (k = workgroup), which combine_balanced_kernel merges.  Consecutive
 // workgroups go to different XCDs, so every XCD gets an equal share of the
 // pages however ragged the lengths are, and no workgroup is empty.
-template <int kDtype, bool kStep>
+template <int kDtype, bool kStep, int kG>
 __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_kernel(DecodeArgs a) {
+  constexpr int kH = kG * kKvHeads;
   const int lane = threadIdx.x & (kWave - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head
   __shared__ int prefix[kMaxBalancedBatch + 1];  // prefix[b] = pages of sequences < b
   __shared__ int wave_total[kDecodeWavesPerBlock];
-  __shared__ StepStash stash;
+  __shared__ StepStash<kG> stash;
 
   // Block-wide exclusive scan of the page counts; thread t owns sequences
   // 8t .. 8t+7.
@@ -717,7 +737,7 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
     // Sequences with nothing to attend to still get q_out (workgroup 0).
     if (blockIdx.x == 0)
       for (int bb = 0; bb < a.B; ++bb)
-        if (prefix[bb + 1] == prefix[bb]) step_q_out_only<kDtype>(a, bb, a.seq_lens[bb], g, lane);
+        if (prefix[bb + 1] == prefix[bb]) step_q_out_only<kDtype, kG>(a, bb, a.seq_lens[bb], g, lane);
   }
 
   const long long T = prefix[a.B];
@@ -740,8 +760,8 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
     const int npages = next - base;
     const int p0 = s - base, p1 = seg_end - base;
     const bool whole = p0 == 0 && p1 == npages;
-    decode_range<kDtype, kStep>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
-                                (size_t)(b + k) * kHeads, 1, g, lane, stash);
+    decode_range<kDtype, kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
+                                    (size_t)(b + k) * kH, 1, g, lane, stash);
     s = seg_end;
     if (s >= e) break;
     do { ++b; } while (prefix[b + 1] == prefix[b]);  // next sequence with pages
@@ -762,17 +782,17 @@ constexpr int kCombineGroups = kCombineThreads / 32;
 
 // Partial i of a row: split layout (row-major splits, all present).
 struct SplitParts {
-  size_t base;  // (b * 16 + h) * splits
+  size_t base;  // (b * H + h) * splits
   __device__ size_t slot(int i) const { return base + i; }
   __device__ bool present(int) const { return true; }
 };
 
-// Partial i of a row: balanced layout, slot (b + k0 + i) * 16 + h; a
+// Partial i of a row: balanced layout, slot (b + k0 + i) * H + h; a
 // workgroup whose page range was empty wrote nothing.
 struct BalancedParts {
-  int b, h, k0;
+  int b, h, k0, H;
   long long T, G;
-  __device__ size_t slot(int i) const { return (size_t)(b + k0 + i) * kHeads + h; }
+  __device__ size_t slot(int i) const { return (size_t)(b + k0 + i) * H + h; }
   __device__ bool present(int i) const {
     const long long k = k0 + i;
     return T >= G || k * T / G < (k + 1) * T / G;
@@ -847,10 +867,10 @@ __device__ __forceinline__ void fill_row(float* out_row, int seq_len) {
 // DAH_PLAN_SPLIT: the non-empty splits of each (sequence, head).
 __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, int B, int max_seq_len, int splits, int pages_per_split,
-    float* __restrict__ o) {
-  const int unit = blockIdx.x;  // b * 16 + h
-  const int b = unit / kHeads;
+    const int32_t* __restrict__ seq_lens, int B, int H, int max_seq_len, int splits,
+    int pages_per_split, float* __restrict__ o) {
+  const int unit = blockIdx.x;  // b * H + h
+  const int b = unit / H;
   const int seq_len = seq_lens[b];
   float* out_row = o + (size_t)unit * kHeadDim;
   if (seq_len < 1 || seq_len > max_seq_len) {
@@ -869,11 +889,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
 // sequence seen by one workgroup was written to o directly.
 __global__ __launch_bounds__(kCombineThreads) void combine_balanced_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, int B, int max_seq_len, int G, float* __restrict__ o) {
+    const int32_t* __restrict__ seq_lens, int B, int H, int max_seq_len, int G,
+    float* __restrict__ o) {
   __shared__ int red[2][kCombineThreads / kWave];
-  const int unit = blockIdx.x;  // b * 16 + h
-  const int b = unit / kHeads;
-  const int h = unit - b * kHeads;
+  const int unit = blockIdx.x;  // b * H + h
+  const int b = unit / H;
+  const int h = unit - b * H;
   const int seq_len = seq_lens[b];
   float* out_row = o + (size_t)unit * kHeadDim;
   if (seq_len < 1 || seq_len > max_seq_len) {
@@ -904,7 +925,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_balanced_kernel(
   const int k0 = (int)(((P + 1) * G - 1) / T);
   const int k1 = (int)(((last + 1) * G - 1) / T);
   if (k0 == k1) return;
-  merge_parts(part_acc, part_ml, BalancedParts{b, h, k0, T, (long long)G}, k1 - k0 + 1, out_row);
+  merge_parts(part_acc, part_ml, BalancedParts{b, h, k0, H, T, (long long)G}, k1 - k0 + 1, out_row);
 }
 
 // ------------------------------------------------------------ norm + RoPE + append
@@ -945,10 +966,12 @@ __device__ __forceinline__ void rotate(float& x0, float& x1, float c, float s) {
   x1 = y1;
 }
 
-// One block of 8 waves per sequence.  Wave w handles query heads w and w+8,
-// key head w and value head w; lane i holds dims i and i+64 (a RoPE pair).
-template <int kDtype>
+// One block of 8 waves per sequence.  Wave w handles query heads w, w+8, ...
+// (kG of them), key head w and value head w; lane i holds dims i and i+64 (a
+// RoPE pair).
+template <int kDtype, int kG>
 __global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
+  constexpr int kH = kG * kKvHeads;
   __shared__ float2 cs[64];
   const int b = blockIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -963,26 +986,31 @@ __global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
     cs[lane] = make_float2(cn, sn);
   }
   // Load while wave 0 computes the angles.
-  const size_t qbase0 = ((size_t)b * kHeads + w) * kHeadDim;
-  const size_t qbase1 = ((size_t)b * kHeads + w + 8) * kHeadDim;
+  float qa[kG], qb[kG];
+#pragma unroll
+  for (int i = 0; i < kG; ++i) {
+    const size_t qbase = ((size_t)b * kH + w + kKvHeads * i) * kHeadDim;
+    qa[i] = a.q[qbase + lane];
+    qb[i] = a.q[qbase + lane + 64];
+  }
   const size_t kvbase = ((size_t)b * kKvHeads + w) * kHeadDim;
-  float q0a = a.q[qbase0 + lane], q0b = a.q[qbase0 + lane + 64];
-  float q1a = a.q[qbase1 + lane], q1b = a.q[qbase1 + lane + 64];
   float ka = a.k_new[kvbase + lane], kb = a.k_new[kvbase + lane + 64];
   const float va = a.v_new[kvbase + lane], vb = a.v_new[kvbase + lane + 64];
   __syncthreads();
   const float2 r = cs[lane];
 
-  rms_norm(q0a, q0b, a.q_gain, a.eps, lane);
-  rms_norm(q1a, q1b, a.q_gain, a.eps, lane);
+#pragma unroll
+  for (int i = 0; i < kG; ++i) rms_norm(qa[i], qb[i], a.q_gain, a.eps, lane);
   rms_norm(ka, kb, a.k_gain, a.eps, lane);
-  rotate(q0a, q0b, r.x, r.y);
-  rotate(q1a, q1b, r.x, r.y);
+#pragma unroll
+  for (int i = 0; i < kG; ++i) rotate(qa[i], qb[i], r.x, r.y);
   rotate(ka, kb, r.x, r.y);
-  a.q_out[qbase0 + lane] = q0a;
-  a.q_out[qbase0 + lane + 64] = q0b;
-  a.q_out[qbase1 + lane] = q1a;
-  a.q_out[qbase1 + lane + 64] = q1b;
+#pragma unroll
+  for (int i = 0; i < kG; ++i) {
+    const size_t qbase = ((size_t)b * kH + w + kKvHeads * i) * kHeadDim;
+    a.q_out[qbase + lane] = qa[i];
+    a.q_out[qbase + lane + 64] = qb[i];
+  }
 
   if (seq_len < 1 || seq_len > a.max_len) return;
   const int page = a.block_table[(size_t)b * a.max_pages_per_seq + pos / kPage];
@@ -1029,6 +1057,18 @@ int device_cu_count(int* out) {
   return DAH_OK;
 }
 
+// Calls f(std::integral_constant<int, G>{}) with the number G of query heads
+// per KV head; num_heads is one of 16, 32, 40, 64 (checked by the caller).
+template <class F>
+void with_group(int num_heads, F&& f) {
+  switch (num_heads) {
+    case 32: f(std::integral_constant<int, 4>{}); break;
+    case 40: f(std::integral_constant<int, 5>{}); break;
+    case 64: f(std::integral_constant<int, 8>{}); break;
+    default: f(std::integral_constant<int, 2>{}); break;
+  }
+}
+
 int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
@@ -1039,8 +1079,8 @@ int check_launch(const char* what) {
 int launch_append(const float* q, const float* k_new, const float* v_new, const float* q_gain,
                   const float* k_gain, float eps, float rope_theta, void* k_cache, void* v_cache,
                   int cache_dtype, int64_t num_pages, const int32_t* block_table,
-                  int max_pages_per_seq, const int32_t* seq_lens, int B, int max_len,
-                  float* q_out, hipStream_t stream) {
+                  int max_pages_per_seq, const int32_t* seq_lens, int B, int num_heads,
+                  int max_len, float* q_out, hipStream_t stream) {
   AppendArgs a;
   a.q = q;
   a.k_new = k_new;
@@ -1057,10 +1097,13 @@ int launch_append(const float* q, const float* k_new, const float* v_new, const 
   a.seq_lens = seq_lens;
   a.max_len = max_len;
   a.q_out = q_out;
-  if (cache_dtype == DAH_BF16)
-    norm_rope_append_kernel<DAH_BF16><<<B, 512, 0, stream>>>(a);
-  else
-    norm_rope_append_kernel<DAH_F32><<<B, 512, 0, stream>>>(a);
+  with_group(num_heads, [&](auto grp) {
+    constexpr int kG = decltype(grp)::value;
+    if (cache_dtype == DAH_BF16)
+      norm_rope_append_kernel<DAH_BF16, kG><<<B, 512, 0, stream>>>(a);
+    else
+      norm_rope_append_kernel<DAH_F32, kG><<<B, 512, 0, stream>>>(a);
+  });
   return check_launch("norm_rope_append_kernel");
 }
 
@@ -1077,39 +1120,39 @@ struct StepInputs {
   void* v_cache;
 };
 
-int plan_for(int B, int max_seq_len, int num_splits, void* workspace, size_t workspace_bytes,
-             dah::Plan* plan) {
+int plan_for(int B, int num_heads, int max_seq_len, int num_splits, void* workspace,
+             size_t workspace_bytes, dah::Plan* plan) {
   int cus = 0;
   int st = device_cu_count(&cus);
   if (st != DAH_OK) return st;
-  st = dah::plan_decode(B, max_seq_len, num_splits, cus, plan);
+  st = dah::plan_decode(B, num_heads, max_seq_len, num_splits, cus, plan);
   if (st != DAH_OK) return st;
   if (plan->workspace > 0) {
     if (workspace == nullptr || workspace_bytes < plan->workspace)
       return dah::set_error(DAH_ERR_WORKSPACE,
-                            "workspace of %zu bytes, need %zu (B=%d, max_seq_len=%d)",
+                            "workspace of %zu bytes, need %zu (B=%d, %d heads, max_seq_len=%d)",
                             workspace == nullptr ? (size_t)0 : workspace_bytes, plan->workspace, B,
-                            max_seq_len);
+                            num_heads, max_seq_len);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return dah::set_error(DAH_ERR_ALIGN, "workspace needs 256-byte alignment");
   }
   return DAH_OK;
 }
 
-template <bool kStep>
+template <bool kStep, int kG>
 void launch_decode_kernel(const dah::Plan& plan, bool bf16, const DecodeArgs& a,
                           hipStream_t stream) {
   const dim3 grid((unsigned)plan.workgroups), block(kWave * kDecodeWavesPerBlock);
   if (plan.mode == DAH_PLAN_BALANCED) {
     if (bf16)
-      decode_balanced_kernel<DAH_BF16, kStep><<<grid, block, 0, stream>>>(a);
+      decode_balanced_kernel<DAH_BF16, kStep, kG><<<grid, block, 0, stream>>>(a);
     else
-      decode_balanced_kernel<DAH_F32, kStep><<<grid, block, 0, stream>>>(a);
+      decode_balanced_kernel<DAH_F32, kStep, kG><<<grid, block, 0, stream>>>(a);
   } else {
     if (bf16)
-      decode_split_kernel<DAH_BF16, kStep><<<grid, block, 0, stream>>>(a);
+      decode_split_kernel<DAH_BF16, kStep, kG><<<grid, block, 0, stream>>>(a);
     else
-      decode_split_kernel<DAH_F32, kStep><<<grid, block, 0, stream>>>(a);
+      decode_split_kernel<DAH_F32, kStep, kG><<<grid, block, 0, stream>>>(a);
   }
 }
 
@@ -1118,8 +1161,8 @@ void launch_decode_kernel(const dah::Plan& plan, bool bf16, const DecodeArgs& a,
 int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
                   const void* v_cache, int cache_dtype, int64_t num_pages,
                   const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
-                  int B, int max_seq_len, float* o, void* workspace, const StepInputs* step,
-                  hipStream_t stream) {
+                  int B, int num_heads, int max_seq_len, float* o, void* workspace,
+                  const StepInputs* step, hipStream_t stream) {
   DecodeArgs a = {};
   a.q = q;
   a.k_cache = static_cast<const char*>(k_cache);
@@ -1135,9 +1178,9 @@ int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
   a.pages_per_split = plan.pages_per_split;
   a.o = o;
   float* ws = static_cast<float*>(workspace);
-  const size_t slots = plan.workspace / ((kHeadDim + 2) * sizeof(float) * kHeads);
+  const size_t rows = plan.workspace / ((kHeadDim + 2) * sizeof(float));  // partial rows
   a.part_acc = plan.workspace > 0 ? ws : nullptr;
-  a.part_ml = plan.workspace > 0 ? ws + slots * kHeads * kHeadDim : nullptr;
+  a.part_ml = plan.workspace > 0 ? ws + rows * kHeadDim : nullptr;
   if (step != nullptr) {
     a.k_new = step->k_new;
     a.v_new = step->v_new;
@@ -1150,19 +1193,23 @@ int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
     a.v_cache_w = static_cast<char*>(step->v_cache);
   }
   const bool bf16 = cache_dtype == DAH_BF16;
-  if (step == nullptr)
-    launch_decode_kernel<false>(plan, bf16, a, stream);
-  else
-    launch_decode_kernel<true>(plan, bf16, a, stream);
+  with_group(num_heads, [&](auto grp) {
+    constexpr int kG = decltype(grp)::value;
+    if (step == nullptr)
+      launch_decode_kernel<false, kG>(plan, bf16, a, stream);
+    else
+      launch_decode_kernel<true, kG>(plan, bf16, a, stream);
+  });
   int st = check_launch("decode kernel");
   if (st != DAH_OK || plan.mode == DAH_PLAN_PER_SEQUENCE) return st;
-  const int cblocks = B * kHeads;  // one workgroup per (sequence, head)
+  const int cblocks = B * num_heads;  // one workgroup per (sequence, head)
   if (plan.mode == DAH_PLAN_BALANCED)
     combine_balanced_kernel<<<cblocks, kCombineThreads, 0, stream>>>(
-        a.part_acc, a.part_ml, seq_lens, B, max_seq_len, plan.workgroups, o);
+        a.part_acc, a.part_ml, seq_lens, B, num_heads, max_seq_len, plan.workgroups, o);
   else
     combine_splits_kernel<<<cblocks, kCombineThreads, 0, stream>>>(
-        a.part_acc, a.part_ml, seq_lens, B, max_seq_len, plan.splits, plan.pages_per_split, o);
+        a.part_acc, a.part_ml, seq_lens, B, num_heads, max_seq_len, plan.splits,
+        plan.pages_per_split, o);
   return check_launch("combine kernel");
 }
 
@@ -1170,35 +1217,97 @@ int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
 
 extern "C" {
 
+int qk_norm_rope_append_ex(const float* q, const float* k_new, const float* v_new,
+                           const float* q_gain, const float* k_gain, float eps, float rope_theta,
+                           void* k_cache, void* v_cache, int cache_dtype, int64_t num_pages,
+                           const int32_t* block_table, int max_pages_per_seq,
+                           const int32_t* seq_lens, int B, int num_heads, float* q_out,
+                           void* stream) {
+  int st = dah::validate_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache,
+                                v_cache, cache_dtype, num_pages, block_table, max_pages_per_seq,
+                                seq_lens, B, num_heads, q_out);
+  if (st != DAH_OK) return st;
+  const long long max_len = (long long)max_pages_per_seq * kPage;
+  return launch_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
+                       cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
+                       num_heads, max_len > INT32_MAX ? INT32_MAX : (int)max_len, q_out,
+                       static_cast<hipStream_t>(stream));
+}
+
 int qk_norm_rope_append(const float* q, const float* k_new, const float* v_new,
                         const float* q_gain, const float* k_gain, float eps, float rope_theta,
                         void* k_cache, void* v_cache, int cache_dtype, int64_t num_pages,
                         const int32_t* block_table, int max_pages_per_seq,
                         const int32_t* seq_lens, int B, float* q_out, void* stream) {
-  int st = dah::validate_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache,
+  return qk_norm_rope_append_ex(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache,
                                 v_cache, cache_dtype, num_pages, block_table, max_pages_per_seq,
-                                seq_lens, B, q_out);
+                                seq_lens, B, kHeads, q_out, stream);
+}
+
+int paged_decode_gqa_ex(const float* q, const void* k_cache, const void* v_cache,
+                        int cache_dtype, int64_t num_pages, const int32_t* block_table,
+                        int max_pages_per_seq, const int32_t* seq_lens, int B, int num_heads,
+                        int max_seq_len, int num_splits, float* o, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = dah::validate_decode(q, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                                max_pages_per_seq, seq_lens, B, num_heads, max_seq_len,
+                                num_splits, o);
   if (st != DAH_OK) return st;
-  const long long max_len = (long long)max_pages_per_seq * kPage;
-  return launch_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
-                       cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
-                       max_len > INT32_MAX ? INT32_MAX : (int)max_len, q_out,
-                       static_cast<hipStream_t>(stream));
+  dah::Plan plan;
+  st = plan_for(B, num_heads, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
+  if (st != DAH_OK) return st;
+  return launch_decode(plan, q, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                       max_pages_per_seq, seq_lens, B, num_heads, max_seq_len, o, workspace,
+                       nullptr, static_cast<hipStream_t>(stream));
 }
 
 int paged_decode_gqa(const float* q, const void* k_cache, const void* v_cache, int cache_dtype,
                      int64_t num_pages, const int32_t* block_table, int max_pages_per_seq,
                      const int32_t* seq_lens, int B, int max_seq_len, int num_splits, float* o,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  int st = dah::validate_decode(q, k_cache, v_cache, cache_dtype, num_pages, block_table,
-                                max_pages_per_seq, seq_lens, B, max_seq_len, num_splits, o);
+  return paged_decode_gqa_ex(q, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                             max_pages_per_seq, seq_lens, B, kHeads, max_seq_len, num_splits, o,
+                             workspace, workspace_bytes, stream);
+}
+
+int decode_attn_step_ex(const float* q, const float* k_new, const float* v_new,
+                        const float* q_gain, const float* k_gain, float eps, float rope_theta,
+                        void* k_cache, void* v_cache, int cache_dtype, int64_t num_pages,
+                        const int32_t* block_table, int max_pages_per_seq,
+                        const int32_t* seq_lens, int B, int num_heads, int max_seq_len,
+                        int num_splits, float* q_out, float* o, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int st = dah::validate_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache,
+                                v_cache, cache_dtype, num_pages, block_table, max_pages_per_seq,
+                                seq_lens, B, num_heads, q_out);
   if (st != DAH_OK) return st;
+  st = dah::validate_decode(q_out, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                            max_pages_per_seq, seq_lens, B, num_heads, max_seq_len, num_splits,
+                            o);
+  if (st != DAH_OK) return st;
+  // Plan and check the workspace before anything is launched, so that a
+  // failing call leaves the cache untouched.
   dah::Plan plan;
-  st = plan_for(B, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
+  st = plan_for(B, num_heads, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
   if (st != DAH_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q_out == q && plan.mode != DAH_PLAN_PER_SEQUENCE) {
+    // In place with several splits: the workgroups of one sequence would read
+    // q while another overwrites it, so norm and rotate first, then decode.
+    st = launch_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
+                       cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
+                       num_heads, max_seq_len, q_out, s);
+    if (st != DAH_OK) return st;
+    return launch_decode(plan, q_out, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                         max_pages_per_seq, seq_lens, B, num_heads, max_seq_len, o, workspace,
+                         nullptr, s);
+  }
+  // One launch: the decode kernel norms and rotates q, writes q_out, and
+  // appends the new key and value (see decode_split_kernel).
+  const StepInputs step = {k_new, v_new, q_gain, k_gain, eps, rope_theta, q_out, k_cache, v_cache};
   return launch_decode(plan, q, k_cache, v_cache, cache_dtype, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, B, max_seq_len, o, workspace, nullptr,
-                       static_cast<hipStream_t>(stream));
+                       max_pages_per_seq, seq_lens, B, num_heads, max_seq_len, o, workspace,
+                       &step, s);
 }
 
 int decode_attn_step(const float* q, const float* k_new, const float* v_new,
@@ -1208,40 +1317,22 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
                      const int32_t* seq_lens, int B, int max_seq_len, int num_splits,
                      float* q_out, float* o, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  int st = dah::validate_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache,
-                                v_cache, cache_dtype, num_pages, block_table, max_pages_per_seq,
-                                seq_lens, B, q_out);
-  if (st != DAH_OK) return st;
-  st = dah::validate_decode(q_out, k_cache, v_cache, cache_dtype, num_pages, block_table,
-                            max_pages_per_seq, seq_lens, B, max_seq_len, num_splits, o);
-  if (st != DAH_OK) return st;
-  // Plan and check the workspace before anything is launched, so that a
-  // failing call leaves the cache untouched.
-  dah::Plan plan;
-  st = plan_for(B, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
-  if (st != DAH_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q_out == q && plan.mode != DAH_PLAN_PER_SEQUENCE) {
-    // In place with several splits: the workgroups of one sequence would read
-    // q while another overwrites it, so norm and rotate first, then decode.
-    st = launch_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
-                       cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
-                       max_seq_len, q_out, s);
-    if (st != DAH_OK) return st;
-    return launch_decode(plan, q_out, k_cache, v_cache, cache_dtype, num_pages, block_table,
-                         max_pages_per_seq, seq_lens, B, max_seq_len, o, workspace, nullptr, s);
-  }
-  // One launch: the decode kernel norms and rotates q, writes q_out, and
-  // appends the new key and value (see decode_split_kernel).
-  const StepInputs step = {k_new, v_new, q_gain, k_gain, eps, rope_theta, q_out, k_cache, v_cache};
-  return launch_decode(plan, q, k_cache, v_cache, cache_dtype, num_pages, block_table,
-                       max_pages_per_seq, seq_lens, B, max_seq_len, o, workspace, &step, s);
+  return decode_attn_step_ex(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
+                             cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
+                             kHeads, max_seq_len, num_splits, q_out, o, workspace,
+                             workspace_bytes, stream);
+}
+
+size_t dah_workspace_bytes_ex(int B, int num_heads, int max_seq_len, int num_splits) {
+  int cus = 0;
+  if (device_cu_count(&cus) != DAH_OK) return 0;
+  dah::Plan p;
+  if (dah::plan_decode(B, num_heads, max_seq_len, num_splits, cus, &p) != DAH_OK) return 0;
+  return p.workspace;
 }
 
 size_t dah_workspace_bytes(int B, int max_seq_len, int num_splits) {
-  int cus = 0;
-  if (device_cu_count(&cus) != DAH_OK) return 0;
-  return dah_workspace_bytes_for(B, max_seq_len, num_splits, cus);
+  return dah_workspace_bytes_ex(B, kHeads, max_seq_len, num_splits);
 }
 
 }  // extern "C"

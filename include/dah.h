@@ -208,6 +208,44 @@ size_t dah_workspace_bytes(int B, int max_seq_len, int num_splits);
 /* dah_workspace_bytes_for -- the same for an explicit compute-unit count (no device query). */
 size_t dah_workspace_bytes_for(int B, int max_seq_len, int num_splits, int num_cus);
 
+/*
+ * The Qwen3 family's other group sizes (nnterp qwen3 page, "Grouped-query
+ * attention, with 128-wide heads on every size": 32 query heads for 4B and
+ * 8B, 40 for 14B, 64 for 32B, all over 8 KV heads of 128 dims; "What loads as
+ * this family": RoPE base 5e6 for the 4B-2507 pair, which is the rope_theta
+ * argument).  The *_ex calls are the calls above with the query-
+ * head count num_heads in {16, 32, 40, 64} after B: q, q_out and o become
+ * [B][num_heads][128], query head h reads KV head h / (num_heads / 8), and
+ * the workspace scales with num_heads.  Everything else -- the cache pools,
+ * block table, sequence lengths, statuses -- is as above; num_heads outside
+ * the set returns DAH_ERR_SHAPE.  The calls above are these with num_heads = 16.
+ */
+int qk_norm_rope_append_ex(const float* q, const float* k_new, const float* v_new,
+                           const float* q_gain, const float* k_gain, float eps, float rope_theta,
+                           void* k_cache, void* v_cache, int cache_dtype, int64_t num_pages,
+                           const int32_t* block_table, int max_pages_per_seq,
+                           const int32_t* seq_lens, int B, int num_heads, float* q_out,
+                           void* stream);
+
+int paged_decode_gqa_ex(const float* q, const void* k_cache, const void* v_cache,
+                        int cache_dtype, int64_t num_pages, const int32_t* block_table,
+                        int max_pages_per_seq, const int32_t* seq_lens, int B, int num_heads,
+                        int max_seq_len, int num_splits, float* o, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+int decode_attn_step_ex(const float* q, const float* k_new, const float* v_new,
+                        const float* q_gain, const float* k_gain, float eps, float rope_theta,
+                        void* k_cache, void* v_cache, int cache_dtype, int64_t num_pages,
+                        const int32_t* block_table, int max_pages_per_seq,
+                        const int32_t* seq_lens, int B, int num_heads, int max_seq_len,
+                        int num_splits, float* q_out, float* o, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+int dah_plan_decode_ex(int B, int num_heads, int max_seq_len, int num_splits, int num_cus,
+                       dah_decode_plan* out);
+
+size_t dah_workspace_bytes_ex(int B, int num_heads, int max_seq_len, int num_splits);
+
 /* Static name of a dah_status value ("DAH_OK", ...); "unknown status" otherwise. */
 const char* dah_status_string(int status);
 

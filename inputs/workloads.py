@@ -6,7 +6,11 @@ path (through the binding) and the CPU oracle can consume what it produces.
 
 Shapes follow the "Qwen3-0.6B" Model Spec page ("At a glance": shape domain
 B <= 256 sequences, S <= 40,960 cached positions, page size 16;
-"Tensors of the main nodes": q [B,16,128], k/v [B,S,8,128]).  Values follow
+"Tensors of the main nodes": q [B,16,128], k/v [B,S,8,128]).  The family
+workloads keep those shapes but give q the head count of a larger member
+(nnterp qwen3 page, "Grouped-query attention, with 128-wide heads on every
+size": 32, 40 or 64 query heads over the same 8 KV heads) and, for the 4B-2507
+pair, RoPE base 5e6 ("What loads as this family").  Values follow
 the conformance methodology of the "Model conformance" page ("How the
 comparison works", step 1): O(1) activations and norm gains perturbed away
 from 1 (here 1 + N(0, 0.1)).
@@ -47,6 +51,8 @@ class Workload:
     lens_args: tuple = ()
     pool_pages: int | None = None     # None: exactly the pages the batch needs
     key_outlier: float | None = None  # multiply one cached key position by this
+    num_heads: int = NUM_HEADS        # query heads (16, 32, 40 or 64) over 8 KV heads
+    rope_theta: float = ROPE_THETA
     description: str = ""
 
     def seq_lens(self) -> np.ndarray:
@@ -87,6 +93,24 @@ WORKLOADS = {
                  description="28 layers, each with its own bf16 pool and gains; "
                              "B=128, seq_lens log-uniform in [16,16384]; one block "
                              "table shared by all layers"),
+        # The same cache as b256_s2048 (identical seeds, so identical KV bytes)
+        # read by the larger family members' query heads.
+        Workload("b256_s2048_h32", batch=256, cache_dtype="bf16", seed=2,
+                 lens_kind="fixed", lens_args=(2048,), pool_pages=65536, num_heads=32,
+                 rope_theta=5e6,
+                 description="b256_s2048 with 32 query heads (group size 4) and "
+                             "RoPE base 5e6, the 4B-2507 attention shape"),
+        Workload("b256_s2048_h40", batch=256, cache_dtype="bf16", seed=2,
+                 lens_kind="fixed", lens_args=(2048,), pool_pages=65536, num_heads=40,
+                 description="b256_s2048 with 40 query heads (group size 5), the 14B shape"),
+        Workload("b256_s2048_h64", batch=256, cache_dtype="bf16", seed=2,
+                 lens_kind="fixed", lens_args=(2048,), pool_pages=65536, num_heads=64,
+                 description="b256_s2048 with 64 query heads (group size 8), the 32B shape"),
+        Workload("ragged_f32_b6", batch=6, cache_dtype="f32", seed=5,
+                 lens_kind="list", lens_args=(1, 16, 17, 100, 333, 1024), pool_pages=256,
+                 description="fp32 cache; B=6, seq_lens {1,16,17,100,333,1024} (one "
+                             "position, a full page, a page plus one, ragged tails); "
+                             "the small case for every head count"),
     ]
 }
 
@@ -152,7 +176,8 @@ def _torch_generator(torch, device, w: Workload, layer: int, tensor_id: int):
 def make_layer(w: Workload, layer: int, device, table=None, num_pages=None, seq_lens=None):
     """Random tensors of one layer on ``device`` (torch tensors).
 
-    Returns dict with q [B,16,128], k_new/v_new [B,8,128] (float32, pre-norm),
+    Returns dict with q [B,H,128] (H = w.num_heads), k_new/v_new [B,8,128]
+    (float32, pre-norm),
     q_gain/k_gain [128] (float32), k_pool/v_pool [num_pages,8,16,128] in the
     cache dtype, and the int32 block_table and seq_lens."""
     import torch
@@ -171,7 +196,7 @@ def make_layer(w: Workload, layer: int, device, table=None, num_pages=None, seq_
                            device=device, dtype=dtype)
 
     out = {
-        "q": randn((B, NUM_HEADS, HEAD_DIM), 0),
+        "q": randn((B, w.num_heads, HEAD_DIM), 0),
         "k_new": randn((B, NUM_KV_HEADS, HEAD_DIM), 1),
         "v_new": randn((B, NUM_KV_HEADS, HEAD_DIM), 2),
         "q_gain": 1.0 + 0.1 * randn((HEAD_DIM,), 3),

@@ -89,6 +89,7 @@ def oracle_decode(snap, cache_dtype):
 
 
 def oracle_step(snap, cache_dtype, eps=W.RMS_EPS, theta=W.ROPE_THETA):
+    """The oracle's decode step on a host snapshot (theta: the workload's RoPE base)."""
     return O.decode_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"],
                          snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
                          cache_dtype, eps=eps, theta=theta)
@@ -148,6 +149,7 @@ def distance_to_uniform(o_ref, snap, cache_dtype):
         n = int(snap["seq_lens"][i])
         v = O.gather_sequence(snap["v_pool"], snap["block_table"][i], n, cache_dtype)
         mean = v.mean(axis=0)                                 # [8,128]
-        for h in range(16):
-            worst = max(worst, float(np.max(np.abs(o_ref[i, h] - mean[h // 2]))))
+        H = o_ref.shape[1]
+        for h in range(H):
+            worst = max(worst, float(np.max(np.abs(o_ref[i, h] - mean[h // (H // 8)]))))
     return worst

@@ -249,3 +249,49 @@ def test_probe_wrappers_refuse_host_tensors():
         probe_copy(a, a.clone())
     with pytest.raises(ValueError):
         probe_read(a, torch.zeros(4, dtype=torch.int32), 1)
+
+
+# The family's other head counts (nnterp qwen3 page, "Grouped-query attention,
+# with 128-wide heads on every size"): 32, 40 and 64 query heads over 8 KV heads.
+FAMILY_HEADS = [16, 32, 40, 64]
+
+
+@pytest.mark.parametrize("H", FAMILY_HEADS)
+@pytest.mark.parametrize("B,L,n", [(256, 2048, 0), (32, 4096, 0), (4, 40960, 0), (128, 16384, 0),
+                                   (7, 999, 3)])
+def test_planner_ex_scales_the_workspace_with_heads(H, B, L, n):
+    lib = _lib()
+    p16, ph = native.DecodePlan(), native.DecodePlan()
+    assert lib.dah_plan_decode(B, L, n, 256, ctypes.byref(p16)) == 0
+    assert lib.dah_plan_decode_ex(B, H, L, n, 256, ctypes.byref(ph)) == 0
+    # the cut of the positions does not depend on the head count
+    assert (ph.mode, ph.splits, ph.pages_per_split, ph.workgroups) == \
+        (p16.mode, p16.splits, p16.pages_per_split, p16.workgroups)
+    assert ph.workspace_bytes * 16 == p16.workspace_bytes * H
+
+
+@pytest.mark.parametrize("H", [0, 8, 15, 24, 48, 65, -16])
+def test_ex_calls_reject_other_head_counts(H):
+    lib = _lib()
+    p = native.DecodePlan()
+    assert lib.dah_plan_decode_ex(2, H, 64, 0, 256, ctypes.byref(p)) == 2
+    assert "num_heads" in lib.dah_last_error().decode()
+    assert lib.paged_decode_gqa_ex(A, A, A, 1, 16, A, 4, A, 2, H, 64, 0, A, None, 0, None) == 2
+    assert lib.qk_norm_rope_append_ex(A, A, A, A, A, 1e-6, 1e6, A, A, 1, 16, A, 4, A, 2, H, A,
+                                      None) == 2
+    assert lib.decode_attn_step_ex(A, A, A, A, A, 1e-6, 1e6, A, A, 1, 16, A, 4, A, 2, H, 64, 0, A,
+                                   A, None, 0, None) == 2
+
+
+@pytest.mark.parametrize("H", FAMILY_HEADS)
+def test_ex_calls_validate_like_the_base_calls(H):
+    lib = _lib()
+    # a NULL pointer, a bad dtype, a misaligned pointer, a too-long max_seq_len
+    assert lib.paged_decode_gqa_ex(None, A, A, 1, 16, A, 4, A, 2, H, 64, 0, A, None, 0, None) == 1
+    assert lib.paged_decode_gqa_ex(A, A, A, 5, 16, A, 4, A, 2, H, 64, 0, A, None, 0, None) == 3
+    assert lib.paged_decode_gqa_ex(A, A, A, 1, 16, A, 4, A, 2, H, 64, 0, A + 4, None, 0, None) == 4
+    assert lib.paged_decode_gqa_ex(A, A, A, 1, 16, A, 4, A, 2, H, 65, 0, A, None, 0, None) == 2
+    assert lib.qk_norm_rope_append_ex(A, A, A, A, A, -1.0, 1e6, A, A, 1, 16, A, 4, A, 2, H, A,
+                                      None) == 2
+    assert lib.decode_attn_step_ex(A, A, A, A, A, 1e-6, 1e6, A, A, 1, 16, A, 4, A, 2, H, 64, 0,
+                                   None, A, None, 0, None) == 1
