@@ -626,6 +626,405 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
   }
 }
 
+// ------------------------------------------------------------ MFMA decode
+//
+// With 4 or more query heads per KV head (the family's 4B/8B, 14B and 32B
+// shapes) the VALU form above runs out of issue slots and registers: the
+// multiply-adds grow with G while the bytes do not.  For a bfloat16 cache
+// both contractions of a page then go to the matrix cores with
+// v_mfma_f32_16x16x32_bf16.  Lane l = 16 r + c.
+//
+// Scores.  A = 16 positions x 32 dims of K, B = 32 dims x 16 query-head
+// columns, D = scores.  The lane loads K position sigma(c) = 4 (c mod 4) +
+// c / 4, dims 32 kk + 8 r .. +7 (16 bytes; the four kk cover a position's
+// 256 bytes in 64-byte pieces).  The permutation sigma makes D land as
+// lane (r, c) = scores of head c at positions 4 v + r, v = 0..3 -- the
+// positions of wave row r in the V tile, which is what the second product
+// needs.  q (float32) enters as the sum of three bfloat16 terms along the
+// contraction (12 products per page), which carries it to 2^-27 relative:
+// the cache values are exact in bfloat16, so the scores are as accurate as
+// a float32 dot product.
+//
+// Weighted V sum.  A = weights (16 head rows x 32), B = V (32 x 16 dims),
+// the 32 contraction slots being (term, position): weights enter as two
+// bfloat16 terms (2^-18 relative).  The V tile keeps the coalesced layout of
+// the VALU path (lane (r, c): dims 8c..8c+7 of positions 4j + r); product
+// nb = 0..7 takes dim 8c + nb of the lane's four positions as the lane's B
+// column, so D holds rows = heads 4r + v, column c = dim 8c + nb.  No value
+// crosses lanes between the two products.
+//
+// Online softmax.  All rows share one reference per head (the products mix
+// rows); the page maximum is reduced across rows and the reference moves
+// only when a score exceeds it by more than kMaxLag (log2 units), so weights
+// stay below 2^kMaxLag and rescaling is rare.  Any reference gives the same
+// softmax (theorem softmax_shift, "Supported models" page).
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr float kMaxLag = 8.0f;
+
+template <int kG>
+constexpr bool use_mfma(int dtype) { return dtype == DAH_BF16 && kG >= 4; }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// K tile in the score product's A layout.
+struct KTileMfma {
+  u32x4 w[4];  // kk = 0..3
+  __device__ __forceinline__ void load(const char* tile, int lane) {
+    const int r = lane >> 4, c = lane & 15;
+    const int pos = 4 * (c & 3) + (c >> 2);
+    const u32x4* p = reinterpret_cast<const u32x4*>(tile) + pos * 16 + r;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) w[kk] = __builtin_nontemporal_load(p + 4 * kk);
+  }
+};
+
+// LDS of one workgroup of the MFMA decode: normed queries (fused step) and
+// the new token's stored words.
+template <int kG>
+struct MfmaStash {
+  u32x4 kv[kDecodeWavesPerBlock][2][16];        // [wave][k|v][column] (bf16: one word each)
+  float q[kDecodeWavesPerBlock][kG][kHeadDim];  // [wave][head][dim]
+};
+
+// Scores of one page: lane (r, c) gets head c at positions 4v + r.
+__device__ __forceinline__ f32x4 page_scores(const KTileMfma& K, const u32x4 (&qb)[4][3]) {
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const bf16x8 a = __builtin_bit_cast(bf16x8, K.w[kk]);
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qb[kk][t]), s, 0,
+                                                   0, 0);
+  }
+  return s;
+}
+
+// Online-softmax state of the MFMA decode.  m and l are per lane for head c
+// (m equal across rows; l the lane's share, summed over rows at the end);
+// acc[nb] holds rows = heads 4r + v, dim 8c + nb.
+struct MfmaState {
+  float m, l;
+  f32x4 acc[8];
+};
+
+// One page: scores -> weights -> weighted V sum.  kMasked: positions
+// >= nvalid are excluded (their V is cleared: 0 * NaN would poison a row).
+template <bool kMasked>
+__device__ __forceinline__ void attend_page_mfma(const KTileMfma& K, Tile<DAH_BF16>& V,
+                                                 const u32x4 (&qb)[4][3], MfmaState& st,
+                                                 int lane, int nvalid) {
+  const int r = lane >> 4;
+  f32x4 s = page_scores(K, qb);
+  if (kMasked) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const bool ok = 4 * v + r < nvalid;
+      s[v] = ok ? s[v] : -INFINITY;
+      if (!ok) V.clear(v);
+    }
+  }
+  float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  pm = fmaxf(pm, __shfl_xor(pm, 16));
+  pm = fmaxf(pm, __shfl_xor(pm, 32));
+  // Move the reference only when a score passes it by more than kMaxLag
+  // (always from -inf); a wave-uniform branch, rarely taken after the
+  // first page.
+  const bool move = pm > st.m + kMaxLag;
+  if (__builtin_amdgcn_ballot_w64(move) != 0) {
+    const float mn = move ? pm : st.m;
+    const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float av = __shfl(alpha, 4 * r + v);  // head 4r + v's factor (column 4r + v)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) st.acc[nb][v] *= av;
+    }
+  }
+  const float mu = st.m == -INFINITY ? 0.0f : st.m;
+  float p[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mu);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  // Weights as hi + lo bfloat16 terms.
+  float lo[4];
+  uint16_t hb[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    hb[v] = to_bf16(p[v]);
+    lo[v] = p[v] - bf16_val(hb[v]);
+  }
+  u32x4 aw;
+  aw[0] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+  aw[1] = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+  aw[2] = pack_bf16x2(lo[0], lo[1]);
+  aw[3] = pack_bf16x2(lo[2], lo[3]);
+  const bf16x8 a = __builtin_bit_cast(bf16x8, aw);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const uint32_t sel = (nb & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t v01 = __builtin_amdgcn_perm(V.w[1][nb >> 1], V.w[0][nb >> 1], sel);
+    const uint32_t v23 = __builtin_amdgcn_perm(V.w[3][nb >> 1], V.w[2][nb >> 1], sel);
+    const u32x4 bw = {v01, v23, v01, v23};
+    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bw),
+                                                          st.acc[nb], 0, 0, 0);
+  }
+}
+
+// Splits 8 float32 values into the three bfloat16 terms of the score
+// product's B operand.
+__device__ __forceinline__ void split3(const float (&x)[8], u32x4 (&out)[3]) {
+  float rem[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rem[e] = x[e];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    uint16_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[e] = to_bf16(rem[e]);
+      rem[e] -= bf16_val(h[e]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[t][i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
+  }
+}
+
+// decode_range for a bfloat16 cache on the matrix cores; same contract.
+template <bool kStep, int kG>
+__device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, int seq_len,
+                                                  int npages, int p0, int p1, bool write_q,
+                                                  bool to_o, size_t part_base, int part_stride,
+                                                  int g, int lane, MfmaStash<kG>& stash) {
+  static_assert(kG <= 16, "one score column per query head");
+  constexpr int kH = kG * kKvHeads;
+  using TileV = Tile<DAH_BF16>;
+  const int wave = g;
+  const int row = lane >> 4;
+  const int col = lane & 15;
+  const int qh = col < kG ? col : kG - 1;            // this lane's score column's head
+  const size_t qrow0 = (size_t)b * kH + g * kG;      // first query head row of this KV head
+
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+  const ConstI32 bt = (ConstI32)(a.block_table + (size_t)b * a.max_pages_per_seq);
+  const int64_t page_bytes = (int64_t)kKvHeads * TileV::kTileBytes;
+  const int64_t head_bytes = (int64_t)g * TileV::kTileBytes;
+  const char* kbase = a.k_cache + head_bytes;
+  const char* vbase = a.v_cache + head_bytes;
+  const int tail = seq_len - (npages - 1) * kPage;
+  const int last = p1 - 1;
+  const bool holds_last = kStep && p1 == npages;
+  const int last_valid = holds_last ? tail - 1 : tail;
+  const bool last_masked = (last == npages - 1) && last_valid < kPage;
+  bool bad_page = false;
+  auto offset_of = [&](int id) -> int64_t {
+    const bool ok = id >= 0 && id < a.num_pages;
+    bad_page |= !ok;
+    return (int64_t)(ok ? id : 0) * page_bytes;
+  };
+  const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+
+  // Small loads first (see decode_range).  Without the step, q arrives
+  // normed: the lane reads its B-operand slice (head qh, dims 32kk + 8r ..)
+  // directly.  With the step, it reads the raw rows in the row layout.
+  float qv[kStep ? 1 : 4][8];
+  float qr[kStep ? kG : 1][8];
+  float qw[8], kx[8], vx[8], kw8[8];
+  if constexpr (!kStep) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) load8(a.q + (qrow0 + qh) * kHeadDim + 32 * kk + 8 * row, qv[kk]);
+  } else {
+#pragma unroll
+    for (int h = 0; h < kG; ++h) load8(a.q + (qrow0 + h) * kHeadDim + 8 * col, qr[h]);
+    load8(a.q_gain + 8 * col, qw);
+    if (holds_last) {
+      load8(a.k_new + ((size_t)b * kKvHeads + g) * kHeadDim + 8 * col, kx);
+      load8(a.v_new + ((size_t)b * kKvHeads + g) * kHeadDim + 8 * col, vx);
+      load8(a.k_gain + 8 * col, kw8);
+    }
+  }
+
+  KTileMfma K0, K1;
+  TileV V0, V1;
+  int id1 = bt[min(p0 + 1, last)];
+  int id2 = bt[min(p0 + 2, last)];
+  {
+    const int64_t off0 = offset_of(bt[p0]);
+    K0.load(kbase + off0, lane);
+    V0.load(vbase + off0, lane);
+  }
+
+  MfmaState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4 qb[4][3];
+  if constexpr (kStep) {
+    const int pos = seq_len - 1;
+    float cr[8], sr[8];
+    rope_table(pos, a.rope, lane, col, cr, sr);
+    float kf[8], vf[8];
+    if (holds_last) {
+      norm_rope_row(kx, kw8, a.eps, cr, sr, col);
+      const SlotWords<DAH_BF16> kw = pack_slot<DAH_BF16>(kx);
+      const SlotWords<DAH_BF16> vw = pack_slot<DAH_BF16>(vx);
+      if (row == 0) {
+        stash.kv[wave][0][col] = kw.w[0];
+        stash.kv[wave][1][col] = vw.w[0];
+      }
+      unpack_slot<DAH_BF16>(kw, kf);  // the new token as the cache holds it
+      unpack_slot<DAH_BF16>(vw, vf);
+    }
+    float s_new = -INFINITY;  // the new token's score for head `col`
+#pragma unroll
+    for (int h = 0; h < kG; ++h) {
+      norm_rope_row(qr[h], qw, a.eps, cr, sr, col);
+      if (row_writes(row, h)) {
+        float4* d = reinterpret_cast<float4*>(&stash.q[wave][h][8 * col]);
+        d[0] = make_float4(qr[h][0], qr[h][1], qr[h][2], qr[h][3]);
+        d[1] = make_float4(qr[h][4], qr[h][5], qr[h][6], qr[h][7]);
+      }
+      if (holds_last) {
+        float sc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc = fmaf(qr[h][e], kf[e], sc);
+        sc = row_sum16(sc) * qscale;
+        s_new = col == h ? sc : s_new;
+      }
+    }
+    if (holds_last) {
+      // Start the state with the new token: reference = its score, weight 1
+      // (counted once, in row 0), value = v_new for every head of this KV head.
+      st.m = col < kG ? s_new : 0.0f;
+      st.l = row == 0 ? 1.0f : 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bool live = 4 * row + v < kG;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) st.acc[nb][v] = live ? vf[nb] : 0.0f;
+      }
+    }
+    // The normed rows are in LDS; read this lane's B-operand slice back.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float x[8];
+      const float4* sq = reinterpret_cast<const float4*>(&stash.q[wave][qh][32 * kk + 8 * row]);
+      const float4 x0 = sq[0], x1 = sq[1];
+      x[0] = x0.x * qscale; x[1] = x0.y * qscale; x[2] = x0.z * qscale; x[3] = x0.w * qscale;
+      x[4] = x1.x * qscale; x[5] = x1.y * qscale; x[6] = x1.z * qscale; x[7] = x1.w * qscale;
+      split3(x, qb[kk]);
+    }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[kk][e] *= qscale;
+      split3(qv[kk], qb[kk]);
+    }
+  }
+  if (col >= kG) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) qb[kk][t] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  int p = p0;
+  for (; p + 2 <= last; p += 2) {
+    const int64_t off1 = offset_of(id1);
+    K1.load(kbase + off1, lane);
+    V1.load(vbase + off1, lane);
+    const int id3 = bt[min(p + 3, last)];
+    __builtin_amdgcn_sched_barrier(0);
+    attend_page_mfma<false>(K0, V0, qb, st, lane, kPage);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t off2 = offset_of(id2);
+    K0.load(kbase + off2, lane);
+    V0.load(vbase + off2, lane);
+    const int id4 = bt[min(p + 4, last)];
+    __builtin_amdgcn_sched_barrier(0);
+    attend_page_mfma<false>(K1, V1, qb, st, lane, kPage);
+    __builtin_amdgcn_sched_barrier(0);
+    id1 = id3;
+    id2 = id4;
+  }
+  if (p + 1 <= last) {
+    const int64_t off1 = offset_of(id1);
+    K1.load(kbase + off1, lane);
+    V1.load(vbase + off1, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    attend_page_mfma<false>(K0, V0, qb, st, lane, kPage);
+    __builtin_amdgcn_sched_barrier(0);
+    if (last_masked)
+      attend_page_mfma<true>(K1, V1, qb, st, lane, last_valid);
+    else
+      attend_page_mfma<false>(K1, V1, qb, st, lane, kPage);
+  } else {
+    if (last_masked)
+      attend_page_mfma<true>(K0, V0, qb, st, lane, last_valid);
+    else
+      attend_page_mfma<false>(K0, V0, qb, st, lane, kPage);
+  }
+
+  // Totals per head (column c): l summed over the rows.
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int h = 4 * row + v;  // this lane's accumulator row v
+    const float lh = __shfl(l, h);
+    const float mh = __shfl(st.m, h);
+    if (h >= kG) continue;
+    float o8[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) o8[nb] = st.acc[nb][v];
+    if (to_o) {
+      store8(a.o + (qrow0 + h) * kHeadDim + 8 * col, o8, bad_page ? NAN : 1.0f / lh);
+    } else {
+      const size_t part = part_base + (size_t)(g * kG + h) * part_stride;
+      store8(a.part_acc + part * kHeadDim + 8 * col, o8, bad_page ? NAN : 1.0f);
+      if (col == 0)
+        reinterpret_cast<float2*>(a.part_ml)[part] = make_float2(mh, bad_page ? NAN : lh);
+    }
+  }
+  if constexpr (kStep) {
+    if (write_q) {
+      // Two 128-float rows per wave store: lanes 0-31 row h, lanes 32-63 row h + 1.
+      const int half = lane >> 5, q4 = lane & 31;
+#pragma unroll
+      for (int h0 = 0; h0 < kG; h0 += 2) {
+        const int h = h0 + half;
+        if (h < kG)
+          reinterpret_cast<float4*>(a.q_out + (qrow0 + h) * kHeadDim)[q4] =
+              reinterpret_cast<const float4*>(&stash.q[wave][h][0])[q4];
+      }
+    }
+    if (holds_last && row == 0) {
+      const int id = bt[npages - 1];
+      if (id >= 0 && id < a.num_pages) {
+        const int64_t slot_off = (int64_t)id * page_bytes + head_bytes +
+                                 (int64_t)(tail - 1) * (TileV::kTileBytes / kPage);
+        reinterpret_cast<u32x4*>(a.k_cache_w + slot_off)[col] = stash.kv[wave][0][col];
+        reinterpret_cast<u32x4*>(a.v_cache_w + slot_off)[col] = stash.kv[wave][1][col];
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ int pages_of(int seq_len, int max_seq_len) {
   return (seq_len >= 1 && seq_len <= max_seq_len) ? (seq_len + kPage - 1) / kPage : 0;
 }
@@ -679,10 +1078,16 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
     if (a.splits == 1) fill_o<kG>(a, b, seq_len, g, lane);
     return;
   }
-  __shared__ StepStash<kG> stash;
-  decode_range<kDtype, kStep, kG>(a, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
-                                  ((size_t)b * kG * kKvHeads) * a.splits + split, a.splits, g,
-                                  lane, stash);
+  const size_t part_base = ((size_t)b * kG * kKvHeads) * a.splits + split;
+  if constexpr (use_mfma<kG>(kDtype)) {
+    __shared__ MfmaStash<kG> stash;
+    decode_range_mfma<kStep, kG>(a, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
+                                 part_base, a.splits, g, lane, stash);
+  } else {
+    __shared__ StepStash<kG> stash;
+    decode_range<kDtype, kStep, kG>(a, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
+                                    part_base, a.splits, g, lane, stash);
+  }
 }
 
 // Balanced decode: the batch's pages, in sequence order, are cut into
@@ -699,7 +1104,7 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head
   __shared__ int prefix[kMaxBalancedBatch + 1];  // prefix[b] = pages of sequences < b
   __shared__ int wave_total[kDecodeWavesPerBlock];
-  __shared__ StepStash<kG> stash;
+  __shared__ std::conditional_t<use_mfma<kG>(kDtype), MfmaStash<kG>, StepStash<kG>> stash;
 
   // Block-wide exclusive scan of the page counts; thread t owns sequences
   // 8t .. 8t+7.
@@ -760,8 +1165,12 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
     const int npages = next - base;
     const int p0 = s - base, p1 = seg_end - base;
     const bool whole = p0 == 0 && p1 == npages;
-    decode_range<kDtype, kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
-                                    (size_t)(b + k) * kH, 1, g, lane, stash);
+    if constexpr (use_mfma<kG>(kDtype))
+      decode_range_mfma<kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
+                                   (size_t)(b + k) * kH, 1, g, lane, stash);
+    else
+      decode_range<kDtype, kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
+                                      (size_t)(b + k) * kH, 1, g, lane, stash);
     s = seg_end;
     if (s >= e) break;
     do { ++b; } while (prefix[b + 1] == prefix[b]);  // next sequence with pages
