@@ -130,8 +130,8 @@ def main():
     B = w.batch
     L = int(seq_lens.max())
     H = w.num_heads
-    plan = dah.plan_decode(B, L, args.num_splits, num_heads=H)
-    ws_bytes = dah.workspace_bytes(B, L, args.num_splits, num_heads=H)
+    plan = dah.plan_decode(B, L, args.num_splits, num_heads=H, cache_dtype=w.cache_dtype)
+    ws_bytes = dah.workspace_bytes(B, L, args.num_splits, num_heads=H, cache_dtype=w.cache_dtype)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     q_out = torch.empty_like(t["q"])
     o = torch.empty_like(t["q"])

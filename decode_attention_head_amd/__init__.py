@@ -94,12 +94,27 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _dtype_code(cache_dtype) -> int:
+    """DAH_BF16 / DAH_F32 from "bf16" / "f32" or a torch dtype."""
+    if cache_dtype in ("bf16", DAH_BF16):
+        return DAH_BF16
+    if cache_dtype in ("f32", DAH_F32):
+        return DAH_F32
+    torch = _torch()
+    if cache_dtype == torch.bfloat16:
+        return DAH_BF16
+    if cache_dtype == torch.float32:
+        return DAH_F32
+    raise TypeError(f"cache dtype must be bfloat16 or float32, got {cache_dtype}")
+
+
 def plan_decode(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | None = None,
-                num_heads: int = NUM_HEADS) -> dict:
+                num_heads: int = NUM_HEADS, cache_dtype="bf16") -> dict:
     """How the decode will cut the work (dah_plan_decode): a dict with mode
     ("per_sequence", "split" or "balanced"), splits, pages_per_split,
     workgroups and workspace_bytes.  num_cus defaults to the current device's
-    compute-unit count."""
+    compute-unit count; num_heads and cache_dtype select the kernel (the
+    matrix-core one for bfloat16 and 32+ heads), which the plan depends on."""
     from ._native import PLAN_MODES, DecodePlan
     if num_cus is None:
         torch = _torch()
@@ -108,19 +123,22 @@ def plan_decode(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | No
     if num_heads == NUM_HEADS:
         st = lib().dah_plan_decode(B, max_seq_len, num_splits, num_cus, ctypes.byref(p))
     else:
-        st = lib().dah_plan_decode_ex(B, num_heads, max_seq_len, num_splits, num_cus,
-                                      ctypes.byref(p))
+        st = lib().dah_plan_decode_ex(B, num_heads, _dtype_code(cache_dtype), max_seq_len,
+                                      num_splits, num_cus, ctypes.byref(p))
     check(st, "dah_plan_decode")
     return {"mode": PLAN_MODES[p.mode], "splits": p.splits, "pages_per_split": p.pages_per_split,
             "workgroups": p.workgroups, "workspace_bytes": int(p.workspace_bytes)}
 
 
 def workspace_bytes(B: int, max_seq_len: int, num_splits: int = 0,
-                    num_cus: int | None = None, num_heads: int = NUM_HEADS) -> int:
+                    num_cus: int | None = None, num_heads: int = NUM_HEADS,
+                    cache_dtype="bf16") -> int:
     if num_heads != NUM_HEADS:
         if num_cus is None:
-            return int(lib().dah_workspace_bytes_ex(B, num_heads, max_seq_len, num_splits))
-        return plan_decode(B, max_seq_len, num_splits, num_cus, num_heads)["workspace_bytes"]
+            return int(lib().dah_workspace_bytes_ex(B, num_heads, _dtype_code(cache_dtype),
+                                                    max_seq_len, num_splits))
+        return plan_decode(B, max_seq_len, num_splits, num_cus, num_heads,
+                           cache_dtype)["workspace_bytes"]
     if num_cus is None:
         return int(lib().dah_workspace_bytes(B, max_seq_len, num_splits))
     return int(lib().dah_workspace_bytes_for(B, max_seq_len, num_splits, num_cus))
@@ -132,9 +150,9 @@ def _heads(q) -> int:
     return int(q.shape[1])
 
 
-def _workspace(workspace, B, H, max_seq_len, num_splits, device):
+def _workspace(workspace, B, H, dt, max_seq_len, num_splits, device):
     torch = _torch()
-    need = workspace_bytes(B, max_seq_len, num_splits, num_heads=H)
+    need = workspace_bytes(B, max_seq_len, num_splits, num_heads=H, cache_dtype=dt)
     if workspace is None:
         if need == 0:
             return None, 0
@@ -185,7 +203,7 @@ def paged_decode_gqa(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: in
     if o is None:
         o = torch.empty_like(q)
     _require(o, "o", torch.float32, (B, H, HEAD_DIM), dev)
-    ws, ws_bytes = _workspace(workspace, B, H, max_seq_len, num_splits, dev)
+    ws, ws_bytes = _workspace(workspace, B, H, dt, max_seq_len, num_splits, dev)
     head = (_ptr(q), _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
             block_table.shape[1], _ptr(seq_lens), B)
     tail = (int(max_seq_len), int(num_splits), _ptr(o), None if ws is None else _ptr(ws),
@@ -218,7 +236,7 @@ def decode_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_ta
         o = torch.empty_like(q)
     _require(q_out, "q_out", torch.float32, (B, H, HEAD_DIM), dev)
     _require(o, "o", torch.float32, (B, H, HEAD_DIM), dev)
-    ws, ws_bytes = _workspace(workspace, B, H, max_seq_len, num_splits, dev)
+    ws, ws_bytes = _workspace(workspace, B, H, dt, max_seq_len, num_splits, dev)
     head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
             _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
             block_table.shape[1], _ptr(seq_lens), B)

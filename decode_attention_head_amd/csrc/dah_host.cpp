@@ -21,7 +21,10 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 //    unit) for batches of at least kBalancedMinBatch sequences, where ragged
 //    lengths would otherwise leave most of the device idle behind the longest
 //    sequences (128 log-uniform lengths: 212 us against 233 us for the best
-//    fixed split);
+//    fixed split); from kBalancedMinBatchMfma sequences for the matrix-core
+//    kernel, whose one workgroup per compute unit gains more from even work
+//    (32 sequences of 512-4096 positions, 40 heads: 61 us against 73 us;
+//    the VALU kernel at 16 heads: 58 us against 56 us);
 //  * fixed splits, spread over the XCDs, for fewer sequences (4 long ones:
 //    88 us against 97 us balanced), keeping splits between kMinPagesPerSplit
 //    and kMaxPagesPerSplit pages and aiming at kTargetWavesPerCu waves.
@@ -30,6 +33,7 @@ constexpr int kMinPagesPerSplit = 4;
 constexpr int kMaxPagesPerSplit = 128;
 constexpr int kBalancedGroupsPerCu = 1;
 constexpr int kBalancedMinBatch = 64;
+constexpr int kBalancedMinBatchMfma = 32;
 }  // namespace
 
 int set_error(int status, const char* fmt, ...) {
@@ -55,7 +59,8 @@ int check_heads(int num_heads) {
 }
 }  // namespace
 
-int plan_decode(int B, int num_heads, int max_seq_len, int num_splits, int num_cus, Plan* out) {
+int plan_decode(int B, int num_heads, int cache_dtype, int max_seq_len, int num_splits,
+                int num_cus, Plan* out) {
   if (out == nullptr) return set_error(DAH_ERR_NULL, "plan_decode: output pointer is NULL");
   if (B < 1) return set_error(DAH_ERR_SHAPE, "B = %d, need B >= 1", B);
   if (check_heads(num_heads) != DAH_OK) return DAH_ERR_SHAPE;
@@ -72,7 +77,9 @@ int plan_decode(int B, int num_heads, int max_seq_len, int num_splits, int num_c
   int want = 0;  // splits for DAH_PLAN_SPLIT
   if (num_splits == 1 || (num_splits == 0 && B >= num_cus && max_pages <= kMaxPagesPerSplit)) {
     p.mode = DAH_PLAN_PER_SEQUENCE;
-  } else if (num_splits == 0 && balanced_fits && B >= kBalancedMinBatch) {
+  } else if (num_splits == 0 && balanced_fits &&
+             B >= (decode_uses_mfma(num_heads, cache_dtype) ? kBalancedMinBatchMfma
+                                                            : kBalancedMinBatch)) {
     p.mode = DAH_PLAN_BALANCED;
   } else {
     p.mode = DAH_PLAN_SPLIT;
@@ -194,11 +201,14 @@ int validate_decode(const void* q, const void* k_cache, const void* v_cache, int
 
 extern "C" {
 
-int dah_plan_decode_ex(int B, int num_heads, int max_seq_len, int num_splits, int num_cus,
-                       dah_decode_plan* out) {
+int dah_plan_decode_ex(int B, int num_heads, int cache_dtype, int max_seq_len, int num_splits,
+                       int num_cus, dah_decode_plan* out) {
   if (!out) return dah::set_error(DAH_ERR_NULL, "dah_plan_decode: output pointer is NULL");
+  if (cache_dtype != DAH_F32 && cache_dtype != DAH_BF16)
+    return dah::set_error(DAH_ERR_DTYPE, "cache_dtype = %d, need DAH_F32 (0) or DAH_BF16 (1)",
+                          cache_dtype);
   dah::Plan p;
-  int st = dah::plan_decode(B, num_heads, max_seq_len, num_splits, num_cus, &p);
+  int st = dah::plan_decode(B, num_heads, cache_dtype, max_seq_len, num_splits, num_cus, &p);
   if (st != DAH_OK) return st;
   out->mode = p.mode;
   out->splits = p.splits;
@@ -209,12 +219,13 @@ int dah_plan_decode_ex(int B, int num_heads, int max_seq_len, int num_splits, in
 }
 
 int dah_plan_decode(int B, int max_seq_len, int num_splits, int num_cus, dah_decode_plan* out) {
-  return dah_plan_decode_ex(B, dah::kHeads, max_seq_len, num_splits, num_cus, out);
+  return dah_plan_decode_ex(B, dah::kHeads, DAH_BF16, max_seq_len, num_splits, num_cus, out);
 }
 
 size_t dah_workspace_bytes_for(int B, int max_seq_len, int num_splits, int num_cus) {
   dah::Plan p;
-  if (dah::plan_decode(B, dah::kHeads, max_seq_len, num_splits, num_cus, &p) != DAH_OK) return 0;
+  if (dah::plan_decode(B, dah::kHeads, DAH_BF16, max_seq_len, num_splits, num_cus, &p) != DAH_OK)
+    return 0;
   return p.workspace;
 }
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dah.h"
+
 namespace dah {
 
 constexpr int kHeads = 16;     // query heads of Qwen3-0.6B (the default entry points)
@@ -32,10 +34,17 @@ struct Plan {
   size_t workspace;     // bytes of partial results
 };
 
-// Planner: pure integer policy from the batch size, the longest sequence and
-// the compute-unit count; the head count sizes the workspace.  Returns a
-// dah_status.
-int plan_decode(int B, int num_heads, int max_seq_len, int num_splits, int num_cus, Plan* out);
+// Whether the decode runs on the matrix cores: a bfloat16 cache with 4 or
+// more query heads per KV head.
+inline bool decode_uses_mfma(int num_heads, int cache_dtype) {
+  return cache_dtype == DAH_BF16 && num_heads / kKvHeads >= 4;
+}
+
+// Planner: pure integer policy from the batch size, the longest sequence, the
+// compute-unit count and the kernel that will run (head count and cache
+// dtype); the head count also sizes the workspace.  Returns a dah_status.
+int plan_decode(int B, int num_heads, int cache_dtype, int max_seq_len, int num_splits,
+                int num_cus, Plan* out);
 
 int validate_append(const void* q, const void* k_new, const void* v_new, const void* q_gain,
                     const void* k_gain, float eps, float rope_theta, const void* k_cache,

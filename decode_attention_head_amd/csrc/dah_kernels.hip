@@ -666,11 +666,25 @@ constexpr float kMaxLag = 8.0f;
 template <int kG>
 constexpr bool use_mfma(int dtype) { return dtype == DAH_BF16 && kG >= 4; }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bfloat16 (round to nearest even; v_cvt_pk_bf16_f32),
+// `lo` in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)to_bf16(lo) | ((uint32_t)to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// Maximum over the four wave rows (lanes c, c+16, c+32, c+48): the two row
+// swaps pair rows (0,1),(2,3), then (0,2),(1,3).
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // K tile in the score product's A layout.
 struct KTileMfma {
@@ -692,18 +706,22 @@ struct MfmaStash {
   float q[kDecodeWavesPerBlock][kG][kHeadDim];  // [wave][head][dim]
 };
 
-// Scores of one page: lane (r, c) gets head c at positions 4v + r.
+// Scores of one page: lane (r, c) gets head c at positions 4v + r.  One
+// accumulator per query term keeps three independent chains of four
+// products in flight instead of one chain of twelve.
 __device__ __forceinline__ f32x4 page_scores(const KTileMfma& K, const u32x4 (&qb)[4][3]) {
-  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4 s[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) s[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const bf16x8 a = __builtin_bit_cast(bf16x8, K.w[kk]);
 #pragma unroll
     for (int t = 0; t < 3; ++t)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qb[kk][t]), s, 0,
-                                                   0, 0);
+      s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qb[kk][t]),
+                                                      s[t], 0, 0, 0);
   }
-  return s;
+  return (s[0] + s[1]) + s[2];
 }
 
 // Online-softmax state of the MFMA decode.  m and l are per lane for head c
@@ -730,9 +748,7 @@ __device__ __forceinline__ void attend_page_mfma(const KTileMfma& K, Tile<DAH_BF
       if (!ok) V.clear(v);
     }
   }
-  float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  pm = fmaxf(pm, __shfl_xor(pm, 16));
-  pm = fmaxf(pm, __shfl_xor(pm, 32));
+  const float pm = max_over_rows(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
   // Move the reference only when a score passes it by more than kMaxLag
   // (always from -inf); a wave-uniform branch, rarely taken after the
   // first page.
@@ -755,18 +771,11 @@ __device__ __forceinline__ void attend_page_mfma(const KTileMfma& K, Tile<DAH_BF
   for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[v] - mu);
   st.l += (p[0] + p[1]) + (p[2] + p[3]);
   // Weights as hi + lo bfloat16 terms.
-  float lo[4];
-  uint16_t hb[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    hb[v] = to_bf16(p[v]);
-    lo[v] = p[v] - bf16_val(hb[v]);
-  }
   u32x4 aw;
-  aw[0] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-  aw[1] = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
-  aw[2] = pack_bf16x2(lo[0], lo[1]);
-  aw[3] = pack_bf16x2(lo[2], lo[3]);
+  aw[0] = pack_bf16x2(p[0], p[1]);
+  aw[1] = pack_bf16x2(p[2], p[3]);
+  aw[2] = pack_bf16x2(p[0] - bf16_lo(aw[0]), p[1] - bf16_hi(aw[0]));
+  aw[3] = pack_bf16x2(p[2] - bf16_lo(aw[1]), p[3] - bf16_hi(aw[1]));
   const bf16x8 a = __builtin_bit_cast(bf16x8, aw);
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
@@ -787,14 +796,12 @@ __device__ __forceinline__ void split3(const float (&x)[8], u32x4 (&out)[3]) {
   for (int e = 0; e < 8; ++e) rem[e] = x[e];
 #pragma unroll
   for (int t = 0; t < 3; ++t) {
-    uint16_t h[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      h[e] = to_bf16(rem[e]);
-      rem[e] -= bf16_val(h[e]);
+    for (int i = 0; i < 4; ++i) {
+      out[t][i] = pack_bf16x2(rem[2 * i], rem[2 * i + 1]);
+      rem[2 * i] -= bf16_lo(out[t][i]);
+      rem[2 * i + 1] -= bf16_hi(out[t][i]);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[t][i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
   }
 }
 
@@ -1165,12 +1172,17 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
     const int npages = next - base;
     const int p0 = s - base, p1 = seg_end - base;
     const bool whole = p0 == 0 && p1 == npages;
+    // An opaque copy of the lane index per segment: otherwise the compiler
+    // hoists lane-dependent values of the range out of this loop and keeps
+    // them live across it, which costs 30-50 registers (and spills).
+    int lane_i = lane;
+    asm volatile("" : "+v"(lane_i));
     if constexpr (use_mfma<kG>(kDtype))
       decode_range_mfma<kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
-                                   (size_t)(b + k) * kH, 1, g, lane, stash);
+                                   (size_t)(b + k) * kH, 1, g, lane_i, stash);
     else
       decode_range<kDtype, kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
-                                      (size_t)(b + k) * kH, 1, g, lane, stash);
+                                      (size_t)(b + k) * kH, 1, g, lane_i, stash);
     s = seg_end;
     if (s >= e) break;
     do { ++b; } while (prefix[b + 1] == prefix[b]);  // next sequence with pages
@@ -1529,12 +1541,12 @@ struct StepInputs {
   void* v_cache;
 };
 
-int plan_for(int B, int num_heads, int max_seq_len, int num_splits, void* workspace,
-             size_t workspace_bytes, dah::Plan* plan) {
+int plan_for(int B, int num_heads, int cache_dtype, int max_seq_len, int num_splits,
+             void* workspace, size_t workspace_bytes, dah::Plan* plan) {
   int cus = 0;
   int st = device_cu_count(&cus);
   if (st != DAH_OK) return st;
-  st = dah::plan_decode(B, num_heads, max_seq_len, num_splits, cus, plan);
+  st = dah::plan_decode(B, num_heads, cache_dtype, max_seq_len, num_splits, cus, plan);
   if (st != DAH_OK) return st;
   if (plan->workspace > 0) {
     if (workspace == nullptr || workspace_bytes < plan->workspace)
@@ -1663,7 +1675,8 @@ int paged_decode_gqa_ex(const float* q, const void* k_cache, const void* v_cache
                                 num_splits, o);
   if (st != DAH_OK) return st;
   dah::Plan plan;
-  st = plan_for(B, num_heads, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
+  st = plan_for(B, num_heads, cache_dtype, max_seq_len, num_splits, workspace, workspace_bytes,
+                &plan);
   if (st != DAH_OK) return st;
   return launch_decode(plan, q, k_cache, v_cache, cache_dtype, num_pages, block_table,
                        max_pages_per_seq, seq_lens, B, num_heads, max_seq_len, o, workspace,
@@ -1697,7 +1710,8 @@ int decode_attn_step_ex(const float* q, const float* k_new, const float* v_new,
   // Plan and check the workspace before anything is launched, so that a
   // failing call leaves the cache untouched.
   dah::Plan plan;
-  st = plan_for(B, num_heads, max_seq_len, num_splits, workspace, workspace_bytes, &plan);
+  st = plan_for(B, num_heads, cache_dtype, max_seq_len, num_splits, workspace, workspace_bytes,
+                &plan);
   if (st != DAH_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (q_out == q && plan.mode != DAH_PLAN_PER_SEQUENCE) {
@@ -1732,16 +1746,19 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
                              workspace_bytes, stream);
 }
 
-size_t dah_workspace_bytes_ex(int B, int num_heads, int max_seq_len, int num_splits) {
+size_t dah_workspace_bytes_ex(int B, int num_heads, int cache_dtype, int max_seq_len,
+                              int num_splits) {
+  if (cache_dtype != DAH_F32 && cache_dtype != DAH_BF16) return 0;
   int cus = 0;
   if (device_cu_count(&cus) != DAH_OK) return 0;
   dah::Plan p;
-  if (dah::plan_decode(B, num_heads, max_seq_len, num_splits, cus, &p) != DAH_OK) return 0;
+  if (dah::plan_decode(B, num_heads, cache_dtype, max_seq_len, num_splits, cus, &p) != DAH_OK)
+    return 0;
   return p.workspace;
 }
 
 size_t dah_workspace_bytes(int B, int max_seq_len, int num_splits) {
-  return dah_workspace_bytes_ex(B, kHeads, max_seq_len, num_splits);
+  return dah_workspace_bytes_ex(B, kHeads, DAH_BF16, max_seq_len, num_splits);
 }
 
 }  // extern "C"

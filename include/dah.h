@@ -241,10 +241,18 @@ int decode_attn_step_ex(const float* q, const float* k_new, const float* v_new,
                         int num_splits, float* q_out, float* o, void* workspace,
                         size_t workspace_bytes, void* stream);
 
-int dah_plan_decode_ex(int B, int num_heads, int max_seq_len, int num_splits, int num_cus,
-                       dah_decode_plan* out);
+/*
+ * The planner and workspace size for num_heads query heads and a cache of
+ * cache_dtype: with a bfloat16 cache and 32 or more heads the decode runs on
+ * the matrix cores, and the balanced plan starts at 32 sequences instead of
+ * 64.  dah_plan_decode_ex returns DAH_ERR_DTYPE for an unknown dtype;
+ * dah_workspace_bytes_ex returns 0 for invalid arguments.
+ */
+int dah_plan_decode_ex(int B, int num_heads, int cache_dtype, int max_seq_len, int num_splits,
+                       int num_cus, dah_decode_plan* out);
 
-size_t dah_workspace_bytes_ex(int B, int num_heads, int max_seq_len, int num_splits);
+size_t dah_workspace_bytes_ex(int B, int num_heads, int cache_dtype, int max_seq_len,
+                              int num_splits);
 
 /* Static name of a dah_status value ("DAH_OK", ...); "unknown status" otherwise. */
 const char* dah_status_string(int status);

@@ -257,14 +257,22 @@ FAMILY_HEADS = [16, 32, 40, 64]
 
 
 @pytest.mark.parametrize("H", FAMILY_HEADS)
+@pytest.mark.parametrize("dt", [0, 1])
 @pytest.mark.parametrize("B,L,n", [(256, 2048, 0), (32, 4096, 0), (4, 40960, 0), (128, 16384, 0),
-                                   (7, 999, 3)])
-def test_planner_ex_scales_the_workspace_with_heads(H, B, L, n):
+                                   (7, 999, 3), (48, 3000, 0), (63, 5000, 0)])
+def test_planner_ex_scales_the_workspace_with_heads(H, dt, B, L, n):
     lib = _lib()
     p16, ph = native.DecodePlan(), native.DecodePlan()
     assert lib.dah_plan_decode(B, L, n, 256, ctypes.byref(p16)) == 0
-    assert lib.dah_plan_decode_ex(B, H, L, n, 256, ctypes.byref(ph)) == 0
-    # the cut of the positions does not depend on the head count
+    assert lib.dah_plan_decode_ex(B, H, dt, L, n, 256, ctypes.byref(ph)) == 0
+    mfma = dt == 1 and H >= 32
+    if mfma and n == 0 and 32 <= B < 64:
+        # the matrix-core kernel takes the balanced plan from 32 sequences
+        assert native.PLAN_MODES[ph.mode] == "balanced"
+        assert native.PLAN_MODES[p16.mode] == "split"
+        assert ph.workspace_bytes == (B + ph.workgroups - 1) * H * 130 * 4
+        return
+    # otherwise the cut of the positions does not depend on the head count
     assert (ph.mode, ph.splits, ph.pages_per_split, ph.workgroups) == \
         (p16.mode, p16.splits, p16.pages_per_split, p16.workgroups)
     assert ph.workspace_bytes * 16 == p16.workspace_bytes * H
@@ -274,7 +282,7 @@ def test_planner_ex_scales_the_workspace_with_heads(H, B, L, n):
 def test_ex_calls_reject_other_head_counts(H):
     lib = _lib()
     p = native.DecodePlan()
-    assert lib.dah_plan_decode_ex(2, H, 64, 0, 256, ctypes.byref(p)) == 2
+    assert lib.dah_plan_decode_ex(2, H, 1, 64, 0, 256, ctypes.byref(p)) == 2
     assert "num_heads" in lib.dah_last_error().decode()
     assert lib.paged_decode_gqa_ex(A, A, A, 1, 16, A, 4, A, 2, H, 64, 0, A, None, 0, None) == 2
     assert lib.qk_norm_rope_append_ex(A, A, A, A, A, 1e-6, 1e6, A, A, 1, 16, A, 4, A, 2, H, A,
@@ -295,3 +303,11 @@ def test_ex_calls_validate_like_the_base_calls(H):
                                       None) == 2
     assert lib.decode_attn_step_ex(A, A, A, A, A, 1e-6, 1e6, A, A, 1, 16, A, 4, A, 2, H, 64, 0,
                                    None, A, None, 0, None) == 1
+
+
+def test_planner_ex_rejects_unknown_dtype():
+    lib = _lib()
+    p = native.DecodePlan()
+    assert lib.dah_plan_decode_ex(8, 32, 2, 64, 0, 256, ctypes.byref(p)) == 3
+    assert lib.dah_plan_decode_ex(8, 32, 1, 64, 0, 256, None) == 1
+    assert lib.dah_workspace_bytes_ex(8, 32, 7, 64, 0) == 0

@@ -132,14 +132,19 @@ def test_full_size_step(H):
 
 
 @pytest.mark.parametrize("H,name", [(32, "long_b4_s40960"), (64, "long_b4_s40960"),
-                                    (40, "stack28_b128"), (64, "stack28_b128")])
+                                    (40, "stack28_b128"), (64, "stack28_b128"),
+                                    (40, "ragged_b32"), (64, "ragged_b32")])
 def test_split_and_balanced_decode(H, name):
     """The split plan (4 sequences up to 40,960 positions) and the balanced
-    plan (128 log-uniform lengths) with more query heads, sampled."""
+    plan (128 log-uniform lengths; 32 ragged lengths, which the matrix-core
+    kernel also cuts evenly) with more query heads, sampled."""
     import torch
     dah = _dah()
     w = _with_heads(name, H)
-    _print(f"[family decode] {name} H={H} plan={dah.plan_decode(w.batch, w.max_seq_len())['mode']}")
+    plan = dah.plan_decode(w.batch, w.max_seq_len(), num_heads=H, cache_dtype=w.cache_dtype)
+    _print(f"[family decode] {name} H={H} plan={plan['mode']}")
+    if name != "long_b4_s40960":
+        assert plan["mode"] == "balanced"
     t, seq_lens, table, _ = build_layer(w)
     sample = sample_batch(seq_lens, 4)
     snap = host_snapshot(t, seq_lens, table, sample)
@@ -150,6 +155,30 @@ def test_split_and_balanced_decode(H, name):
     dist = distance_to_uniform(o_ref, snap, "bf16")
     e_abs, e_rel = gates(o[sample].cpu().numpy().astype(np.float64), o_ref, dist, 2e-2,
                          label=f"{name} H={H}")
+    _print(f"  o max abs {e_abs:.3g}  rel-to-max {e_rel:.3g}")
+
+
+@pytest.mark.parametrize("H", [32, 64])
+def test_balanced_step(H):
+    """The fused step under the balanced plan (32 ragged sequences, bf16
+    cache: the matrix-core kernel), sampled, q_out and the stored slot too."""
+    import torch
+    dah = _dah()
+    w = _with_heads("ragged_b32", H, 5e6)
+    _print(f"[family balanced step] H={H}")
+    t, seq_lens, table, _ = build_layer(w)
+    sample = sample_batch(seq_lens, 6)
+    snap = host_snapshot(t, seq_lens, table, sample)
+    q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    int(seq_lens.max()), rope_theta=5e6)
+    torch.cuda.synchronize()
+    ref = oracle_step(snap, "bf16", theta=5e6)
+    assert float(np.max(np.abs(q_out[sample].cpu().numpy() - ref["q_out"]))) <= 1e-5
+    _, v_slot = read_slots(t, seq_lens, table, sample)
+    assert np.array_equal(v_slot, ref["v_slot"])
+    e_abs, e_rel = gates(o[sample].cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
+                         label=f"H={H}")
     _print(f"  o max abs {e_abs:.3g}  rel-to-max {e_rel:.3g}")
 
 
