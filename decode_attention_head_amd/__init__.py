@@ -110,30 +110,28 @@ def _dtype_code(cache_dtype) -> int:
 
 def plan_decode(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | None = None,
                 num_heads: int = NUM_HEADS, cache_dtype="bf16") -> dict:
-    """How the decode will cut the work (dah_plan_decode): a dict with mode
+    """How the decode will cut the work (dah_plan_decode_ex): a dict with mode
     ("per_sequence", "split" or "balanced"), splits, pages_per_split,
-    workgroups and workspace_bytes.  num_cus defaults to the current device's
-    compute-unit count; num_heads and cache_dtype select the kernel (the
-    matrix-core one for bfloat16 and 32+ heads), which the plan depends on."""
+    workgroups, workspace_bytes and kernel ("valu" or "mfma").  num_cus
+    defaults to the current device's compute-unit count; the plan depends on
+    the head count and the cache dtype through the kernel they select."""
     from ._native import PLAN_MODES, DecodePlan
     if num_cus is None:
         torch = _torch()
         num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
     p = DecodePlan()
-    if num_heads == NUM_HEADS:
-        st = lib().dah_plan_decode(B, max_seq_len, num_splits, num_cus, ctypes.byref(p))
-    else:
-        st = lib().dah_plan_decode_ex(B, num_heads, _dtype_code(cache_dtype), max_seq_len,
-                                      num_splits, num_cus, ctypes.byref(p))
-    check(st, "dah_plan_decode")
+    st = lib().dah_plan_decode_ex(B, num_heads, _dtype_code(cache_dtype), max_seq_len,
+                                  num_splits, num_cus, ctypes.byref(p))
+    check(st, "dah_plan_decode_ex")
     return {"mode": PLAN_MODES[p.mode], "splits": p.splits, "pages_per_split": p.pages_per_split,
-            "workgroups": p.workgroups, "workspace_bytes": int(p.workspace_bytes)}
+            "workgroups": p.workgroups, "workspace_bytes": int(p.workspace_bytes),
+            "kernel": "mfma" if p.kernel == 1 else "valu"}
 
 
 def workspace_bytes(B: int, max_seq_len: int, num_splits: int = 0,
                     num_cus: int | None = None, num_heads: int = NUM_HEADS,
                     cache_dtype="bf16") -> int:
-    if num_heads != NUM_HEADS:
+    if num_heads != NUM_HEADS or _dtype_code(cache_dtype) != DAH_BF16:
         if num_cus is None:
             return int(lib().dah_workspace_bytes_ex(B, num_heads, _dtype_code(cache_dtype),
                                                     max_seq_len, num_splits))

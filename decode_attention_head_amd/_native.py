@@ -64,7 +64,7 @@ class DecodePlan(ctypes.Structure):
     """dah_decode_plan of include/dah.h."""
     _fields_ = [("mode", ctypes.c_int), ("splits", ctypes.c_int),
                 ("pages_per_split", ctypes.c_int), ("workgroups", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int)]
 
 
 class DahError(RuntimeError):

@@ -21,13 +21,18 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 //    unit) for batches of at least kBalancedMinBatch sequences, where ragged
 //    lengths would otherwise leave most of the device idle behind the longest
 //    sequences (128 log-uniform lengths: 212 us against 233 us for the best
-//    fixed split); from kBalancedMinBatchMfma sequences for the matrix-core
-//    kernel, whose one workgroup per compute unit gains more from even work
-//    (32 sequences of 512-4096 positions, 40 heads: 61 us against 73 us;
-//    the VALU kernel at 16 heads: 58 us against 56 us);
+//    fixed split); from kBalancedMinBatchMfma sequences when 4+ query heads
+//    per KV head put the decode on the matrix cores, whose one workgroup per
+//    compute unit gains more from even work (32 sequences of 512-4096
+//    positions, 40 heads: 61 us against 73 us; at 16 heads 58.7 us against
+//    56.8 us for fixed splits on the VALU kernel);
 //  * fixed splits, spread over the XCDs, for fewer sequences (4 long ones:
 //    88 us against 97 us balanced), keeping splits between kMinPagesPerSplit
 //    and kMaxPagesPerSplit pages and aiming at kTargetWavesPerCu waves.
+// Kernel: with a bfloat16 cache the matrix-core decode runs for 4+ query
+// heads per KV head always, and for 2 unless the plan is fixed splits
+// (B=256, S=2048: 323 us against 329 us; 128 ragged sequences, balanced:
+// 205 against 210; 4 long sequences, split: 95 against 88).
 constexpr int kTargetWavesPerCu = 8;
 constexpr int kMinPagesPerSplit = 4;
 constexpr int kMaxPagesPerSplit = 128;
@@ -71,6 +76,8 @@ int plan_decode(int B, int num_heads, int cache_dtype, int max_seq_len, int num_
   if (num_cus < 1) return set_error(DAH_ERR_SHAPE, "num_cus = %d, need >= 1", num_cus);
 
   const int max_pages = (max_seq_len + kPage - 1) / kPage;
+  const bool bf16 = cache_dtype == DAH_BF16;
+  const bool big_group = num_heads / kKvHeads >= 4;
   Plan p = {};
   const bool balanced_fits =
       B <= kMaxBalancedBatch && static_cast<long long>(B) * max_pages < (1LL << 31);
@@ -78,8 +85,7 @@ int plan_decode(int B, int num_heads, int cache_dtype, int max_seq_len, int num_
   if (num_splits == 1 || (num_splits == 0 && B >= num_cus && max_pages <= kMaxPagesPerSplit)) {
     p.mode = DAH_PLAN_PER_SEQUENCE;
   } else if (num_splits == 0 && balanced_fits &&
-             B >= (decode_uses_mfma(num_heads, cache_dtype) ? kBalancedMinBatchMfma
-                                                            : kBalancedMinBatch)) {
+             B >= (bf16 && big_group ? kBalancedMinBatchMfma : kBalancedMinBatch)) {
     p.mode = DAH_PLAN_BALANCED;
   } else {
     p.mode = DAH_PLAN_SPLIT;
@@ -132,6 +138,7 @@ int plan_decode(int B, int num_heads, int cache_dtype, int max_seq_len, int num_
       }
     }
   }
+  p.mfma = bf16 && (big_group || p.mode != DAH_PLAN_SPLIT);
   *out = p;
   return DAH_OK;
 }
@@ -215,6 +222,7 @@ int dah_plan_decode_ex(int B, int num_heads, int cache_dtype, int max_seq_len, i
   out->pages_per_split = p.pages_per_split;
   out->workgroups = p.workgroups;
   out->workspace_bytes = p.workspace;
+  out->kernel = p.mfma ? DAH_KERNEL_MFMA : DAH_KERNEL_VALU;
   return DAH_OK;
 }
 

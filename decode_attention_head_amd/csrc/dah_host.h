@@ -32,13 +32,8 @@ struct Plan {
   int grid_splits;      // DAH_PLAN_SPLIT: splits padded to a multiple of 8 for the XCD mapping
   int workgroups;       // grid of the decode launch
   size_t workspace;     // bytes of partial results
+  bool mfma;            // matrix-core decode (bfloat16 cache only)
 };
-
-// Whether the decode runs on the matrix cores: a bfloat16 cache with 4 or
-// more query heads per KV head.
-inline bool decode_uses_mfma(int num_heads, int cache_dtype) {
-  return cache_dtype == DAH_BF16 && num_heads / kKvHeads >= 4;
-}
 
 // Planner: pure integer policy from the batch size, the longest sequence, the
 // compute-unit count and the kernel that will run (head count and cache

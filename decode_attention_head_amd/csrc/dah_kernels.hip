@@ -632,7 +632,9 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
 // shapes) the VALU form above runs out of issue slots and registers: the
 // multiply-adds grow with G while the bytes do not.  For a bfloat16 cache
 // both contractions of a page then go to the matrix cores with
-// v_mfma_f32_16x16x32_bf16.  Lane l = 16 r + c.
+// v_mfma_f32_16x16x32_bf16 (the planner also picks this form for G = 2
+// unless the sequences are cut into fixed splits, where the VALU form's
+// two workgroups per compute unit do better).  Lane l = 16 r + c.
 //
 // Scores.  A = 16 positions x 32 dims of K, B = 32 dims x 16 query-head
 // columns, D = scores.  The lane loads K position sigma(c) = 4 (c mod 4) +
@@ -662,9 +664,6 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kMaxLag = 8.0f;
-
-template <int kG>
-constexpr bool use_mfma(int dtype) { return dtype == DAH_BF16 && kG >= 4; }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -1051,8 +1050,9 @@ __device__ __forceinline__ void fill_o(const DecodeArgs& a, int b, int seq_len, 
 // One workgroup (8 waves = 8 KV heads) per (sequence, split), each split
 // `pages_per_split` pages; splits == 1 writes o directly, otherwise
 // combine_splits_kernel merges the partials.
-template <int kDtype, bool kStep, int kG>
+template <int kDtype, bool kStep, int kG, bool kMfma>
 __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_kernel(DecodeArgs a) {
+  static_assert(!kMfma || kDtype == DAH_BF16, "the matrix-core decode reads a bfloat16 cache");
   const int lane = threadIdx.x & (kWave - 1);
   // The wave index is uniform across the wave; saying so keeps everything
   // derived from it (sequence, page range, page addresses) in scalar registers.
@@ -1086,7 +1086,7 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
     return;
   }
   const size_t part_base = ((size_t)b * kG * kKvHeads) * a.splits + split;
-  if constexpr (use_mfma<kG>(kDtype)) {
+  if constexpr (kMfma) {
     __shared__ MfmaStash<kG> stash;
     decode_range_mfma<kStep, kG>(a, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
                                  part_base, a.splits, g, lane, stash);
@@ -1104,14 +1104,15 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
 // b + k (k = workgroup), which combine_balanced_kernel merges.  Consecutive
 // workgroups go to different XCDs, so every XCD gets an equal share of the
 // pages however ragged the lengths are, and no workgroup is empty.
-template <int kDtype, bool kStep, int kG>
+template <int kDtype, bool kStep, int kG, bool kMfma>
 __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_kernel(DecodeArgs a) {
+  static_assert(!kMfma || kDtype == DAH_BF16, "the matrix-core decode reads a bfloat16 cache");
   constexpr int kH = kG * kKvHeads;
   const int lane = threadIdx.x & (kWave - 1);
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head
   __shared__ int prefix[kMaxBalancedBatch + 1];  // prefix[b] = pages of sequences < b
   __shared__ int wave_total[kDecodeWavesPerBlock];
-  __shared__ std::conditional_t<use_mfma<kG>(kDtype), MfmaStash<kG>, StepStash<kG>> stash;
+  __shared__ std::conditional_t<kMfma, MfmaStash<kG>, StepStash<kG>> stash;
 
   // Block-wide exclusive scan of the page counts; thread t owns sequences
   // 8t .. 8t+7.
@@ -1177,7 +1178,7 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
     // them live across it, which costs 30-50 registers (and spills).
     int lane_i = lane;
     asm volatile("" : "+v"(lane_i));
-    if constexpr (use_mfma<kG>(kDtype))
+    if constexpr (kMfma)
       decode_range_mfma<kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
                                    (size_t)(b + k) * kH, 1, g, lane_i, stash);
     else
@@ -1560,20 +1561,28 @@ int plan_for(int B, int num_heads, int cache_dtype, int max_seq_len, int num_spl
   return DAH_OK;
 }
 
+// The kernel the plan chose: the matrix-core form for a bfloat16 cache when
+// plan.mfma (always for 4+ query heads per KV head), else the VALU form.
 template <bool kStep, int kG>
 void launch_decode_kernel(const dah::Plan& plan, bool bf16, const DecodeArgs& a,
                           hipStream_t stream) {
   const dim3 grid((unsigned)plan.workgroups), block(kWave * kDecodeWavesPerBlock);
-  if (plan.mode == DAH_PLAN_BALANCED) {
-    if (bf16)
-      decode_balanced_kernel<DAH_BF16, kStep, kG><<<grid, block, 0, stream>>>(a);
+  const bool balanced = plan.mode == DAH_PLAN_BALANCED;
+  if (!bf16) {
+    if (balanced)
+      decode_balanced_kernel<DAH_F32, kStep, kG, false><<<grid, block, 0, stream>>>(a);
     else
-      decode_balanced_kernel<DAH_F32, kStep, kG><<<grid, block, 0, stream>>>(a);
-  } else {
-    if (bf16)
-      decode_split_kernel<DAH_BF16, kStep, kG><<<grid, block, 0, stream>>>(a);
+      decode_split_kernel<DAH_F32, kStep, kG, false><<<grid, block, 0, stream>>>(a);
+  } else if (plan.mfma) {
+    if (balanced)
+      decode_balanced_kernel<DAH_BF16, kStep, kG, true><<<grid, block, 0, stream>>>(a);
     else
-      decode_split_kernel<DAH_F32, kStep, kG><<<grid, block, 0, stream>>>(a);
+      decode_split_kernel<DAH_BF16, kStep, kG, true><<<grid, block, 0, stream>>>(a);
+  } else if constexpr (kG < 4) {
+    if (balanced)
+      decode_balanced_kernel<DAH_BF16, kStep, kG, false><<<grid, block, 0, stream>>>(a);
+    else
+      decode_split_kernel<DAH_BF16, kStep, kG, false><<<grid, block, 0, stream>>>(a);
   }
 }
 

@@ -187,14 +187,22 @@ typedef enum {
   DAH_PLAN_BALANCED = 2
 } dah_plan_mode;
 
+typedef enum {
+  DAH_KERNEL_VALU = 0,  /* dot products on the vector ALUs (any cache dtype) */
+  DAH_KERNEL_MFMA = 1   /* both products on the matrix cores (bfloat16 cache) */
+} dah_decode_kernel;
+
 typedef struct {
   int mode;               /* dah_plan_mode */
   int splits;             /* splits per sequence (PER_SEQUENCE: 1; BALANCED: 0) */
   int pages_per_split;    /* pages per split (PER_SEQUENCE: the longest sequence; BALANCED: 0) */
   int workgroups;         /* workgroups of the decode launch */
   size_t workspace_bytes; /* workspace the call needs */
+  int kernel;             /* dah_decode_kernel: MFMA for a bfloat16 cache with 4+ query heads
+                             per KV head, or with 2 unless mode is DAH_PLAN_SPLIT */
 } dah_decode_plan;
 
+/* For 16 query heads and a bfloat16 cache (the kernel field); the cut is the same for float32. */
 int dah_plan_decode(int B, int max_seq_len, int num_splits, int num_cus, dah_decode_plan* out);
 
 /*

@@ -311,3 +311,25 @@ def test_planner_ex_rejects_unknown_dtype():
     assert lib.dah_plan_decode_ex(8, 32, 2, 64, 0, 256, ctypes.byref(p)) == 3
     assert lib.dah_plan_decode_ex(8, 32, 1, 64, 0, 256, None) == 1
     assert lib.dah_workspace_bytes_ex(8, 32, 7, 64, 0) == 0
+
+
+@pytest.mark.parametrize("B,L,n", [(256, 2048, 0), (32, 4096, 0), (4, 40960, 0), (128, 16384, 0),
+                                   (2, 12, 0), (7, 999, 3), (64, 100, 1)])
+@pytest.mark.parametrize("H", FAMILY_HEADS)
+def test_planner_kernel_choice(B, L, n, H):
+    """bfloat16: matrix cores for 4+ query heads per KV head, and for 2 unless
+    the plan is fixed splits; float32: always the VALU kernel."""
+    lib = _lib()
+    p = native.DecodePlan()
+    assert lib.dah_plan_decode_ex(B, H, 1, L, n, 256, ctypes.byref(p)) == 0
+    mode = native.PLAN_MODES[p.mode]
+    assert p.kernel == (1 if (H >= 32 or mode != "split") else 0), (mode, p.kernel)
+    assert lib.dah_plan_decode_ex(B, H, 0, L, n, 256, ctypes.byref(p)) == 0
+    assert p.kernel == 0
+    if H == 16:
+        q = native.DecodePlan()
+        assert lib.dah_plan_decode(B, L, n, 256, ctypes.byref(q)) == 0
+        r = native.DecodePlan()
+        assert lib.dah_plan_decode_ex(B, 16, 1, L, n, 256, ctypes.byref(r)) == 0
+        assert (q.mode, q.splits, q.workgroups, q.workspace_bytes, q.kernel) == \
+            (r.mode, r.splits, r.workgroups, r.workspace_bytes, r.kernel)

@@ -56,16 +56,22 @@ def test_split_count_invariance():
     snap = host_snapshot(t, seq_lens, table, range(len(lens)))
     ref = oracle_decode(snap, "bf16")
     L = int(max(lens))
-    outs = {}
+    outs, kernel = {}, {}
     for n in (1, 0, 2, 3, 7, 16, 64, 256):
-        _print(f"[splits] num_splits={n}")
+        kernel[n] = _dah().plan_decode(len(lens), L, n)["kernel"]
+        _print(f"[splits] num_splits={n} kernel={kernel[n]}")
         o = _decode(t, L, num_splits=n)
         torch.cuda.synchronize()
         outs[n] = o.cpu().numpy().astype(np.float64)
         gates(outs[n], ref, None, 2e-2, label=f"splits={n}")
+    # Within the VALU kernel the partition changes only the rounding order
+    # (flashAttn_eq); the matrix-core kernel (one split here) carries the
+    # weights to 2^-18, so against it the bound is that.
     base = outs[1]
+    scale = float(np.max(np.abs(base)))
     for n, o in outs.items():
-        assert np.max(np.abs(o - base)) <= 1e-6, f"splits={n} differs from 1 split"
+        tol = 1e-6 if kernel[n] == kernel[1] == "valu" else 2.0 ** -16 * scale
+        assert np.max(np.abs(o - base)) <= tol, f"splits={n} differs from 1 split"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -378,7 +384,12 @@ def test_balanced_plan_with_more_workgroups_than_pages():
     o_one = _decode(t, L, num_splits=1)
     torch.cuda.synchronize()
     assert torch.isfinite(o_bal).all()
-    assert torch.allclose(o_bal, o_one, atol=1e-6, rtol=0)
+    # The matrix-core kernel's weights depend (at 2^-18) on the softmax
+    # reference, which depends on the partition; the VALU kernel's only on
+    # the rounding order.
+    mfma = plan["kernel"] == "mfma"
+    tol = 2.0 ** -16 * float(o_one.abs().max()) if mfma else 1e-6
+    assert torch.allclose(o_bal, o_one, atol=tol, rtol=0)
     snap = host_snapshot(t, seq_lens, table, range(len(lens)))
     gates(o_bal.cpu().numpy().astype(np.float64), oracle_decode(snap, "bf16"), None, 2e-2,
           label="balanced, T < G")
