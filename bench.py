@@ -34,7 +34,11 @@ from inputs import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_head_amd", "csrc", "dah_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_b256_s2048_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"decode_split_kernel_{workload}_traffic.txt")
 
 
 def parse():
@@ -61,12 +65,14 @@ def source_digest() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic():
+def read_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    summary of this workload's fused step, if it was taken on the current
+    kernel source; else None."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_src or not m_val or m_src.group(1) != source_digest():
@@ -199,7 +205,7 @@ def main():
     kv_bytes = W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (launch_ms * 1e-3) / 1e9
-    traffic = read_traffic() if (w.name == "b256_s2048" and args.num_splits == 0) else None
+    traffic = read_traffic(w.name) if (args.num_splits == 0 and not args.decode_only) else None
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -232,7 +238,9 @@ def main():
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(B / (ms_step * 1e-3), 1),
         "roofline": {
-            "kernel": ("decode_split_kernel" + ("" if args.decode_only else " (fused step)") +
+            "kernel": (("decode_balanced_kernel" if plan["mode"] == "balanced"
+                        else "decode_split_kernel") + f" [{plan['kernel']}]" +
+                       ("" if args.decode_only else " (fused step)") +
                        ("" if plan["mode"] == "per_sequence" else " + combine")),
             "bound": "hbm",
             "achieved": round(achieved, 1),
