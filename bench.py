@@ -14,6 +14,11 @@ The JSON line reports
                   bytes per launch / its average duration measured with HIP
                   events on the launch stream, against MI355X's 8 TB/s HBM peak
   cpu_baseline    the float64 CPU oracle on a bounded sample of the same workload
+
+--block also times the projections on either side of the block (attn.qkv_proj
+before the step, attn.o_proj after it) on the same batch and reports them under
+"block": per-launch durations (HIP events), their bytes and flops, and the
+whole x -> qkv_proj -> decode_attn_step -> o_proj pass.
 """
 from __future__ import annotations
 
@@ -54,6 +59,8 @@ def parse():
                     help="time paged_decode_gqa alone (profiling aid)")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the streaming-read probe (practical bandwidth ceiling)")
+    ap.add_argument("--block", action="store_true",
+                    help="also time qkv_proj and o_proj around the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 plain device copies of this many MiB (a kernel of "
                          "known traffic, to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -114,6 +121,59 @@ def cpu_baseline(w, t, seq_lens, table, budget_s):
         "sample": f"{done} of {len(seq_lens)} sequences of {w.name}, full decode step each "
                   f"(float64 NumPy, {elapsed:.1f} s)",
     }
+
+
+def _events_mean_us(torch, stream, fn, n):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def time_block(dah, torch, w, t, L, ws, stream, args):
+    """qkv_proj and o_proj around the step, each timed alone, and the three
+    in sequence (the step then reads the projection's q, k, v)."""
+    p = W.make_projections(w, 0, t["q"].device)
+    B, H, hid = w.batch, w.num_heads, w.hidden
+    q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
+    q_out, o = torch.empty_like(q), torch.empty_like(q)
+
+    def qkv():
+        dah.qkv_proj(p["x"], p["w_qkv"], H, q=q, k=k, v=v)
+
+    def oproj():
+        dah.o_proj(o, p["w_o"], y=y)
+
+    def whole():
+        qkv()
+        dah.decode_attn_step(q, k, v, t["q_gain"], t["k_gain"], t["k_pool"], t["v_pool"],
+                             t["block_table"], t["seq_lens"], L, rope_theta=w.rope_theta,
+                             num_splits=args.num_splits, q_out=q_out, o=o, workspace=ws)
+        oproj()
+
+    y = torch.empty((B, hid), dtype=torch.float32, device=o.device)
+    n = max(20, min(args.steps, 100))
+    for fn in (qkv, oproj, whole):
+        for _ in range(5):
+            fn()
+    torch.cuda.synchronize()
+    qkv_us = _events_mean_us(torch, stream, qkv, n)
+    o_us = _events_mean_us(torch, stream, oproj, n)
+    whole_us = _events_mean_us(torch, stream, whole, max(10, n // 4))
+
+    def stats(us, n_out, k_in):
+        byts = n_out * k_in * 2 + B * k_in * 4 + B * n_out * 4   # bf16 weights, f32 x and y
+        flop = 2.0 * B * n_out * k_in
+        return {"us": round(us, 2), "bytes": byts, "gbs": round(byts / us / 1e3, 1),
+                "tflops": round(flop / us / 1e6, 2)}
+    n_qkv = (H + 2 * W.NUM_KV_HEADS) * W.HEAD_DIM
+    return {"qkv_proj": stats(qkv_us, n_qkv, hid), "o_proj": stats(o_us, hid, H * W.HEAD_DIM),
+            "block_us": round(whole_us, 2), "hidden": hid,
+            "note": "x [B,hidden] f32, bf16 weights; block = qkv_proj + decode_attn_step + o_proj"}
 
 
 def main():
@@ -207,6 +267,8 @@ def main():
     achieved = kv_bytes / (launch_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name) if (args.num_splits == 0 and not args.decode_only) else None
 
+    block = time_block(dah, torch, w, t, L, ws, stream, args) if args.block else None
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, t, seq_lens, table, args.cpu_seconds)
@@ -255,6 +317,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if block is not None:
+        line["block"] = block
     print(json.dumps(line), flush=True)
 
 

@@ -8,6 +8,8 @@ computation runs in the library's HIP kernels.
     qk_norm_rope_append  nodes attn.qk_norm + attn.rope and the cache store
     paged_decode_gqa     node attn.core (decodeGQA) over the paged cache
     decode_attn_step     both, in order, on one stream
+    qkv_proj, o_proj     nodes attn.qkv_proj and attn.o_proj around them
+    linear               the product both use (float32 x, bfloat16 weights)
 
 (Node names from the "Qwen3-0.6B" Model Spec page, "Compute-graph nodes".)
 
@@ -28,7 +30,7 @@ from ._native import DAH_BF16, DAH_F32, DahError, LIB_PATH, check, lib
 __all__ = [
     "qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step", "plan_decode",
     "workspace_bytes", "DahError", "LIB_PATH", "NUM_HEADS", "NUM_KV_HEADS", "HEAD_DIM",
-    "PAGE_SIZE", "HEAD_COUNTS",
+    "PAGE_SIZE", "HEAD_COUNTS", "linear", "qkv_proj", "o_proj",
 ]
 
 NUM_HEADS = 16
@@ -246,3 +248,68 @@ def decode_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_ta
         st = lib().decode_attn_step_ex(*head, H, *tail)
     check(st, "decode_attn_step")
     return q_out, o
+
+
+# ---------------------------------------------------------------- projections
+
+def _require_weights(w, name, shape, device):
+    torch = _torch()
+    _require(w, name, torch.bfloat16, shape, device)
+
+
+def linear(x, w, *, y=None, stream=None):
+    """y [T,N] = x [T,K] . w^T with x float32, w bfloat16 [N,K] (dah_linear)."""
+    torch = _torch()
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("linear: x must be [T,K] and w [N,K]")
+    T, K = x.shape
+    N = w.shape[0]
+    _require(x, "x", torch.float32, (T, K))
+    _require_weights(w, "w", (N, K), x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    _require(y, "y", torch.float32, (T, N), x.device)
+    check(lib().dah_linear(_ptr(x), _ptr(w), T, N, K, _ptr(y), _stream(x.device, stream)),
+          "dah_linear")
+    return y
+
+
+def qkv_proj(x, w_qkv, num_heads: int = NUM_HEADS, *, q=None, k=None, v=None, stream=None):
+    """attn.qkv_proj: x [T,hidden] float32, w_qkv [H*128 + 2048, hidden] bfloat16
+    (q_proj, k_proj, v_proj rows stacked) -> (q [T,H,128], k [T,8,128],
+    v [T,8,128]) float32, the layouts decode_attn_step takes."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("qkv_proj: x must be [T,hidden]")
+    T, hidden = x.shape
+    H = int(num_heads)
+    _require(x, "x", torch.float32, (T, hidden))
+    _require_weights(w_qkv, "w_qkv", ((H + 2 * NUM_KV_HEADS) * HEAD_DIM, hidden), x.device)
+    dev = x.device
+    q = torch.empty((T, H, HEAD_DIM), dtype=torch.float32, device=dev) if q is None else q
+    k = torch.empty((T, NUM_KV_HEADS, HEAD_DIM), dtype=torch.float32, device=dev) if k is None else k
+    v = torch.empty((T, NUM_KV_HEADS, HEAD_DIM), dtype=torch.float32, device=dev) if v is None else v
+    _require(q, "q", torch.float32, (T, H, HEAD_DIM), dev)
+    _require(k, "k", torch.float32, (T, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(v, "v", torch.float32, (T, NUM_KV_HEADS, HEAD_DIM), dev)
+    check(lib().attn_qkv_proj(_ptr(x), _ptr(w_qkv), T, hidden, H, _ptr(q), _ptr(k), _ptr(v),
+                              _stream(dev, stream)), "attn_qkv_proj")
+    return q, k, v
+
+
+def o_proj(o, w_o, *, y=None, stream=None):
+    """attn.o_proj: o [T,H,128] float32 (heads side by side), w_o [hidden, H*128]
+    bfloat16 -> y [T,hidden] float32."""
+    torch = _torch()
+    if o.dim() != 3:
+        raise ValueError("o_proj: o must be [T,H,128]")
+    T, H = o.shape[0], _heads(o)
+    hidden = w_o.shape[0]
+    _require(o, "o", torch.float32, (T, H, HEAD_DIM))
+    _require_weights(w_o, "w_o", (hidden, H * HEAD_DIM), o.device)
+    if y is None:
+        y = torch.empty((T, hidden), dtype=torch.float32, device=o.device)
+    _require(y, "y", torch.float32, (T, hidden), o.device)
+    check(lib().attn_o_proj(_ptr(o), _ptr(w_o), T, H, hidden, _ptr(y), _stream(o.device, stream)),
+          "attn_o_proj")
+    return y

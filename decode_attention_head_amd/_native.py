@@ -44,6 +44,9 @@ SIGNATURES = {
     "dah_plan_decode_ex": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.c_void_p]),
     "dah_workspace_bytes_ex": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "dah_linear": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "attn_qkv_proj": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "attn_o_proj": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "dah_status_string": (ctypes.c_char_p, [_c_int]),
     "dah_last_error": (ctypes.c_char_p, []),
 }

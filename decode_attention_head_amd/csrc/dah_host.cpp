@@ -172,6 +172,20 @@ int validate_append(const void* q, const void* k_new, const void* v_new, const v
   return DAH_OK;
 }
 
+int validate_linear(const void* x, const void* w, int T, int N, int K, const void* y) {
+  if (!x || !w || !y) return set_error(DAH_ERR_NULL, "linear: a required pointer is NULL");
+  if (T < 1) return set_error(DAH_ERR_SHAPE, "T = %d, need T >= 1", T);
+  if (N < 64 || N % 64 != 0)
+    return set_error(DAH_ERR_SHAPE, "N = %d, need a positive multiple of 64", N);
+  if (K < 256 || K % 256 != 0)
+    return set_error(DAH_ERR_SHAPE, "K = %d, need a positive multiple of 256", K);
+  if (static_cast<long long>(T) * K > (1LL << 40) || static_cast<long long>(N) * K > (1LL << 40))
+    return set_error(DAH_ERR_SHAPE, "linear: T*K or N*K too large");
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
+    return set_error(DAH_ERR_ALIGN, "linear: x, w and y need 16-byte alignment");
+  return DAH_OK;
+}
+
 int validate_decode(const void* q, const void* k_cache, const void* v_cache, int cache_dtype,
                     int64_t num_pages, const void* block_table, int max_pages_per_seq,
                     const void* seq_lens, int B, int num_heads, int max_seq_len, int num_splits,

@@ -262,6 +262,38 @@ int dah_plan_decode_ex(int B, int num_heads, int cache_dtype, int max_seq_len, i
 size_t dah_workspace_bytes_ex(int B, int num_heads, int cache_dtype, int max_seq_len,
                               int num_splits);
 
+/*
+ * The linear layers on either side of the block: attn.qkv_proj and
+ * attn.o_proj of the "Qwen3-0.6B" Model Spec page ("Compute-graph nodes",
+ * the `linear` rows: y[t,n] = sum_k x[t,k] w[n,k]), on the matrix cores.
+ * Activations are float32, weights bfloat16 (the checkpoints' dtype, nnterp
+ * qwen3 page, configuration table), outputs float32.  x enters the products
+ * as two bfloat16 terms (2^-18 relative), accumulation is float32.
+ *
+ * dah_linear -- y [T][N] = x [T][K] . w^T, w [N][K] row-major (device
+ *   pointers, 16-byte aligned).  T >= 1; N a multiple of 64; K a multiple of
+ *   256.  Returns DAH_ERR_NULL / _SHAPE / _ALIGN before any launch.
+ *
+ * attn_qkv_proj -- x [T][hidden] times w_qkv [H*128 + 2048][hidden], whose
+ *   rows are q_proj (H*128 rows), k_proj (1024) and v_proj (1024) stacked;
+ *   the outputs go to q [T][H][128], k [T][8][128], v [T][8][128] -- the
+ *   layouts decode_attn_step[_ex] takes as q, k_new, v_new.  H = num_heads
+ *   in {16, 32, 40, 64}; hidden a multiple of 256 (1024 for Qwen3-0.6B).
+ *
+ * attn_o_proj -- o [T][H][128] (heads side by side, as decode_attn_step
+ *   writes it) times w_o [hidden][H*128] -> y [T][hidden]; hidden a multiple
+ *   of 64.
+ *
+ * None of them allocates or synchronises; stream as for the other calls.
+ */
+int dah_linear(const float* x, const void* w, int T, int N, int K, float* y, void* stream);
+
+int attn_qkv_proj(const float* x, const void* w_qkv, int T, int hidden, int num_heads, float* q,
+                  float* k, float* v, void* stream);
+
+int attn_o_proj(const float* o, const void* w_o, int T, int num_heads, int hidden, float* y,
+                void* stream);
+
 /* Static name of a dah_status value ("DAH_OK", ...); "unknown status" otherwise. */
 const char* dah_status_string(int status);
 

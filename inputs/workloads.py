@@ -38,6 +38,7 @@ HEAD_DIM = 128
 PAGE_SIZE = 16
 RMS_EPS = 1e-6
 ROPE_THETA = 1e6
+HIDDEN = 1024   # Qwen3-0.6B ("At a glance"); 2560 for 4B, 5120 for 14B/32B (nnterp qwen3 page)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -53,6 +54,7 @@ class Workload:
     key_outlier: float | None = None  # multiply one cached key position by this
     num_heads: int = NUM_HEADS        # query heads (16, 32, 40 or 64) over 8 KV heads
     rope_theta: float = ROPE_THETA
+    hidden: int = HIDDEN              # model width the projections map from and to
     description: str = ""
 
     def seq_lens(self) -> np.ndarray:
@@ -248,3 +250,26 @@ def algorithmic_kv_bytes(seq_lens: np.ndarray, cache_dtype: str) -> int:
     sequence, 8 KV heads x 128 dims x (K and V) x element size."""
     elt = 4 if cache_dtype == "f32" else 2
     return int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * NUM_KV_HEADS * HEAD_DIM * 2 * elt
+
+
+def make_projections(w: Workload, layer: int, device):
+    """Inputs of the projections around the block (torch tensors on device):
+    x [B, hidden] float32 ~ N(0,1) (the block's input, one token per
+    sequence); w_qkv [(H + 16) * 128, hidden] and w_o [hidden, H * 128] in
+    bfloat16, entries N(0,1) / sqrt(fan-in) so that outputs stay O(1), as
+    the conformance check draws linear weights ("Model conformance" page,
+    "How the comparison works", step 1)."""
+    import torch
+
+    H = w.num_heads
+    n_qkv = (H + 2 * NUM_KV_HEADS) * HEAD_DIM
+
+    def randn(shape, tensor_id):
+        return torch.randn(shape, generator=_torch_generator(torch, device, w, layer, tensor_id),
+                           device=device, dtype=torch.float32)
+
+    return {
+        "x": randn((w.batch, w.hidden), 10),
+        "w_qkv": (randn((n_qkv, w.hidden), 11) / math.sqrt(w.hidden)).to(torch.bfloat16),
+        "w_o": (randn((w.hidden, H * HEAD_DIM), 12) / math.sqrt(H * HEAD_DIM)).to(torch.bfloat16),
+    }

@@ -333,3 +333,26 @@ def test_planner_kernel_choice(B, L, n, H):
         assert lib.dah_plan_decode_ex(B, 16, 1, L, n, 256, ctypes.byref(r)) == 0
         assert (q.mode, q.splits, q.workgroups, q.workspace_bytes, q.kernel) == \
             (r.mode, r.splits, r.workgroups, r.workspace_bytes, r.kernel)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, A, 4, 64, 256, A), 1), ((A, None, 4, 64, 256, A), 1), ((A, A, 4, 64, 256, None), 1),
+    ((A, A, 0, 64, 256, A), 2), ((A, A, 4, 96, 256, A), 2), ((A, A, 4, 0, 256, A), 2),
+    ((A, A, 4, 64, 128, A), 2), ((A, A, 4, 64, 300, A), 2),
+    ((A + 4, A, 4, 64, 256, A), 4), ((A, A + 2, 4, 64, 256, A), 4), ((A, A, 4, 64, 256, A + 8), 4),
+])
+def test_linear_rejects(args, status):
+    lib = _lib()
+    assert lib.dah_linear(*args, None) == status
+    assert lib.dah_last_error().decode() != ""
+
+
+def test_projection_entry_points_reject():
+    lib = _lib()
+    # heads outside the family, a NULL output, misaligned k, bad hidden
+    assert lib.attn_qkv_proj(A, A, 4, 1024, 24, A, A, A, None) == 2
+    assert lib.attn_qkv_proj(A, A, 4, 1024, 16, A, None, A, None) == 1
+    assert lib.attn_qkv_proj(A, A, 4, 1024, 16, A, A + 4, A, None) == 4
+    assert lib.attn_qkv_proj(A, A, 4, 1000, 16, A, A, A, None) == 2
+    assert lib.attn_o_proj(A, A, 4, 48, 1024, A, None) == 2
+    assert lib.attn_o_proj(A, A, 4, 16, 1000, A, None) == 2

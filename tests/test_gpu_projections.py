@@ -1,0 +1,136 @@
+"""GPU parity of the projections around the block (attn.qkv_proj and
+attn.o_proj of the "Qwen3-0.6B" Model Spec page, `linear` rows), through the
+C ABI, against the float64 oracle (oracle/projections.py).
+
+Gate, elementwise: |y_gpu - y_oracle| <= 2^-16 * sum_k |x[t,k] w[n,k]|.
+The kernels feed x to the matrix cores as two bfloat16 terms (2^-18
+relative per element) and accumulate in float32 (K <= 5120 terms in chains
+of at most a few dozen additions); 2^-16 of the absolute sum covers both with
+room, and a wrong index, a dropped k chunk or a missing x term misses it by
+orders of magnitude.  Also rel-to-max <= 1e-5 ("Model conformance" page's
+metric).
+"""
+import numpy as np
+import pytest
+
+from dah_testlib import (build_layer, cuda_available, gates, host_snapshot, read_slots,
+                         sample_batch)
+from inputs import workloads as W
+from oracle import decode_attention as O
+from oracle import projections as P
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not cuda_available(), reason="needs a GPU")]
+
+
+def _dah():
+    import decode_attention_head_amd as dah
+    return dah
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _bits(w):
+    import torch
+    return w.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _check(y_gpu, x, w_bits, label):
+    ref = P.linear(x, w_bits)
+    bound = 2.0 ** -16 * P.linear(np.abs(x), np.abs(O.bf16_bits_to_f64(w_bits)), "f64") + 1e-30
+    err = np.abs(np.asarray(y_gpu, np.float64) - ref)
+    worst = float(np.max(err / bound))
+    assert np.all(np.isfinite(y_gpu)), label
+    assert worst <= 1.0, f"{label}: error {worst:.3g} x the bound"
+    rel = O.rel_to_max_err(y_gpu, ref)
+    assert rel <= 1e-5, f"{label}: rel-to-max {rel:.3g}"
+    return worst, rel
+
+
+def _rand(shape, seed, scale=1.0, dtype=None):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device="cuda") * scale
+    return t if dtype is None else t.to(dtype)
+
+
+@pytest.mark.parametrize("N,K", [(4096, 1024), (1024, 2048), (192, 256)])
+@pytest.mark.parametrize("T", [1, 7, 16, 17, 48, 64, 65, 128, 256, 300])
+def test_linear_parity(T, N, K):
+    """Both kernels (T <= 64: split-k skinny; T > 64: tiled), ragged row
+    tails, three shapes; a guard row after the output stays untouched."""
+    import torch
+    dah = _dah()
+    x = _rand((T, K), 100 + T)
+    w = _rand((N, K), 200 + N, 1.0 / np.sqrt(K), torch.bfloat16)
+    y_all = torch.full((T + 1, N), float("nan"), device="cuda")
+    y = dah.linear(x, w, y=y_all[:T])
+    torch.cuda.synchronize()
+    assert torch.isnan(y_all[T]).all(), "wrote past the output"
+    worst, rel = _check(y.cpu().numpy(), x.cpu().numpy(), _bits(w), f"T={T} N={N} K={K}")
+    _print(f"[linear] T={T} N={N} K={K}: {worst:.3f} of bound, rel-to-max {rel:.2e}")
+
+
+@pytest.mark.parametrize("H,hidden", [(16, 1024), (32, 2560), (40, 5120), (64, 5120)])
+@pytest.mark.parametrize("T", [1, 37, 256])
+def test_qkv_and_o_proj_parity(H, hidden, T):
+    """attn.qkv_proj split into q, k, v and attn.o_proj, at the family's
+    widths (nnterp qwen3 page: hidden 1024 / 2560 / 5120)."""
+    import dataclasses
+    import torch
+    dah = _dah()
+    w = dataclasses.replace(W.WORKLOADS["b256_s2048"], batch=T, num_heads=H, hidden=hidden)
+    p = W.make_projections(w, 0, "cuda")
+    q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
+    o = _rand((T, H, 128), 300 + H)
+    y = dah.o_proj(o, p["w_o"])
+    torch.cuda.synchronize()
+    x = p["x"].cpu().numpy()
+    y_qkv = np.concatenate([q.cpu().numpy().reshape(T, -1), k.cpu().numpy().reshape(T, -1),
+                            v.cpu().numpy().reshape(T, -1)], axis=1)
+    wq, rq = _check(y_qkv, x, _bits(p["w_qkv"]), f"qkv H={H}")
+    rq_split = P.qkv_proj(x, _bits(p["w_qkv"]), H)
+    for got, ref in zip((q, k, v), rq_split):
+        assert O.rel_to_max_err(got.cpu().numpy(), ref) <= 1e-5
+    wo, ro = _check(y.cpu().numpy(), o.cpu().numpy().reshape(T, -1), _bits(p["w_o"]),
+                    f"o_proj H={H}")
+    _print(f"[proj] H={H} hidden={hidden} T={T}: qkv {wq:.3f} / o {wo:.3f} of bound")
+
+
+@pytest.mark.parametrize("name,H", [("ragged_f32_b6", 16), ("ragged_f32_b6", 64),
+                                    ("b256_s2048", 16), ("b256_s2048_h64", 64)])
+def test_attention_block_parity(name, H):
+    """x -> attn_qkv_proj -> decode_attn_step -> attn_o_proj against the
+    oracle's composed block.  The device's q, k, v carry the projection's
+    error (x as two bf16 terms: ~2.5e-6 relative, measured) into the norm and
+    the attention, so the composed gates are 1e-4 absolute on q_out and, for
+    a float32 cache, on o and y (2e-2 for bf16), with rel-to-max <= 1e-4."""
+    import dataclasses
+    import torch
+    dah = _dah()
+    w = dataclasses.replace(W.WORKLOADS[name], num_heads=H)
+    _print(f"[block] {name} H={H}")
+    t, seq_lens, table, _ = build_layer(w)
+    p = W.make_projections(w, 0, "cuda")
+    sample = sample_batch(seq_lens, 6)
+    snap = host_snapshot(t, seq_lens, table, sample)
+    q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
+    q_out, o = dah.decode_attn_step(q, k, v, t["q_gain"], t["k_gain"], t["k_pool"], t["v_pool"],
+                                    t["block_table"], t["seq_lens"], int(seq_lens.max()),
+                                    rope_theta=w.rope_theta)
+    y = dah.o_proj(o, p["w_o"])
+    torch.cuda.synchronize()
+    x = p["x"].cpu().numpy()[sample]
+    ref = P.attention_block(x, _bits(p["w_qkv"]), _bits(p["w_o"]), snap["q_gain"], snap["k_gain"],
+                            snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
+                            w.cache_dtype, num_heads=H, theta=w.rope_theta)
+    tol = 1e-4 if w.cache_dtype == "f32" else 2e-2
+    e_q = float(np.max(np.abs(q_out[sample].cpu().numpy() - ref["q_out"])))
+    assert e_q <= 1e-4, f"q_out {e_q:.3g}"
+    assert O.rel_to_max_err(q_out[sample].cpu().numpy(), ref["q_out"]) <= 1e-4
+    e_o, r_o = gates(o[sample].cpu().numpy().astype(np.float64), ref["o"], None, tol, label="o")
+    e_y, r_y = gates(y[sample].cpu().numpy().astype(np.float64), ref["y"], None, tol, label="y")
+    _print(f"  q_out {e_q:.2e}  o {e_o:.2e} (rel {r_o:.2e})  y {e_y:.2e} (rel {r_y:.2e})")
