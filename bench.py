@@ -123,24 +123,36 @@ def cpu_baseline(w, t, seq_lens, table, budget_s):
     }
 
 
-def _events_mean_us(torch, stream, fn, n):
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
-    for a, b in ev:
-        a.record(stream)
+def _graph_us(torch, fn, n):
+    """Mean time of fn over n calls captured in one HIP graph and replayed
+    (no host launch cost between the kernels, as a serving loop would run)."""
+    for _ in range(3):
         fn()
-        b.record(stream)
     torch.cuda.synchronize()
-    return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / n
 
 
 def time_block(dah, torch, w, t, L, ws, stream, args):
-    """qkv_proj and o_proj around the step, each timed alone, and the three
-    in sequence (the step then reads the projection's q, k, v)."""
+    """qkv_proj and o_proj around the step, each alone, and the three in
+    sequence (the step reads the projection's q, k, v), each captured in a
+    HIP graph and replayed."""
     p = W.make_projections(w, 0, t["q"].device)
     B, H, hid = w.batch, w.num_heads, w.hidden
     q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
     q_out, o = torch.empty_like(q), torch.empty_like(q)
+    y = torch.empty((B, hid), dtype=torch.float32, device=o.device)
 
     def qkv():
         dah.qkv_proj(p["x"], p["w_qkv"], H, q=q, k=k, v=v)
@@ -148,22 +160,19 @@ def time_block(dah, torch, w, t, L, ws, stream, args):
     def oproj():
         dah.o_proj(o, p["w_o"], y=y)
 
-    def whole():
-        qkv()
+    def step():
         dah.decode_attn_step(q, k, v, t["q_gain"], t["k_gain"], t["k_pool"], t["v_pool"],
                              t["block_table"], t["seq_lens"], L, rope_theta=w.rope_theta,
                              num_splits=args.num_splits, q_out=q_out, o=o, workspace=ws)
+
+    def whole():
+        qkv()
+        step()
         oproj()
 
-    y = torch.empty((B, hid), dtype=torch.float32, device=o.device)
-    n = max(20, min(args.steps, 100))
-    for fn in (qkv, oproj, whole):
-        for _ in range(5):
-            fn()
-    torch.cuda.synchronize()
-    qkv_us = _events_mean_us(torch, stream, qkv, n)
-    o_us = _events_mean_us(torch, stream, oproj, n)
-    whole_us = _events_mean_us(torch, stream, whole, max(10, n // 4))
+    n = 20
+    qkv_us, o_us = _graph_us(torch, qkv, n), _graph_us(torch, oproj, n)
+    step_us, whole_us = _graph_us(torch, step, n), _graph_us(torch, whole, n)
 
     def stats(us, n_out, k_in):
         byts = n_out * k_in * 2 + B * k_in * 4 + B * n_out * 4   # bf16 weights, f32 x and y
@@ -172,7 +181,8 @@ def time_block(dah, torch, w, t, L, ws, stream, args):
                 "tflops": round(flop / us / 1e6, 2)}
     n_qkv = (H + 2 * W.NUM_KV_HEADS) * W.HEAD_DIM
     return {"qkv_proj": stats(qkv_us, n_qkv, hid), "o_proj": stats(o_us, hid, H * W.HEAD_DIM),
-            "block_us": round(whole_us, 2), "hidden": hid,
+            "step_us": round(step_us, 2), "block_us": round(whole_us, 2), "hidden": hid,
+            "timing": "HIP graph replay of 20 calls, mean per call",
             "note": "x [B,hidden] f32, bf16 weights; block = qkv_proj + decode_attn_step + o_proj"}
 
 

@@ -97,23 +97,28 @@ __device__ __forceinline__ void store_block(const LinearArgs& a, const Segment& 
 constexpr int kLinWaves = 8;        // waves per workgroup, each an eighth of k
 constexpr int kLinMinGroups = 256;  // aim: one workgroup per compute unit or more
 
-// One workgroup computes a (16 kMB) x (16 kNB) output tile; wave w sums
-// k in [w K/8, (w+1) K/8) with operands loaded straight into registers
-// (up to four 32-wide k steps in flight), and the eight partial tiles are
-// added in LDS.  The weight tile is read exactly once per row tile.
-template <int kMB, int kNB>
+// One workgroup computes a (16 kMB kMW) x (16 kNB) output tile with 8 waves:
+// wave w takes row group w mod kMW (16 kMB rows) and k slice w / kMW of
+// kKS = 8 / kMW equal slices, with operands loaded straight into registers
+// (up to four 32-wide k steps in flight); the kKS partial tiles of each row
+// group are added in LDS.  The weight tile is read once per row tile (by the
+// kMW row groups together, from L1/L2 after the first).
+template <int kMB, int kNB, int kMW>
 __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(LinearArgs a) {
+  constexpr int kKS = kLinWaves / kMW;
+  static_assert(kLinWaves % kMW == 0, "row groups must divide the waves");
   __shared__ f32x4 part[kLinWaves][kMB * kNB][kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mw = wave % kMW, ks = wave / kMW;
   const int r = lane >> 4, c = lane & 15;
   const int n_tiles = a.N / (16 * kNB);
   const int n_tile = blockIdx.x % n_tiles;
   const int m_tile = blockIdx.x / n_tiles;
-  const int m0 = m_tile * 16 * kMB, n0 = n_tile * 16 * kNB;
-  const int kw = a.K / kLinWaves;
-  const int k_begin = wave * kw;
+  const int m0 = m_tile * 16 * kMB * kMW + 16 * kMB * mw, n0 = n_tile * 16 * kNB;
+  const int kw = a.K / kKS;
+  const int k_begin = ks * kw;
   const int steps = kw / 32;
 
   // Lane (r, c): row c of each 16-row block of x and of each 16-column block
@@ -158,18 +163,16 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
       u32x4 hi, lo;
       split8(st.x[mb][0], st.x[mb][1], hi, lo);
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        acc[mb][nb] = mfma(hi, st.w[nb], acc[mb][nb]);
-        acc[mb][nb] = mfma(lo, st.w[nb], acc[mb][nb]);
-      }
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = mfma(hi, st.w[nb], acc[mb][nb]);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = mfma(lo, st.w[nb], acc[mb][nb]);
     }
   };
 
-  // steps = K / 256 is a power of two for the model widths, and a multiple
-  // of 4 from K = 1024 on: four k steps in flight per wave, each buffer
-  // refilled as soon as it is consumed.  Shorter slices load everything first.
+  // A multiple of 4 steps: four in flight per wave, each buffer refilled as
+  // soon as it is consumed.  Otherwise two at a time.
   Step b0, b1, b2, b3;
-  if (steps >= 4 && (steps & 3) == 0) {
+  if ((steps & 3) == 0) {
     load(b0, 0);
     load(b1, 1);
     load(b2, 2);
@@ -207,41 +210,72 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) part[wave][mb * kNB + nb][lane] = acc[mb][nb];
   __syncthreads();
+  // (row group g, block blk) pairs spread over the waves; slice q of row
+  // group g is wave g + kMW q.
   const Segment sg = segment_of(a, n0);
-  for (int blk = wave; blk < kMB * kNB; blk += kLinWaves) {
-    f32x4 t = part[0][blk][lane];
+  const int m_base = m_tile * 16 * kMB * kMW;
+  for (int job = wave; job < kMW * kMB * kNB; job += kLinWaves) {
+    const int g = job / (kMB * kNB), blk = job % (kMB * kNB);
+    f32x4 t = part[g][blk][lane];
 #pragma unroll
-    for (int q = 1; q < kLinWaves; ++q) t += part[q][blk][lane];
-    store_block(a, sg, m0 + 16 * (blk / kNB), n0 + 16 * (blk % kNB), t, lane);
+    for (int q = 1; q < kKS; ++q) t += part[g + kMW * q][blk][lane];
+    store_block(a, sg, m_base + 16 * kMB * g + 16 * (blk / kNB), n0 + 16 * (blk % kNB), t, lane);
   }
 }
 
-template <int kMB>
-void launch_splitk(const LinearArgs& a, int nb, hipStream_t stream) {
-  const int m_tiles = (a.T + 16 * kMB - 1) / (16 * kMB);
-  const dim3 block(kWave * kLinWaves);
-  if (nb == 4)
-    linear_splitk_kernel<kMB, 4><<<dim3(m_tiles * (a.N / 64)), block, 0, stream>>>(a);
-  else if (nb == 2)
-    linear_splitk_kernel<kMB, 2><<<dim3(m_tiles * (a.N / 32)), block, 0, stream>>>(a);
-  else
-    linear_splitk_kernel<kMB, 1><<<dim3(m_tiles * (a.N / 16)), block, 0, stream>>>(a);
+struct LinearConfig {
+  int mb, nb, mw;
+};
+
+// Tile shape: the widest of 64, 32, 16 columns (32 rows per tile) that
+// still gives kLinMinGroups workgroups, else 16 x 16 tiles.  Swept on MI355X
+// over 12 shapes (rows per wave 1-2, columns 1-4 blocks, 1-4 row groups) at
+// T = 2 .. 256 and N x K = 4096 x 1024, 1024 x 2048 (graph-replayed launch
+// times): this rule picks the fastest shape or one within 3% of it in every
+// case.  What the time follows is the traffic from L2: x is read once per
+// column tile and w once per row tile, at ~6 TB/s.
+LinearConfig pick_config(int T, int N) {
+#ifdef DAH_LINEAR_CONFIG
+  (void)T; (void)N;
+  return LinearConfig{DAH_LINEAR_CONFIG};
+#else
+  if (T > 16) {
+    const int m_tiles = (T + 31) / 32;
+    for (int nb = 4; nb >= 1; nb /= 2)
+      if (m_tiles * (N / (16 * nb)) >= kLinMinGroups) return {2, nb, 1};
+  }
+  return {1, 1, 1};
+#endif
 }
 
-// Tile shape: 16 rows for a single row block, else 32; the widest of 64, 32,
-// 16 columns that still gives kLinMinGroups workgroups.
+template <int kMB, int kNB, int kMW>
+void launch_cfg(const LinearArgs& a, hipStream_t stream) {
+  const int rows = 16 * kMB * kMW;
+  const dim3 grid(((a.T + rows - 1) / rows) * (a.N / (16 * kNB)));
+  linear_splitk_kernel<kMB, kNB, kMW><<<grid, kWave * kLinWaves, 0, stream>>>(a);
+}
+
 int launch_linear(LinearArgs& a, hipStream_t stream) {
-  const int mb = a.T <= 16 ? 1 : 2;
-  const int m_tiles = (a.T + 16 * mb - 1) / (16 * mb);
-  int nb = 1;
-  if (m_tiles * (a.N / 64) >= kLinMinGroups)
-    nb = 4;
-  else if (m_tiles * (a.N / 32) >= kLinMinGroups)
-    nb = 2;
-  if (mb == 1)
-    launch_splitk<1>(a, nb, stream);
-  else
-    launch_splitk<2>(a, nb, stream);
+  const LinearConfig c = pick_config(a.T, a.N);
+  // The instantiated shapes; N is a multiple of 64, so every column tiling divides it.
+#define DAH_LIN_CASE(MB, NB, MW) \
+  if (c.mb == MB && c.nb == NB && c.mw == MW) launch_cfg<MB, NB, MW>(a, stream); else
+  DAH_LIN_CASE(1, 1, 1)
+  DAH_LIN_CASE(2, 1, 1)
+  DAH_LIN_CASE(2, 2, 1)
+  DAH_LIN_CASE(2, 4, 1)
+#ifdef DAH_LINEAR_CONFIG
+  DAH_LIN_CASE(1, 1, 2)
+  DAH_LIN_CASE(1, 2, 2)
+  DAH_LIN_CASE(1, 4, 2)
+  DAH_LIN_CASE(2, 1, 2)
+  DAH_LIN_CASE(2, 2, 2)
+  DAH_LIN_CASE(2, 4, 2)
+  DAH_LIN_CASE(2, 2, 4)
+  DAH_LIN_CASE(1, 4, 4)
+#endif
+  return dah::set_error(DAH_ERR_HIP, "linear: no kernel for tile %d/%d/%d", c.mb, c.nb, c.mw);
+#undef DAH_LIN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return dah::set_error(DAH_ERR_HIP, "linear kernel launch failed: %s", hipGetErrorString(e));

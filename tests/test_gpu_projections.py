@@ -134,3 +134,57 @@ def test_attention_block_parity(name, H):
     e_o, r_o = gates(o[sample].cpu().numpy().astype(np.float64), ref["o"], None, tol, label="o")
     e_y, r_y = gates(y[sample].cpu().numpy().astype(np.float64), ref["y"], None, tol, label="y")
     _print(f"  q_out {e_q:.2e}  o {e_o:.2e} (rel {r_o:.2e})  y {e_y:.2e} (rel {r_y:.2e})")
+
+
+@pytest.mark.parametrize("name", ["b256_s2048", "ragged_b32"])
+def test_block_under_graph_replay(name):
+    """The whole block (qkv_proj, decode_attn_step, o_proj) captured in one
+    HIP graph: every replay, with eager work and synchronisations between
+    replays, equals the eager result bit for bit (the library records no
+    memset, allocation or host synchronisation).  The cache is restored
+    before each run, since the step appends to it."""
+    import torch
+    dah = _dah()
+    w = W.WORKLOADS[name]
+    t, seq_lens, table, _ = build_layer(w)
+    p = W.make_projections(w, 0, "cuda")
+    L = int(seq_lens.max())
+    H = w.num_heads
+    ws = torch.empty(max(dah.workspace_bytes(w.batch, L), 256), dtype=torch.uint8, device="cuda")
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
+    q_out, o = torch.empty_like(q), torch.empty_like(q)
+    y = torch.empty((w.batch, w.hidden), device="cuda")
+
+    def block():
+        dah.qkv_proj(p["x"], p["w_qkv"], H, q=q, k=k, v=v)
+        dah.decode_attn_step(q, k, v, t["q_gain"], t["k_gain"], t["k_pool"], t["v_pool"],
+                             t["block_table"], t["seq_lens"], L, q_out=q_out, o=o, workspace=ws)
+        dah.o_proj(o, p["w_o"], y=y)
+
+    def restore():
+        t["k_pool"].copy_(k0)
+        t["v_pool"].copy_(v0)
+
+    block()
+    torch.cuda.synchronize()
+    want_y, want_o, want_k = y.clone(), o.clone(), t["k_pool"].clone()
+    restore()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            block()
+    torch.cuda.synchronize()
+    for i in range(3):
+        restore()
+        y.zero_()
+        o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want_y), f"replay {i}: y differs"
+        assert torch.equal(o, want_o), f"replay {i}: o differs"
+        assert torch.equal(t["k_pool"], want_k), f"replay {i}: cache differs"
+        _ = (p["x"] * 2).sum().item()   # eager work between replays
