@@ -12,6 +12,8 @@ What it computes, in the order of the model spec's compute graph (the
   2. ``rope``      rotation of the pairs (i, i+64) by pos * theta^(-2i/128)
   3. ``append``    the new token's roped k and raw v stored in the paged cache
   4. ``decode_gqa`` o[b,h] = sum_{s<seq_lens[b]} softmax_s(<q[b,h],k[b,s,h/2]>/sqrt(128)) v[b,s,h/2]
+  5. ``chunk_step`` the same four steps for a chunk of n new tokens per
+     sequence, each attending causally to the positions up to its own
 
 Every step is the plain definition evaluated in float64 with NumPy: no
 blocking, no online softmax, no fusion.  Inputs are taken exactly as the
@@ -323,3 +325,58 @@ def rel_to_max_err(impl: np.ndarray, ref: np.ndarray) -> float:
     ref = np.asarray(ref, dtype=np.float64)
     denom = float(np.max(np.abs(ref))) if ref.size else 0.0
     return max_abs_err(impl, ref) / denom if denom > 0 else max_abs_err(impl, ref)
+
+
+# ---------------------------------------------------------------------------
+# Chunks of several new tokens per sequence (chunked prefill, verification of
+# drafted tokens): the same nodes over positions pos0 .. pos0 + n - 1, each
+# token attending causally (the Model Spec page's shape domain allows
+# T in [1, 40,960] new tokens; causality is the theorem forward_causal of the
+# "Supported models" page).
+# ---------------------------------------------------------------------------
+
+def chunk_step(q, k_new, v_new, q_gain, k_gain, k_pool, v_pool, block_table, seq_lens,
+               cu_tokens, cache_dtype: str, eps: float = RMS_EPS, theta: float = ROPE_THETA,
+               batch_indices=None):
+    """Sequence b owns tokens cu_tokens[b] .. cu_tokens[b+1]-1 (n_b of them);
+    seq_lens[b] counts the cache after the chunk, so token i of the chunk
+    sits at position seq_lens[b] - n_b + i and attends to positions 0 .. that
+    position: the cached ones from the pools, the chunk's own from its
+    appended (normed, roped, stored) keys and values.
+
+    q [N,H,128], k_new/v_new [N,8,128] (N = cu_tokens[B]).  Returns a dict
+    of float64 arrays over the tokens of the selected sequences, in order:
+    q_out [n,H,128], k_slot / v_slot [n,8,128] (what the cache holds after
+    the append), o [n,H,128], and pos [n]."""
+    q = np.asarray(q)
+    cu = np.asarray(cu_tokens, dtype=np.int64)
+    idx = range(len(cu) - 1) if batch_indices is None else list(batch_indices)
+    res = {"q_out": [], "k_slot": [], "v_slot": [], "o": [], "pos": []}
+    for b in idx:
+        t0, t1 = int(cu[b]), int(cu[b + 1])
+        n = t1 - t0
+        L = int(seq_lens[b])
+        if n < 1:
+            continue
+        if L < n:
+            raise ValueError("seq_lens[b] must count the chunk's tokens")
+        pos = np.arange(L - n, L, dtype=np.float64)
+        q_out = rope(qk_norm(q[t0:t1], q_gain, eps), pos, theta)
+        k_rot = rope(qk_norm(np.asarray(k_new)[t0:t1], k_gain, eps), pos, theta)
+        k_slot = store_as_cache_dtype(k_rot, cache_dtype)
+        v_slot = store_as_cache_dtype(np.asarray(v_new, dtype=np.float64)[t0:t1], cache_dtype)
+        old = L - n
+        k_old = gather_sequence(k_pool, block_table[b], old, cache_dtype) if old else \
+            np.empty((0, NUM_KV_HEADS, HEAD_DIM))
+        v_old = gather_sequence(v_pool, block_table[b], old, cache_dtype) if old else \
+            np.empty((0, NUM_KV_HEADS, HEAD_DIM))
+        k_all = np.concatenate([k_old, k_slot], axis=0)
+        v_all = np.concatenate([v_old, v_slot], axis=0)
+        for i in range(n):
+            p = old + i
+            res["o"].append(decode_gqa_dense(q_out[i], k_all[:p + 1], v_all[:p + 1]))
+        res["q_out"].extend(q_out)
+        res["k_slot"].extend(k_slot)
+        res["v_slot"].extend(v_slot)
+        res["pos"].extend(pos.astype(np.int64))
+    return {key: np.stack(val) if val else np.zeros((0,)) for key, val in res.items()}
