@@ -8,6 +8,7 @@ computation runs in the library's HIP kernels.
     qk_norm_rope_append  nodes attn.qk_norm + attn.rope and the cache store
     paged_decode_gqa     node attn.core (decodeGQA) over the paged cache
     decode_attn_step     both, in order, on one stream
+    chunk_attn_step      the same for several new tokens per sequence (causal)
     qkv_proj, o_proj     nodes attn.qkv_proj and attn.o_proj around them
     linear               the product both use (float32 x, bfloat16 weights)
 
@@ -30,7 +31,7 @@ from ._native import DAH_BF16, DAH_F32, DahError, LIB_PATH, check, lib
 __all__ = [
     "qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step", "plan_decode",
     "workspace_bytes", "DahError", "LIB_PATH", "NUM_HEADS", "NUM_KV_HEADS", "HEAD_DIM",
-    "PAGE_SIZE", "HEAD_COUNTS", "linear", "qkv_proj", "o_proj",
+    "PAGE_SIZE", "HEAD_COUNTS", "linear", "qkv_proj", "o_proj", "chunk_attn_step",
 ]
 
 NUM_HEADS = 16
@@ -313,3 +314,37 @@ def o_proj(o, w_o, *, y=None, stream=None):
     check(lib().attn_o_proj(_ptr(o), _ptr(w_o), T, H, hidden, _ptr(y), _stream(o.device, stream)),
           "attn_o_proj")
     return y
+
+
+# ---------------------------------------------------------------- chunks
+
+def chunk_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_table, seq_lens,
+                    cu_tokens, max_chunk: int, max_seq_len: int, *, eps: float = 1e-6,
+                    rope_theta: float = 1e6, q_out=None, o=None, stream=None):
+    """Several new tokens per sequence (chunk_attn_step): token i of sequence
+    b's chunk (rows cu_tokens[b] .. cu_tokens[b+1]-1) sits at position
+    seq_lens[b] - n_b + i; norm, RoPE, append, then causal decodeGQA.
+    q [N,H,128], k_new/v_new [N,8,128] float32, cu_tokens int32 [B+1];
+    bfloat16 cache.  Returns (q_out, o), both [N,H,128] float32."""
+    torch = _torch()
+    N, H = q.shape[0], _heads(q)
+    B = seq_lens.shape[0]
+    dev = q.device
+    _require(q, "q", torch.float32, (N, H, HEAD_DIM))
+    _require(k_new, "k_new", torch.float32, (N, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(v_new, "v_new", torch.float32, (N, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(q_gain, "q_gain", torch.float32, (HEAD_DIM,), dev)
+    _require(k_gain, "k_gain", torch.float32, (HEAD_DIM,), dev)
+    _require(cu_tokens, "cu_tokens", torch.int32, (B + 1,), dev)
+    dt = _check_cache(k_cache, v_cache, block_table, seq_lens, B, dev)
+    q_out = torch.empty_like(q) if q_out is None else q_out
+    o = torch.empty_like(q) if o is None else o
+    _require(q_out, "q_out", torch.float32, (N, H, HEAD_DIM), dev)
+    _require(o, "o", torch.float32, (N, H, HEAD_DIM), dev)
+    st = lib().chunk_attn_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
+        _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), _ptr(cu_tokens), B, N, int(max_chunk),
+        int(max_seq_len), H, _ptr(q_out), _ptr(o), _stream(dev, stream))
+    check(st, "chunk_attn_step")
+    return q_out, o

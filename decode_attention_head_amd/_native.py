@@ -44,6 +44,9 @@ SIGNATURES = {
     "dah_plan_decode_ex": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.c_void_p]),
     "dah_workspace_bytes_ex": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "chunk_attn_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_float, _c_float, _vp, _vp, _c_int,
+                                 _c_i64, _vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _vp, _vp, _vp]),
     "dah_linear": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "attn_qkv_proj": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "attn_o_proj": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),

@@ -172,6 +172,35 @@ int validate_append(const void* q, const void* k_new, const void* v_new, const v
   return DAH_OK;
 }
 
+int validate_chunk(const void* q, const void* k_new, const void* v_new, const void* q_gain,
+                   const void* k_gain, float eps, float rope_theta, const void* k_cache,
+                   const void* v_cache, int cache_dtype, int64_t num_pages,
+                   const void* block_table, int max_pages_per_seq, const void* seq_lens,
+                   const void* cu_tokens, int B, int total_tokens, int max_chunk, int max_seq_len,
+                   int num_heads, const void* q_out, const void* o) {
+  int st = validate_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
+                           cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
+                           num_heads, q_out);
+  if (st != DAH_OK) return st;
+  if (!cu_tokens || !o) return set_error(DAH_ERR_NULL, "chunk_attn_step: cu_tokens or o is NULL");
+  if (cache_dtype != DAH_BF16)
+    return set_error(DAH_ERR_DTYPE, "chunk_attn_step: needs a bfloat16 cache (the matrix-core "
+                                    "kernel)");
+  if (total_tokens < 1) return set_error(DAH_ERR_SHAPE, "total_tokens = %d, need >= 1", total_tokens);
+  if (max_chunk < 1 || max_chunk > total_tokens)
+    return set_error(DAH_ERR_SHAPE, "max_chunk = %d, need 1 <= max_chunk <= total_tokens (%d)",
+                     max_chunk, total_tokens);
+  if (static_cast<long long>(B) * max_chunk > INT32_MAX)
+    return set_error(DAH_ERR_SHAPE, "B * max_chunk too large");
+  if (max_seq_len < 1 ||
+      static_cast<long long>(max_seq_len) > static_cast<long long>(max_pages_per_seq) * kPage)
+    return set_error(DAH_ERR_SHAPE, "max_seq_len = %d, need 1 .. max_pages_per_seq * 16",
+                     max_seq_len);
+  if (!aligned(cu_tokens, 4) || !aligned(o, 16))
+    return set_error(DAH_ERR_ALIGN, "cu_tokens needs 4-byte, o 16-byte alignment");
+  return DAH_OK;
+}
+
 int validate_linear(const void* x, const void* w, int T, int N, int K, const void* y) {
   if (!x || !w || !y) return set_error(DAH_ERR_NULL, "linear: a required pointer is NULL");
   if (T < 1) return set_error(DAH_ERR_SHAPE, "T = %d, need T >= 1", T);

@@ -47,6 +47,15 @@ int validate_append(const void* q, const void* k_new, const void* v_new, const v
                     const void* block_table, int max_pages_per_seq, const void* seq_lens, int B,
                     int num_heads, const void* q_out);
 
+// chunk_attn_step: the append checks, plus cu_tokens, the token count, the
+// chunk bound, max_seq_len and a bfloat16 cache.
+int validate_chunk(const void* q, const void* k_new, const void* v_new, const void* q_gain,
+                   const void* k_gain, float eps, float rope_theta, const void* k_cache,
+                   const void* v_cache, int cache_dtype, int64_t num_pages,
+                   const void* block_table, int max_pages_per_seq, const void* seq_lens,
+                   const void* cu_tokens, int B, int total_tokens, int max_chunk, int max_seq_len,
+                   int num_heads, const void* q_out, const void* o);
+
 // dah_linear: T >= 1, N a multiple of 64, K a multiple of 256, 16-byte alignment.
 int validate_linear(const void* x, const void* w, int T, int N, int K, const void* y);
 

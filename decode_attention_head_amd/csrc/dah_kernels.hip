@@ -733,10 +733,13 @@ struct MfmaState {
 
 // One page: scores -> weights -> weighted V sum.  kMasked: positions
 // >= nvalid are excluded (their V is cleared: 0 * NaN would poison a row).
-template <bool kMasked>
+// kCausal (chunks of several new tokens): column c also sees only the page
+// positions below climit, its own limit (per lane); those positions hold
+// valid keys and values, so only the scores are masked.
+template <bool kMasked, bool kCausal = false>
 __device__ __forceinline__ void attend_page_mfma(const KTileMfma& K, Tile<DAH_BF16>& V,
                                                  const u32x4 (&qb)[4][3], MfmaState& st,
-                                                 int lane, int nvalid) {
+                                                 int lane, int nvalid, int climit = kPage) {
   const int r = lane >> 4;
   f32x4 s = page_scores(K, qb);
   if (kMasked) {
@@ -746,6 +749,10 @@ __device__ __forceinline__ void attend_page_mfma(const KTileMfma& K, Tile<DAH_BF
       s[v] = ok ? s[v] : -INFINITY;
       if (!ok) V.clear(v);
     }
+  }
+  if (kCausal) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s[v] = 4 * v + r < climit ? s[v] : -INFINITY;
   }
   const float pm = max_over_rows(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
   // Move the reference only when a score passes it by more than kMaxLag
@@ -1388,18 +1395,17 @@ __device__ __forceinline__ void rotate(float& x0, float& x1, float c, float s) {
   x1 = y1;
 }
 
-// One block of 8 waves per sequence.  Wave w handles query heads w, w+8, ...
-// (kG of them), key head w and value head w; lane i holds dims i and i+64 (a
-// RoPE pair).
+// One block of 8 waves per token row.  Wave w handles query heads w, w+8,
+// ... (kG of them), key head w and value head w; lane i holds dims i and
+// i+64 (a RoPE pair).  `row` indexes q, k_new, v_new and q_out; the cache
+// slot is position pos of block-table row b, written only when `append`.
 template <int kDtype, int kG>
-__global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
+__device__ __forceinline__ void norm_rope_append_row(const AppendArgs& a, size_t row, int b,
+                                                     int pos, bool append) {
   constexpr int kH = kG * kKvHeads;
   __shared__ float2 cs[64];
-  const int b = blockIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & (kWave - 1);
-  const int seq_len = a.seq_lens[b];
-  const int pos = seq_len >= 1 ? seq_len - 1 : 0;
   if (w == 0) {
     // cos/sin of pos * theta^(-2i/128), angle formed in float64 (at pos near
     // 40,960 a float32 angle would be off by ~4e-3 rad); see dah_rope.h.
@@ -1411,11 +1417,11 @@ __global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
   float qa[kG], qb[kG];
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
-    const size_t qbase = ((size_t)b * kH + w + kKvHeads * i) * kHeadDim;
+    const size_t qbase = (row * kH + w + kKvHeads * i) * kHeadDim;
     qa[i] = a.q[qbase + lane];
     qb[i] = a.q[qbase + lane + 64];
   }
-  const size_t kvbase = ((size_t)b * kKvHeads + w) * kHeadDim;
+  const size_t kvbase = (row * kKvHeads + w) * kHeadDim;
   float ka = a.k_new[kvbase + lane], kb = a.k_new[kvbase + lane + 64];
   const float va = a.v_new[kvbase + lane], vb = a.v_new[kvbase + lane + 64];
   __syncthreads();
@@ -1429,12 +1435,12 @@ __global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
   rotate(ka, kb, r.x, r.y);
 #pragma unroll
   for (int i = 0; i < kG; ++i) {
-    const size_t qbase = ((size_t)b * kH + w + kKvHeads * i) * kHeadDim;
+    const size_t qbase = (row * kH + w + kKvHeads * i) * kHeadDim;
     a.q_out[qbase + lane] = qa[i];
     a.q_out[qbase + lane + 64] = qb[i];
   }
 
-  if (seq_len < 1 || seq_len > a.max_len) return;
+  if (!append) return;
   const int page = a.block_table[(size_t)b * a.max_pages_per_seq + pos / kPage];
   if (page < 0 || page >= a.num_pages) return;
   const size_t elem = (((size_t)page * kKvHeads + w) * kPage + (pos % kPage)) * kHeadDim;
@@ -1452,6 +1458,201 @@ __global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
     kc[lane + 64] = kb;
     vc[lane] = va;
     vc[lane + 64] = vb;
+  }
+}
+
+// One workgroup per sequence: its new token at pos = seq_len - 1.
+template <int kDtype, int kG>
+__global__ __launch_bounds__(512) void norm_rope_append_kernel(AppendArgs a) {
+  const int b = blockIdx.x;
+  const int seq_len = a.seq_lens[b];
+  norm_rope_append_row<kDtype, kG>(a, b, b, seq_len >= 1 ? seq_len - 1 : 0,
+                                   seq_len >= 1 && seq_len <= a.max_len);
+}
+
+// Chunks: workgroup (b, i) handles token i of sequence b's chunk (rows
+// cu_tokens[b] .. cu_tokens[b+1]-1, n_b of them), at position
+// seq_len - n_b + i.  Sequences whose length cannot hold their chunk, or
+// exceeds max_len, get q_out at position 0 and no append.
+template <int kDtype, int kG>
+__global__ __launch_bounds__(512) void norm_rope_append_chunk_kernel(AppendArgs a,
+                                                                     const int32_t* cu_tokens,
+                                                                     int max_chunk, int total) {
+  const int b = blockIdx.x / max_chunk;
+  const int i = blockIdx.x - b * max_chunk;
+  const int t0 = min(max(cu_tokens[b], 0), total);
+  const int t1 = min(max(cu_tokens[b + 1], t0), total);
+  const int n = t1 - t0;
+  if (i >= n) return;
+  const int seq_len = a.seq_lens[b];
+  const bool ok = n <= max_chunk && seq_len >= n && seq_len <= a.max_len;
+  norm_rope_append_row<kDtype, kG>(a, (size_t)t0 + i, b, ok ? seq_len - n + i : 0, ok);
+}
+
+// ------------------------------------------------------------ chunk attention
+//
+// Causal attention of a chunk of new tokens over the paged cache (their keys
+// and values already appended), on the matrix cores: the 16 score columns of
+// a wave are (token, query head) pairs -- 16 / G tokens of one KV head -- so
+// each K/V page is read once for all of them.  Column c sees positions up to
+// its token's own; pages wholly below the tile's first token need no mask.
+
+struct ChunkArgs {
+  const float* q;  // normed and roped, [tokens][H][128]
+  const char* k_cache;
+  const char* v_cache;
+  int num_pages;
+  const int32_t* block_table;
+  int max_pages_per_seq;
+  const int32_t* seq_lens;
+  const int32_t* cu_tokens;
+  int total;       // tokens
+  int max_chunk;   // host bound on n_b
+  int tiles;       // tiles per sequence: ceil(max_chunk / (16 / G))
+  int max_seq_len;
+  float* o;        // [tokens][H][128]
+};
+
+template <int kG>
+__global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void chunk_attn_kernel(ChunkArgs a) {
+  constexpr int kH = kG * kKvHeads;
+  constexpr int kTpt = 16 / kG;  // tokens per tile
+  using TileV = Tile<DAH_BF16>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head
+  const int row = lane >> 4, col = lane & 15;
+  const int b = blockIdx.x / a.tiles;
+  const int tile = blockIdx.x - b * a.tiles;
+  const int t0 = min(max(a.cu_tokens[b], 0), a.total);
+  const int t1 = min(max(a.cu_tokens[b + 1], t0), a.total);
+  const int n = t1 - t0;
+  const int i0 = tile * kTpt;
+  if (i0 >= n) return;
+  const int ntok = min(kTpt, n - i0);
+  const int seq_len = a.seq_lens[b];
+  if (n > a.max_chunk || seq_len < n || seq_len > a.max_seq_len) {
+    // Outside the preconditions: NaN for this tile's tokens (and, from tile
+    // 0, for tokens past max_chunk tiles), nothing read from the cache.
+    const int last = tile == 0 ? n : i0 + ntok;
+    for (int i = i0; i < last; ++i) {
+      if (tile == 0 && i >= ntok && i < a.tiles * kTpt) continue;  // owned by another tile
+      for (int h = 0; h < kG; ++h)
+        reinterpret_cast<float2*>(a.o + (((size_t)t0 + i) * kH + g * kG + h) * kHeadDim)[lane] =
+            make_float2(NAN, NAN);
+    }
+    return;
+  }
+
+  const int pos0 = seq_len - n + i0;    // position of the tile's first token
+  const int pmax = pos0 + ntok - 1;
+  const int ti = col / kG, hh = col - ti * kG;
+  const bool live = ti < ntok;
+  const int climit_pos = pos0 + (live ? ti : ntok - 1);  // last position column col sees
+  const size_t qrow = ((size_t)t0 + i0 + (live ? ti : 0)) * kH + g * kG + (live ? hh : 0);
+
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+  const ConstI32 bt = (ConstI32)(a.block_table + (size_t)b * a.max_pages_per_seq);
+  const int64_t page_bytes = (int64_t)kKvHeads * TileV::kTileBytes;
+  const int64_t head_bytes = (int64_t)g * TileV::kTileBytes;
+  const char* kbase = a.k_cache + head_bytes;
+  const char* vbase = a.v_cache + head_bytes;
+  const int last = pmax / kPage;              // last page the tile reads
+  const int first_masked = (pos0 + 1) / kPage;  // pages below are seen whole by every column
+  bool bad_page = false;
+  auto offset_of = [&](int id) -> int64_t {
+    const bool ok = id >= 0 && id < a.num_pages;
+    bad_page |= !ok;
+    return (int64_t)(ok ? id : 0) * page_bytes;
+  };
+
+  float qv[4][8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) load8(a.q + qrow * kHeadDim + 32 * kk + 8 * row, qv[kk]);
+
+  KTileMfma K0, K1;
+  TileV V0, V1;
+  int id1 = bt[min(1, last)];
+  int id2 = bt[min(2, last)];
+  {
+    const int64_t off0 = offset_of(bt[0]);
+    K0.load(kbase + off0, lane);
+    V0.load(vbase + off0, lane);
+  }
+  const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  u32x4 qb[4][3];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[kk][e] *= qscale;
+    split3(qv[kk], qb[kk]);
+  }
+  if (!live) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) qb[kk][t] = u32x4{0u, 0u, 0u, 0u};
+  }
+  MfmaState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Page p: positions 16p .. 16p+15; the tile needs none past pmax (their
+  // slots may hold anything) and column col none past climit_pos.
+  auto attend = [&](const KTileMfma& K, TileV& V, int p) {
+    if (p < first_masked) {
+      attend_page_mfma<false>(K, V, qb, st, lane, kPage);
+    } else {
+      attend_page_mfma<true, true>(K, V, qb, st, lane, pmax - kPage * p + 1,
+                                   climit_pos - kPage * p + 1);
+    }
+  };
+  int p = 0;
+  for (; p + 2 <= last; p += 2) {
+    const int64_t off1 = offset_of(id1);
+    K1.load(kbase + off1, lane);
+    V1.load(vbase + off1, lane);
+    const int id3 = bt[min(p + 3, last)];
+    __builtin_amdgcn_sched_barrier(0);
+    attend(K0, V0, p);
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t off2 = offset_of(id2);
+    K0.load(kbase + off2, lane);
+    V0.load(vbase + off2, lane);
+    const int id4 = bt[min(p + 4, last)];
+    __builtin_amdgcn_sched_barrier(0);
+    attend(K1, V1, p + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    id1 = id3;
+    id2 = id4;
+  }
+  if (p + 1 <= last) {
+    const int64_t off1 = offset_of(id1);
+    K1.load(kbase + off1, lane);
+    V1.load(vbase + off1, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    attend(K0, V0, p);
+    __builtin_amdgcn_sched_barrier(0);
+    attend(K1, V1, p + 1);
+  } else {
+    attend(K0, V0, p);
+  }
+
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int j = 4 * row + v;   // accumulator row: column j = (token j / G, head j % G)
+    const float lj = __shfl(l, j);
+    const int tj = j / kG, hj = j - tj * kG;
+    if (tj >= ntok) continue;
+    float o8[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) o8[nb] = st.acc[nb][v];
+    store8(a.o + (((size_t)t0 + i0 + tj) * kH + g * kG + hj) * kHeadDim + 8 * col, o8,
+           bad_page ? NAN : 1.0f / lj);
   }
 }
 
@@ -1527,6 +1728,60 @@ int launch_append(const float* q, const float* k_new, const float* v_new, const 
       norm_rope_append_kernel<DAH_F32, kG><<<B, 512, 0, stream>>>(a);
   });
   return check_launch("norm_rope_append_kernel");
+}
+
+// The chunk step: every chunk token normed, rotated and appended, then the
+// causal attention of the chunks (two launches).
+int launch_chunk(const float* q, const float* k_new, const float* v_new, const float* q_gain,
+                 const float* k_gain, float eps, float rope_theta, void* k_cache, void* v_cache,
+                 int64_t num_pages, const int32_t* block_table, int max_pages_per_seq,
+                 const int32_t* seq_lens, const int32_t* cu_tokens, int B, int total,
+                 int max_chunk, int max_seq_len, int num_heads, float* q_out, float* o,
+                 hipStream_t stream) {
+  AppendArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.q_gain = q_gain;
+  a.k_gain = k_gain;
+  a.eps = eps;
+  a.rope = dah::rope_powers((double)rope_theta);
+  a.k_cache = static_cast<char*>(k_cache);
+  a.v_cache = static_cast<char*>(v_cache);
+  a.num_pages = static_cast<int>(num_pages);
+  a.block_table = block_table;
+  a.max_pages_per_seq = max_pages_per_seq;
+  a.seq_lens = seq_lens;
+  a.max_len = max_seq_len;
+  a.q_out = q_out;
+  ChunkArgs c;
+  c.q = q_out;
+  c.k_cache = static_cast<const char*>(k_cache);
+  c.v_cache = static_cast<const char*>(v_cache);
+  c.num_pages = static_cast<int>(num_pages);
+  c.block_table = block_table;
+  c.max_pages_per_seq = max_pages_per_seq;
+  c.seq_lens = seq_lens;
+  c.cu_tokens = cu_tokens;
+  c.total = total;
+  c.max_chunk = max_chunk;
+  c.max_seq_len = max_seq_len;
+  c.o = o;
+  int st = DAH_OK;
+  with_group(num_heads, [&](auto grp) {
+    constexpr int kG = decltype(grp)::value;
+    constexpr int kTpt = 16 / kG;
+    norm_rope_append_chunk_kernel<DAH_BF16, kG>
+        <<<dim3((unsigned)((long long)B * max_chunk)), 512, 0, stream>>>(a, cu_tokens, max_chunk,
+                                                                         total);
+    st = check_launch("norm_rope_append_chunk_kernel");
+    if (st != DAH_OK) return;
+    c.tiles = (max_chunk + kTpt - 1) / kTpt;
+    chunk_attn_kernel<kG><<<dim3((unsigned)((long long)B * c.tiles)),
+                            kWave * kDecodeWavesPerBlock, 0, stream>>>(c);
+    st = check_launch("chunk_attn_kernel");
+  });
+  return st;
 }
 
 // The extra inputs of the fused decode step.
@@ -1753,6 +2008,23 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
                              cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
                              kHeads, max_seq_len, num_splits, q_out, o, workspace,
                              workspace_bytes, stream);
+}
+
+int chunk_attn_step(const float* q, const float* k_new, const float* v_new, const float* q_gain,
+                    const float* k_gain, float eps, float rope_theta, void* k_cache,
+                    void* v_cache, int cache_dtype, int64_t num_pages,
+                    const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
+                    const int32_t* cu_tokens, int B, int total_tokens, int max_chunk,
+                    int max_seq_len, int num_heads, float* q_out, float* o, void* stream) {
+  int st = dah::validate_chunk(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
+                               cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens,
+                               cu_tokens, B, total_tokens, max_chunk, max_seq_len, num_heads,
+                               q_out, o);
+  if (st != DAH_OK) return st;
+  return launch_chunk(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
+                      num_pages, block_table, max_pages_per_seq, seq_lens, cu_tokens, B,
+                      total_tokens, max_chunk, max_seq_len, num_heads, q_out, o,
+                      static_cast<hipStream_t>(stream));
 }
 
 size_t dah_workspace_bytes_ex(int B, int num_heads, int cache_dtype, int max_seq_len,

@@ -263,6 +263,39 @@ size_t dah_workspace_bytes_ex(int B, int num_heads, int cache_dtype, int max_seq
                               int num_splits);
 
 /*
+ * chunk_attn_step -- several new tokens per sequence (chunked prefill, or
+ * verification of drafted tokens): for every sequence b with chunk tokens
+ * t = cu_tokens[b] .. cu_tokens[b+1]-1 (n_b = cu_tokens[b+1] - cu_tokens[b],
+ * 0 allowed), token i of the chunk sits at position seq_lens[b] - n_b + i
+ * (seq_lens counts the cache after the chunk).  Each token is normed and
+ * rotated at its position and its key and value appended as in
+ * qk_norm_rope_append; then every token attends (decodeGQA over positions
+ * 0 .. its own) causally -- the Model Spec page's shape domain allows
+ * T in [1, 40,960] new tokens, and forward_causal ("Supported models" page)
+ * states that later tokens cannot change earlier outputs.
+ *
+ *   q, q_out     [device] float32 [total_tokens][H][128]; q_out may equal q
+ *   k_new, v_new [device] float32 [total_tokens][8][128]
+ *   o            [device] float32 [total_tokens][H][128]
+ *   cu_tokens    [device] int32 [B+1], non-decreasing, cu_tokens[B] = total_tokens
+ *   max_chunk    host bound on every n_b (1 .. total_tokens); the grids are sized by it
+ *   max_seq_len  host bound on every seq_lens[b] (<= max_pages_per_seq * 16)
+ *   num_heads    16, 32, 40 or 64; the cache must be DAH_BF16 (matrix-core kernel)
+ *   other arguments as in decode_attn_step.
+ *
+ * Two launches (append, attention), no workspace.  A sequence with
+ * seq_lens[b] < n_b, seq_lens[b] > max_seq_len or n_b > max_chunk gets NaN
+ * outputs and no append; a page id outside the pool gives NaN for the tokens
+ * that read it.
+ */
+int chunk_attn_step(const float* q, const float* k_new, const float* v_new, const float* q_gain,
+                    const float* k_gain, float eps, float rope_theta, void* k_cache,
+                    void* v_cache, int cache_dtype, int64_t num_pages,
+                    const int32_t* block_table, int max_pages_per_seq, const int32_t* seq_lens,
+                    const int32_t* cu_tokens, int B, int total_tokens, int max_chunk,
+                    int max_seq_len, int num_heads, float* q_out, float* o, void* stream);
+
+/*
  * The linear layers on either side of the block: attn.qkv_proj and
  * attn.o_proj of the "Qwen3-0.6B" Model Spec page ("Compute-graph nodes",
  * the `linear` rows: y[t,n] = sum_k x[t,k] w[n,k]), on the matrix cores.

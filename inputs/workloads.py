@@ -273,3 +273,50 @@ def make_projections(w: Workload, layer: int, device):
         "w_qkv": (randn((n_qkv, w.hidden), 11) / math.sqrt(w.hidden)).to(torch.bfloat16),
         "w_o": (randn((w.hidden, H * HEAD_DIM), 12) / math.sqrt(H * HEAD_DIM)).to(torch.bfloat16),
     }
+
+
+def make_chunk_inputs(lens_old, chunks, num_heads: int, cache_dtype: str, seed: int, device,
+                      pool_pages: int | None = None):
+    """Inputs of a chunk step: sequence b holds lens_old[b] cached positions
+    and receives chunks[b] new tokens (seq_lens = lens_old + chunks).
+    Values N(0,1), gains 1 + N(0, 0.1); pages of every sequence drawn from a
+    seeded permutation of the pool; unused pool pages hold N(0,1) too.
+    Returns torch tensors on `device` and the host block table."""
+    import torch
+
+    lens_old = np.asarray(lens_old, np.int64)
+    chunks = np.asarray(chunks, np.int64)
+    B = len(lens_old)
+    seq_lens = (lens_old + chunks).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    N = int(cu[-1])
+    need = np.array([pages_for(n) for n in seq_lens], np.int64)
+    total = int(need.sum())
+    num_pages = max(total, 1) if pool_pages is None else int(pool_pages)
+    rng = np.random.Generator(np.random.PCG64([seed, 2]))
+    perm = rng.permutation(num_pages)[:total].astype(np.int32)
+    table = np.zeros((B, max(1, int(need.max()))), np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[at:at + n]
+        at += n
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 7919 + 17)
+    cdt = torch.float32 if cache_dtype == "f32" else torch.bfloat16
+
+    def randn(shape, dtype=torch.float32):
+        return torch.randn(shape, generator=g, device=device, dtype=dtype)
+
+    t = {
+        "q": randn((N, num_heads, HEAD_DIM)),
+        "k_new": randn((N, NUM_KV_HEADS, HEAD_DIM)),
+        "v_new": randn((N, NUM_KV_HEADS, HEAD_DIM)),
+        "q_gain": 1.0 + 0.1 * randn((HEAD_DIM,)),
+        "k_gain": 1.0 + 0.1 * randn((HEAD_DIM,)),
+        "k_pool": randn((num_pages, NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM), cdt),
+        "v_pool": randn((num_pages, NUM_KV_HEADS, PAGE_SIZE, HEAD_DIM), cdt),
+        "block_table": torch.from_numpy(table).to(device),
+        "seq_lens": torch.from_numpy(seq_lens).to(device),
+        "cu_tokens": torch.from_numpy(cu).to(device),
+    }
+    return t, table, seq_lens, cu

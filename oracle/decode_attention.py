@@ -337,7 +337,7 @@ def rel_to_max_err(impl: np.ndarray, ref: np.ndarray) -> float:
 
 def chunk_step(q, k_new, v_new, q_gain, k_gain, k_pool, v_pool, block_table, seq_lens,
                cu_tokens, cache_dtype: str, eps: float = RMS_EPS, theta: float = ROPE_THETA,
-               batch_indices=None):
+               batch_indices=None, k_stored=None):
     """Sequence b owns tokens cu_tokens[b] .. cu_tokens[b+1]-1 (n_b of them);
     seq_lens[b] counts the cache after the chunk, so token i of the chunk
     sits at position seq_lens[b] - n_b + i and attends to positions 0 .. that
@@ -347,11 +347,17 @@ def chunk_step(q, k_new, v_new, q_gain, k_gain, k_pool, v_pool, block_table, seq
     q [N,H,128], k_new/v_new [N,8,128] (N = cu_tokens[B]).  Returns a dict
     of float64 arrays over the tokens of the selected sequences, in order:
     q_out [n,H,128], k_slot / v_slot [n,8,128] (what the cache holds after
-    the append), o [n,H,128], and pos [n]."""
+    the append), o [n,H,128], and pos [n].
+
+    k_stored, if given ([n,8,128] over the same tokens), replaces the stored
+    keys of the chunk: a caller that knows a key value lies within rounding
+    error of a bf16 midpoint can evaluate the step with the other admissible
+    rounding."""
     q = np.asarray(q)
     cu = np.asarray(cu_tokens, dtype=np.int64)
     idx = range(len(cu) - 1) if batch_indices is None else list(batch_indices)
     res = {"q_out": [], "k_slot": [], "v_slot": [], "o": [], "pos": []}
+    done = 0
     for b in idx:
         t0, t1 = int(cu[b]), int(cu[b + 1])
         n = t1 - t0
@@ -364,6 +370,9 @@ def chunk_step(q, k_new, v_new, q_gain, k_gain, k_pool, v_pool, block_table, seq
         q_out = rope(qk_norm(q[t0:t1], q_gain, eps), pos, theta)
         k_rot = rope(qk_norm(np.asarray(k_new)[t0:t1], k_gain, eps), pos, theta)
         k_slot = store_as_cache_dtype(k_rot, cache_dtype)
+        if k_stored is not None:
+            k_slot = np.asarray(k_stored, dtype=np.float64)[done:done + n]
+        done += n
         v_slot = store_as_cache_dtype(np.asarray(v_new, dtype=np.float64)[t0:t1], cache_dtype)
         old = L - n
         k_old = gather_sequence(k_pool, block_table[b], old, cache_dtype) if old else \

@@ -1,0 +1,228 @@
+"""GPU parity of the chunk step (several new tokens per sequence, causal
+within the chunk: chunked prefill and verification of drafted tokens),
+through the C ABI, against the oracle's chunk_step.
+
+The kernel reads a bfloat16 cache on the matrix cores (q as three bf16
+terms, weights as two), so the gates are the bf16 ones: max abs error 2e-2,
+relative-to-max <= 1e-4, and q_out within 1e-5.  The appended keys must be
+the round-to-nearest-even of the exact value (or its neighbour within float32
+error of a midpoint) and the values exact.
+
+Where an exact key element lies within float32 error of a bf16 midpoint,
+both roundings are correct, and for a token that attends to only a few
+positions the choice moves o by ~1e-4.  The oracle is therefore also
+evaluated with every such element rounded the other way (found from the
+exact values alone), and a token's gate is 1e-4 x max|o| plus the spread
+between the two oracle results.
+"""
+import numpy as np
+import pytest
+
+from dah_testlib import bf16_alternative, check_rounded, cuda_available, pool_to_numpy
+from inputs import workloads as W
+from oracle import decode_attention as O
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not cuda_available(), reason="needs a GPU")]
+
+
+def _dah():
+    import decode_attention_head_amd as dah
+    return dah
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _snapshot(t, table, seq_lens, cu, seqs):
+    """Host copies of the pages and tokens of the selected sequences, with a
+    compact pool and remapped block table (taken before the step runs)."""
+    import torch
+    pages, rows, toks = [], [], []
+    at = 0
+    for b in seqs:
+        n = W.pages_for(int(seq_lens[b]))
+        pages.append(table[b, :n])
+        rows.append(np.arange(at, at + n))
+        at += n
+        toks.append(np.arange(cu[b], cu[b + 1]))
+    idx = torch.from_numpy(np.concatenate(pages).astype(np.int64)).to(t["k_pool"].device)
+    mini = np.zeros((len(seqs), max(len(r) for r in rows)), np.int32)
+    for i, r in enumerate(rows):
+        mini[i, :len(r)] = r
+    tok = np.concatenate(toks).astype(np.int64)
+    sel = torch.from_numpy(tok).to(t["q"].device)
+    counts = [int(cu[b + 1] - cu[b]) for b in seqs]
+    return {
+        "k_pool": pool_to_numpy(t["k_pool"].index_select(0, idx)),
+        "v_pool": pool_to_numpy(t["v_pool"].index_select(0, idx)),
+        "block_table": mini, "seq_lens": np.asarray(seq_lens)[list(seqs)].astype(np.int64),
+        "cu": np.concatenate([[0], np.cumsum(counts)]).astype(np.int64),
+        "q": t["q"].index_select(0, sel).cpu().numpy(),
+        "k_new": t["k_new"].index_select(0, sel).cpu().numpy(),
+        "v_new": t["v_new"].index_select(0, sel).cpu().numpy(),
+        "q_gain": t["q_gain"].cpu().numpy(), "k_gain": t["k_gain"].cpu().numpy(),
+        "tokens": tok,
+    }
+
+
+def _oracle(s, theta=1e6, k_stored=None):
+    return O.chunk_step(s["q"], s["k_new"], s["v_new"], s["q_gain"], s["k_gain"], s["k_pool"],
+                        s["v_pool"], s["block_table"], s["seq_lens"], s["cu"], "bf16", theta=theta,
+                        k_stored=k_stored)
+
+
+def _check_o(o_gpu, s, ref, theta, label):
+    """The gates on o with the admissible-rounding spread (module docstring)."""
+    _, k_exact = O.norm_rope(s["q"], s["k_new"], s["q_gain"], s["k_gain"],
+                             np.asarray(ref["pos"]) + 1, theta=theta)
+    _, k_alt, flagged = bf16_alternative(k_exact)
+    spread = np.zeros(len(ref["o"]))
+    if flagged.any():
+        alt = _oracle(s, theta, k_stored=k_alt)
+        spread = np.max(np.abs(alt["o"] - ref["o"]), axis=(1, 2))
+    o_gpu = np.asarray(o_gpu, np.float64)
+    scale = float(np.max(np.abs(ref["o"])))
+    err = np.max(np.abs(o_gpu - ref["o"]), axis=(1, 2))
+    assert np.all(np.isfinite(o_gpu)), label
+    bad = err > 1e-4 * scale + spread
+    assert not bad.any(), (f"{label}: tokens {np.nonzero(bad)[0][:8]} exceed 1e-4 x max|o| + "
+                           f"spread; worst {float(np.max(err - spread)) / scale:.3g} rel")
+    assert float(np.max(err)) <= 2e-2, label
+    return float(np.max(err)), float(np.max(err) / scale), int(flagged.sum())
+
+
+def _slots(t, table, seq_lens, cu, seqs):
+    """(k, v) the cache holds at every chunk position of the selected sequences."""
+    import torch
+    ks, vs = [], []
+    for b in seqs:
+        n = int(cu[b + 1] - cu[b])
+        for i in range(n):
+            pos = int(seq_lens[b]) - n + i
+            page, slot = int(table[b, pos // 16]), pos % 16
+            ks.append(t["k_pool"][page, :, slot].to(torch.float64).cpu().numpy())
+            vs.append(t["v_pool"][page, :, slot].to(torch.float64).cpu().numpy())
+    return np.stack(ks), np.stack(vs)
+
+
+def _run(t, cu, seq_lens, max_chunk, theta=1e6):
+    import torch
+    dah = _dah()
+    q_out, o = dah.chunk_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                   t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                   t["cu_tokens"], max_chunk, int(np.max(seq_lens)),
+                                   rope_theta=theta)
+    torch.cuda.synchronize()
+    return q_out, o
+
+
+@pytest.mark.parametrize("H", [16, 32, 40, 64])
+@pytest.mark.parametrize("theta", [1e6, 5e6])
+def test_small_chunks_every_token(H, theta):
+    """Chunks of 1, 4, 7, 16, 19 and 33 tokens after 0, 3, 16, 30, 100 and
+    9 cached positions (tiles of 16/G tokens with ragged tails, chunks that
+    start mid-page, cross pages and start at position 0)."""
+    lens_old, chunks = [0, 3, 16, 30, 100, 9], [1, 4, 7, 16, 19, 33]
+    t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, chunks, H, "bf16", 11 + H, "cuda",
+                                                 pool_pages=64)
+    seqs = list(range(len(chunks)))
+    snap = _snapshot(t, table, seq_lens, cu, seqs)
+    q_out, o = _run(t, cu, seq_lens, max(chunks), theta)
+    ref = _oracle(snap, theta)
+    e_q = float(np.max(np.abs(q_out.cpu().numpy() - ref["q_out"])))
+    assert e_q <= 1e-5, f"q_out {e_q:.3g}"
+    k_slot, v_slot = _slots(t, table, seq_lens, cu, seqs)
+    _, k_exact = O.norm_rope(snap["q"], snap["k_new"], snap["q_gain"], snap["k_gain"],
+                             np.array(ref["pos"]) + 1, theta=theta)
+    check_rounded(k_slot, k_exact)
+    assert np.array_equal(v_slot, ref["v_slot"])
+    e_abs, e_rel, nflag = _check_o(o.cpu().numpy(), snap, ref, theta, f"H={H}")
+    _print(f"[chunk] H={H} theta={theta:g}: q_out {e_q:.2e}  o {e_abs:.2e} rel {e_rel:.2e} "
+           f"({nflag} near-midpoint keys)")
+
+
+@pytest.mark.parametrize("name,lens_old,chunk,B,H", [
+    ("verify", 2044, 4, 64, 16), ("verify", 2044, 4, 64, 64),
+    ("prefill", 0, 1024, 4, 16), ("prefill_after_context", 3000, 512, 4, 40)])
+def test_large_chunks_sampled(name, lens_old, chunk, B, H):
+    """Verification of 4 drafted tokens over 2,044 cached positions at B=64,
+    and chunked prefill of 512-1,024 tokens, sampled sequences."""
+    rng = np.random.default_rng(B + chunk)
+    olds = [lens_old + int(x) for x in rng.integers(0, 8, B)] if lens_old else [0] * B
+    t, table, seq_lens, cu = W.make_chunk_inputs(olds, [chunk] * B, H, "bf16", 100 + H, "cuda")
+    seqs = sorted(set([0, B - 1] + [int(x) for x in rng.permutation(B)[:2]]))
+    snap = _snapshot(t, table, seq_lens, cu, seqs)
+    q_out, o = _run(t, cu, seq_lens, chunk)
+    ref = _oracle(snap)
+    tok = snap["tokens"]
+    e_q = float(np.max(np.abs(q_out.cpu().numpy()[tok] - ref["q_out"])))
+    assert e_q <= 1e-5
+    e_abs, e_rel, nflag = _check_o(o.cpu().numpy()[tok], snap, ref, 1e6, name)
+    _print(f"[chunk {name}] B={B} H={H}: o {e_abs:.2e} rel {e_rel:.2e} ({nflag} near-midpoint keys)")
+
+
+def test_one_token_chunks_match_the_decode_step():
+    """A chunk of one token per sequence is the decode step: the same o up
+    to the two kernels' rounding (the decode here runs on the same matrix-
+    core form; both are gated against the oracle elsewhere)."""
+    import torch
+    dah = _dah()
+    lens_old = [5, 16, 200, 1000]
+    t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, [1] * 4, 16, "bf16", 5, "cuda",
+                                                 pool_pages=128)
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    q_c, o_c = _run(t, cu, seq_lens, 1)
+    kc, vc = t["k_pool"].clone(), t["v_pool"].clone()
+    t["k_pool"].copy_(k0)
+    t["v_pool"].copy_(v0)
+    q_d, o_d = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    int(seq_lens.max()), num_splits=1)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(q_c, q_d, rtol=0, atol=1e-6)
+    torch.testing.assert_close(o_c, o_d, rtol=0, atol=2.0 ** -16 * float(o_d.abs().max()))
+    assert torch.equal(vc, t["v_pool"])
+
+
+def test_later_tokens_leave_earlier_outputs_bit_identical():
+    """forward_causal: changing the last token of a chunk changes no earlier
+    token's output, bit for bit (the kernel's masking, not just rounding)."""
+    import torch
+    lens_old, chunks = [40, 0], [13, 9]
+    t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, chunks, 32, "bf16", 9, "cuda",
+                                                 pool_pages=32)
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    _, o1 = _run(t, cu, seq_lens, 13)
+    o1 = o1.clone()
+    t["k_pool"].copy_(k0)
+    t["v_pool"].copy_(v0)
+    for last in (12, 21):
+        t["q"][last] += 3.0
+        t["k_new"][last] *= -2.0
+        t["v_new"][last] += 5.0
+    _, o2 = _run(t, cu, seq_lens, 13)
+    assert torch.equal(o2[:12], o1[:12]) and torch.equal(o2[13:21], o1[13:21])
+    assert not torch.equal(o2[12], o1[12]) and not torch.equal(o2[21], o1[21])
+
+
+def test_out_of_domain_sequences():
+    """seq_len < n_b or > max_seq_len: NaN outputs, nothing appended; an
+    empty chunk: nothing; other sequences unaffected."""
+    import torch
+    lens_old, chunks = [20, 20, 20, 20], [3, 3, 0, 3]
+    t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, chunks, 16, "bf16", 13, "cuda",
+                                                 pool_pages=16)
+    t["seq_lens"][1] = 2           # cannot hold its 3-token chunk
+    t["seq_lens"][3] = 60          # past max_seq_len = 23 below
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    dah = _dah()
+    q_out, o = dah.chunk_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                   t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                   t["cu_tokens"], 3, 23)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o[0:3]).all()
+    assert torch.isnan(o[3:6]).all() and torch.isnan(o[6:9]).all()
+    changed = (t["k_pool"] != k0).any(dim=3) | (t["v_pool"] != v0).any(dim=3)
+    assert int(changed.sum()) == 3 * 8       # sequence 0's three slots, 8 heads each
