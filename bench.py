@@ -15,6 +15,10 @@ The JSON line reports
                   events on the launch stream, against MI355X's 8 TB/s HBM peak
   cpu_baseline    the float64 CPU oracle on a bounded sample of the same workload
 
+--chunk N also times chunk_attn_step with N new tokens per sequence (the
+workload's lengths counting them), under "chunk": HIP-graph-replayed time,
+K/V bytes (each cached position once per sequence) and attention flops.
+
 --block also times the projections on either side of the block (attn.qkv_proj
 before the step, attn.o_proj after it) on the same batch and reports them under
 "block": per-launch durations (HIP events), their bytes and flops, and the
@@ -59,6 +63,8 @@ def parse():
                     help="time paged_decode_gqa alone (profiling aid)")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the streaming-read probe (practical bandwidth ceiling)")
+    ap.add_argument("--chunk", type=int, default=0, metavar="N",
+                    help="also time chunk_attn_step with N new tokens per sequence")
     ap.add_argument("--block", action="store_true",
                     help="also time qkv_proj and o_proj around the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -186,6 +192,36 @@ def time_block(dah, torch, w, t, L, ws, stream, args):
             "note": "x [B,hidden] f32, bf16 weights; block = qkv_proj + decode_attn_step + o_proj"}
 
 
+def time_chunk(dah, torch, w, seq_lens, num_pages, n):
+    """chunk_attn_step with n new tokens per sequence of the workload (its
+    seq_lens count them), bf16 cache, graph-replayed."""
+    lens = np.asarray(seq_lens, np.int64)
+    if np.any(lens < n):
+        return {"skipped": f"sequences shorter than {n} tokens"}
+    B, H = w.batch, w.num_heads
+    t, table, sl, cu = W.make_chunk_inputs(lens - n, [n] * B, H, "bf16", 777, "cuda",
+                                           pool_pages=max(num_pages, int(sum(
+                                               W.pages_for(int(x)) for x in lens))))
+    L = int(sl.max())
+    q_out, o = torch.empty_like(t["q"]), torch.empty_like(t["q"])
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+
+    def run():
+        dah.chunk_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"], t["k_pool"],
+                            t["v_pool"], t["block_table"], t["seq_lens"], t["cu_tokens"], n, L,
+                            q_out=q_out, o=o)
+    us = _graph_us(torch, run, 10)
+    t["k_pool"].copy_(k0)
+    t["v_pool"].copy_(v0)
+    kv_bytes = int(lens.sum()) * W.NUM_KV_HEADS * W.HEAD_DIM * 2 * 2
+    attended = sum(int(L0) * n - n * (n - 1) // 2 for L0 in lens)   # sum over tokens of (pos + 1)
+    flop = 4.0 * W.HEAD_DIM * H * attended
+    return {"tokens_per_seq": n, "us": round(us, 2), "kv_bytes": kv_bytes,
+            "kv_gbs": round(kv_bytes / us / 1e3, 1), "tflops": round(flop / us / 1e6, 2),
+            "tokens_per_s": round(B * n / (us * 1e-6), 1),
+            "timing": "HIP graph replay of 10 calls (append + attention launches), mean per call"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -278,6 +314,7 @@ def main():
     traffic = read_traffic(w.name) if (args.num_splits == 0 and not args.decode_only) else None
 
     block = time_block(dah, torch, w, t, L, ws, stream, args) if args.block else None
+    chunk = time_chunk(dah, torch, w, seq_lens, num_pages, args.chunk) if args.chunk > 0 else None
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -329,6 +366,8 @@ def main():
     }
     if block is not None:
         line["block"] = block
+    if chunk is not None:
+        line["chunk"] = chunk
     print(json.dumps(line), flush=True)
 
 
