@@ -9,6 +9,7 @@ computation runs in the library's HIP kernels.
     paged_decode_gqa     node attn.core (decodeGQA) over the paged cache
     decode_attn_step     both, in order, on one stream
     chunk_attn_step      the same for several new tokens per sequence (causal)
+    decoder_layer_step   a whole layer around the block (norms, residuals, SwiGLU MLP)
     qkv_proj, o_proj     nodes attn.qkv_proj and attn.o_proj around them
     linear               the product both use (float32 x, bfloat16 weights)
 
@@ -31,7 +32,8 @@ from ._native import DAH_BF16, DAH_F32, DahError, LIB_PATH, check, lib
 __all__ = [
     "qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step", "plan_decode",
     "workspace_bytes", "DahError", "LIB_PATH", "NUM_HEADS", "NUM_KV_HEADS", "HEAD_DIM",
-    "PAGE_SIZE", "HEAD_COUNTS", "linear", "qkv_proj", "o_proj", "chunk_attn_step",
+    "PAGE_SIZE", "HEAD_COUNTS", "linear", "qkv_proj", "o_proj", "chunk_attn_step", "rmsnorm",
+    "silu_mul", "decoder_layer_step", "layer_workspace_bytes", "LAYER_WEIGHTS",
 ]
 
 NUM_HEADS = 16
@@ -348,3 +350,80 @@ def chunk_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_tab
         int(max_seq_len), H, _ptr(q_out), _ptr(o), _stream(dev, stream))
     check(st, "chunk_attn_step")
     return q_out, o
+
+
+# ---------------------------------------------------------------- decoder layer
+
+def rmsnorm(x, w, *, eps: float = 1e-6, y=None, stream=None):
+    """Rows of a hidden-size RMSNorm (dah_rmsnorm): x [T,H] float32, w [H]."""
+    torch = _torch()
+    T, width = x.shape
+    _require(x, "x", torch.float32, (T, width))
+    _require(w, "w", torch.float32, (width,), x.device)
+    y = torch.empty_like(x) if y is None else y
+    _require(y, "y", torch.float32, (T, width), x.device)
+    check(lib().dah_rmsnorm(_ptr(x), _ptr(w), eps, T, width, _ptr(y), _stream(x.device, stream)),
+          "dah_rmsnorm")
+    return y
+
+
+def silu_mul(gate_up, *, act=None, stream=None):
+    """mlp.act (dah_silu_mul): gate_up [T, 2I] float32 -> [T, I]."""
+    torch = _torch()
+    T, two_i = gate_up.shape
+    _require(gate_up, "gate_up", torch.float32, (T, two_i))
+    act = torch.empty((T, two_i // 2), dtype=torch.float32, device=gate_up.device) \
+        if act is None else act
+    _require(act, "act", torch.float32, (T, two_i // 2), gate_up.device)
+    check(lib().dah_silu_mul(_ptr(gate_up), T, two_i // 2, _ptr(act),
+                             _stream(gate_up.device, stream)), "dah_silu_mul")
+    return act
+
+
+LAYER_WEIGHTS = ("w_in", "w_qkv", "q_gain", "k_gain", "w_o", "w_post", "w_gate_up", "w_down")
+
+
+def layer_workspace_bytes(B: int, hidden: int, inter: int, max_seq_len: int, num_splits: int = 0,
+                          num_heads: int = NUM_HEADS, cache_dtype="bf16") -> int:
+    return int(lib().dah_layer_workspace_bytes(B, hidden, inter, num_heads,
+                                               _dtype_code(cache_dtype), max_seq_len, num_splits))
+
+
+def decoder_layer_step(x, weights: dict, k_cache, v_cache, block_table, seq_lens,
+                       max_seq_len: int, *, eps: float = 1e-6, rope_theta: float = 1e6,
+                       num_splits: int = 0, y=None, workspace=None, stream=None):
+    """One decoder layer's decode step (decoder_layer_step): x [B, hidden]
+    float32 (one new token per sequence) -> y [B, hidden].  weights holds
+    the tensors named in LAYER_WEIGHTS (bf16 matrices, float32 gains)."""
+    import ctypes as _ct
+    from ._native import LayerWeights
+    torch = _torch()
+    B, hidden = x.shape
+    dev = x.device
+    _require(x, "x", torch.float32, (B, hidden))
+    w_o, w_down = weights["w_o"], weights["w_down"]
+    H = w_o.shape[1] // HEAD_DIM
+    inter = w_down.shape[1]
+    if H not in HEAD_COUNTS:
+        raise ValueError(f"w_o must be [hidden, H*128] with H in {HEAD_COUNTS}")
+    shapes = {"w_in": (hidden,), "w_qkv": ((H + 2 * NUM_KV_HEADS) * HEAD_DIM, hidden),
+              "q_gain": (HEAD_DIM,), "k_gain": (HEAD_DIM,), "w_o": (hidden, H * HEAD_DIM),
+              "w_post": (hidden,), "w_gate_up": (2 * inter, hidden), "w_down": (hidden, inter)}
+    for name in LAYER_WEIGHTS:
+        dtype = torch.float32 if shapes[name] == (hidden,) or name in ("q_gain", "k_gain") \
+            else torch.bfloat16
+        _require(weights[name], name, dtype, shapes[name], dev)
+    dt = _check_cache(k_cache, v_cache, block_table, seq_lens, B, dev)
+    y = torch.empty_like(x) if y is None else y
+    _require(y, "y", torch.float32, (B, hidden), dev)
+    need = layer_workspace_bytes(B, hidden, inter, max_seq_len, num_splits, H, k_cache.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    lw = LayerWeights(*[_ptr(weights[n]) for n in LAYER_WEIGHTS])
+    st = lib().decoder_layer_step(
+        _ptr(x), _ct.byref(lw), hidden, inter, H, eps, rope_theta, _ptr(k_cache), _ptr(v_cache),
+        dt, k_cache.shape[0], _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B,
+        int(max_seq_len), int(num_splits), _ptr(y), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    check(st, "decoder_layer_step")
+    return y

@@ -50,6 +50,14 @@ SIGNATURES = {
     "dah_linear": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "attn_qkv_proj": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp]),
     "attn_o_proj": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "dah_linear_residual": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "dah_rmsnorm": (_c_int, [_vp, _vp, _c_float, _c_int, _c_int, _vp, _vp]),
+    "dah_silu_mul": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),
+    "dah_layer_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int]),
+    "decoder_layer_step": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_float, _c_float, _vp,
+                                    _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int, _c_int, _c_int,
+                                    _vp, _vp, _c_size, _vp]),
     "dah_status_string": (ctypes.c_char_p, [_c_int]),
     "dah_last_error": (ctypes.c_char_p, []),
 }
@@ -71,6 +79,12 @@ class DecodePlan(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("splits", ctypes.c_int),
                 ("pages_per_split", ctypes.c_int), ("workgroups", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t), ("kernel", ctypes.c_int)]
+
+
+class LayerWeights(ctypes.Structure):
+    """dah_layer_weights of include/dah.h."""
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("w_in", "w_qkv", "q_gain", "k_gain", "w_o", "w_post", "w_gate_up", "w_down")]
 
 
 class DahError(RuntimeError):

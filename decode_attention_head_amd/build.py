@@ -21,7 +21,7 @@ PROBE_LIB_PATH = os.path.join(PKG_DIR, "libdah_probe.so")
 
 # (output, sources): the attention library and the benchmark's memory probes
 TARGETS = [
-    (LIB_PATH, ["dah_kernels.hip", "dah_linear.hip", "dah_host.cpp"]),
+    (LIB_PATH, ["dah_kernels.hip", "dah_linear.hip", "dah_layer.hip", "dah_host.cpp"]),
     (PROBE_LIB_PATH, ["dah_probe.hip"]),
 ]
 

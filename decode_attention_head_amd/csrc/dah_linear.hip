@@ -57,11 +57,13 @@ __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Output columns [begin, begin + width) go to y[t * width + (n - begin)].
+// Output columns [begin, begin + width) go to y[t * width + (n - begin)],
+// plus res at the same place when res is set (res may be y).
 struct Segment {
   float* y;
   int begin;
   int width;
+  const float* res;
 };
 
 struct LinearArgs {
@@ -85,10 +87,14 @@ __device__ __forceinline__ void store_block(const LinearArgs& a, const Segment& 
                                             const f32x4& acc, int lane) {
   const int r = lane >> 4, c = lane & 15;
   float* col = s.y + (n - s.begin) + c;
+  const float* rcol = s.res != nullptr ? s.res + (n - s.begin) + c : nullptr;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int t = m + 4 * r + v;
-    if (t < a.T) col[(size_t)t * s.width] = acc[v];
+    if (t < a.T) {
+      const size_t at = (size_t)t * s.width;
+      col[at] = rcol != nullptr ? acc[v] + rcol[at] : acc[v];
+    }
   }
 }
 
@@ -296,7 +302,25 @@ int dah_linear(const float* x, const void* w, int T, int N, int K, float* y, voi
   a.N = N;
   a.K = K;
   a.nseg = 1;
-  a.seg[0] = Segment{y, 0, N};
+  a.seg[0] = Segment{y, 0, N, nullptr};
+  return launch_linear(a, static_cast<hipStream_t>(stream));
+}
+
+int dah_linear_residual(const float* x, const void* w, const float* residual, int T, int N,
+                        int K, float* y, void* stream) {
+  if (!residual) return dah::set_error(DAH_ERR_NULL, "dah_linear_residual: residual is NULL");
+  if (reinterpret_cast<uintptr_t>(residual) % 16 != 0)
+    return dah::set_error(DAH_ERR_ALIGN, "dah_linear_residual: residual needs 16-byte alignment");
+  int st = dah::validate_linear(x, w, T, N, K, y);
+  if (st != DAH_OK) return st;
+  LinearArgs a = {};
+  a.x = x;
+  a.w = static_cast<const uint16_t*>(w);
+  a.T = T;
+  a.N = N;
+  a.K = K;
+  a.nseg = 1;
+  a.seg[0] = Segment{y, 0, N, residual};
   return launch_linear(a, static_cast<hipStream_t>(stream));
 }
 
@@ -317,9 +341,9 @@ int attn_qkv_proj(const float* x, const void* w_qkv, int T, int hidden, int num_
   a.N = nq + 2 * nkv;
   a.K = hidden;
   a.nseg = 3;
-  a.seg[0] = Segment{q, 0, nq};
-  a.seg[1] = Segment{k, nq, nkv};
-  a.seg[2] = Segment{v, nq + nkv, nkv};
+  a.seg[0] = Segment{q, 0, nq, nullptr};
+  a.seg[1] = Segment{k, nq, nkv, nullptr};
+  a.seg[2] = Segment{v, nq + nkv, nkv, nullptr};
   return launch_linear(a, static_cast<hipStream_t>(stream));
 }
 

@@ -327,6 +327,72 @@ int attn_qkv_proj(const float* x, const void* w_qkv, int T, int hidden, int num_
 int attn_o_proj(const float* o, const void* w_o, int T, int num_heads, int hidden, float* y,
                 void* stream);
 
+/*
+ * dah_linear_residual -- y = x . w^T + residual (shapes as dah_linear;
+ *   residual [T][N] float32, 16-byte aligned, may equal y): the residual
+ *   adds of the decoder layer (attn_residual, mlp_residual) folded into the
+ *   product's store.
+ */
+int dah_linear_residual(const float* x, const void* w, const float* residual, int T, int N,
+                        int K, float* y, void* stream);
+
+/*
+ * dah_rmsnorm -- rows of a hidden-size RMSNorm (the input_norm,
+ *   post_attn_norm and final_norm rows of the Model Spec page:
+ *   y = x / sqrt(sum x^2 / H + eps) * w, H = width): x, y [T][width]
+ *   float32 (may be the same), w [width] float32; width a multiple of 4;
+ *   16-byte alignment.
+ *
+ * dah_silu_mul -- mlp.act: act[t][i] = silu(g[t][i]) * g[t][inter + i],
+ *   silu(z) = z / (1 + e^-z); gate_up [T][2 inter], act [T][inter] float32.
+ */
+int dah_rmsnorm(const float* x, const float* w, float eps, int T, int width, float* y,
+                void* stream);
+
+int dah_silu_mul(const float* gate_up, int T, int inter, float* act, void* stream);
+
+/*
+ * decoder_layer_step -- one decoder layer's decode step (the per-layer rows
+ * of the Model Spec page's "Compute-graph nodes", in order): input_norm,
+ * attn.qkv_proj, the attention step (decode_attn_step_ex), attn.o_proj plus
+ * the attention residual, post_attn_norm, mlp.gate_up, mlp.act and mlp.down
+ * plus the MLP residual.
+ *
+ *   x, y         [device] float32 [B][hidden] (the residual stream in and
+ *                out; y may equal x)
+ *   w            the layer's weights (pointers to device memory, below)
+ *   hidden, inter  model width and MLP width, multiples of 256 (1024 and
+ *                3072 for Qwen3-0.6B)
+ *   num_heads, eps, rope_theta, the cache, block table, seq_lens, B,
+ *   max_seq_len, num_splits   as for decode_attn_step_ex
+ *   workspace    [device] at least dah_layer_workspace_bytes(...) bytes,
+ *                256-byte aligned (the intermediates and the attention's
+ *                workspace); contents need no initialisation.
+ *
+ * Eight launches in order on `stream` (nine with a cut sequence); the
+ * attention's arguments are checked before the first.
+ */
+typedef struct {
+  const float* w_in;       /* input_norm gain [hidden], float32 */
+  const void* w_qkv;       /* bfloat16 [(H + 16) * 128][hidden]: q_proj, k_proj, v_proj rows */
+  const float* q_gain;     /* q_norm gain [128] */
+  const float* k_gain;     /* k_norm gain [128] */
+  const void* w_o;         /* bfloat16 [hidden][H * 128] */
+  const float* w_post;     /* post_attn_norm gain [hidden] */
+  const void* w_gate_up;   /* bfloat16 [2 * inter][hidden]: gate rows, then up rows */
+  const void* w_down;      /* bfloat16 [hidden][inter] */
+} dah_layer_weights;
+
+size_t dah_layer_workspace_bytes(int B, int hidden, int inter, int num_heads, int cache_dtype,
+                                 int max_seq_len, int num_splits);
+
+int decoder_layer_step(const float* x, const dah_layer_weights* w, int hidden, int inter,
+                       int num_heads, float eps, float rope_theta, void* k_cache, void* v_cache,
+                       int cache_dtype, int64_t num_pages, const int32_t* block_table,
+                       int max_pages_per_seq, const int32_t* seq_lens, int B, int max_seq_len,
+                       int num_splits, float* y, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Static name of a dah_status value ("DAH_OK", ...); "unknown status" otherwise. */
 const char* dah_status_string(int status);
 

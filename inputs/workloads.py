@@ -320,3 +320,31 @@ def make_chunk_inputs(lens_old, chunks, num_heads: int, cache_dtype: str, seed: 
         "cu_tokens": torch.from_numpy(cu).to(device),
     }
     return t, table, seq_lens, cu
+
+
+INTERMEDIATE = 3072   # Qwen3-0.6B MLP width (Model Spec page: mlp.act I = 3072)
+
+
+def make_layer_weights(w: Workload, layer: int, device, inter: int = INTERMEDIATE):
+    """A decoder layer's weights on `device` (random, as the conformance check
+    draws them: "Model conformance" page, "How the comparison works", step 1):
+    the projections of make_projections, q/k gains of make_layer's draw,
+    norm gains 1 + N(0, 0.1), gate_up [2I, hidden] and down [hidden, I] with
+    entries N(0,1)/sqrt(fan-in) in bfloat16; plus the input x [B, hidden]."""
+    import torch
+
+    p = make_projections(w, layer, device)
+
+    def randn(shape, tensor_id):
+        return torch.randn(shape, generator=_torch_generator(torch, device, w, layer, tensor_id),
+                           device=device, dtype=torch.float32)
+
+    return {
+        "x": p["x"], "w_qkv": p["w_qkv"], "w_o": p["w_o"],
+        "w_in": 1.0 + 0.1 * randn((w.hidden,), 20),
+        "q_gain": 1.0 + 0.1 * randn((HEAD_DIM,), 3),
+        "k_gain": 1.0 + 0.1 * randn((HEAD_DIM,), 4),
+        "w_post": 1.0 + 0.1 * randn((w.hidden,), 21),
+        "w_gate_up": (randn((2 * inter, w.hidden), 22) / math.sqrt(w.hidden)).to(torch.bfloat16),
+        "w_down": (randn((w.hidden, inter), 23) / math.sqrt(inter)).to(torch.bfloat16),
+    }

@@ -1,0 +1,141 @@
+"""GPU parity of the decoder layer's pieces and of the whole layer step
+(decoder_layer_step) against the float64 oracle (oracle/layer.py).
+
+Gates: the hidden-size RMSNorm and silu*up elementwise within float32
+rounding (rel 1e-6 of the row / element); the residual product within the
+projection bound plus the add's rounding; the whole layer's x1 and y with
+rel-to-max <= 1e-4 (the products feed x as two bf16 terms, the attention its
+weights as two) and max abs 1e-4 (float32 cache) or 2e-2 (bf16 cache).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from dah_testlib import build_layer, cuda_available, gates, host_snapshot, sample_batch
+from inputs import workloads as W
+from oracle import decode_attention as O
+from oracle import layer as L
+from oracle import projections as P
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not cuda_available(), reason="needs a GPU")]
+
+
+def _dah():
+    import decode_attention_head_amd as dah
+    return dah
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _bits(w):
+    import torch
+    return w.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _rand(shape, seed, scale=1.0):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda") * scale
+
+
+@pytest.mark.parametrize("T,width", [(1, 1024), (37, 2560), (256, 1024), (5, 5120)])
+def test_rmsnorm_parity(T, width):
+    import torch
+    dah = _dah()
+    x = _rand((T, width), T + width, 2.0)
+    w = 1.0 + 0.1 * _rand((width,), 7)
+    y = dah.rmsnorm(x, w)
+    y2 = x.clone()
+    dah.rmsnorm(y2, w, y=y2)          # in place
+    torch.cuda.synchronize()
+    ref = L.rmsnorm(x.cpu().numpy(), w.cpu().numpy())
+    err = np.abs(y.cpu().numpy() - ref)
+    assert np.all(err <= 1e-6 * np.max(np.abs(ref), axis=1, keepdims=True)), float(err.max())
+    assert torch.equal(y2, y)
+
+
+@pytest.mark.parametrize("T,inter", [(1, 3072), (64, 3072), (256, 9728 // 4 * 4)])
+def test_silu_mul_parity(T, inter):
+    import torch
+    dah = _dah()
+    gu = _rand((T, 2 * inter), T + inter, 3.0)
+    gu[0, :8] = torch.tensor([0.0, -30.0, 30.0, -88.0, 1e-6, -1e-6, 10.0, -10.0], device="cuda")
+    act = dah.silu_mul(gu)
+    torch.cuda.synchronize()
+    ref = L.silu_mul(gu.cpu().numpy())
+    err = np.abs(act.cpu().numpy() - ref)
+    assert np.all(err <= 2e-6 * np.abs(ref) + 1e-30), float(np.max(err / (np.abs(ref) + 1e-30)))
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 1024, 2048), (48, 1024, 3072), (256, 1024, 3072)])
+def test_linear_residual_parity(T, N, K):
+    import torch
+    dah = _dah()
+    x = _rand((T, K), T + K)
+    w = (_rand((N, K), N + K) / np.sqrt(K)).to(torch.bfloat16)
+    r = _rand((T, N), T + N + K)
+    y = torch.empty_like(r)
+    lib = dah.lib()
+    dah.check(lib.dah_linear_residual(x.data_ptr(), w.data_ptr(), r.data_ptr(), T, N, K,
+                                      y.data_ptr(), None), "dah_linear_residual")
+    r2 = r.clone()
+    dah.check(lib.dah_linear_residual(x.data_ptr(), w.data_ptr(), r2.data_ptr(), T, N, K,
+                                      r2.data_ptr(), None), "dah_linear_residual")   # in place
+    torch.cuda.synchronize()
+    xr, wb, rr = x.cpu().numpy(), _bits(w), r.cpu().numpy()
+    ref = P.linear(xr, wb) + rr
+    bound = 2.0 ** -16 * P.linear(np.abs(xr), np.abs(O.bf16_bits_to_f64(wb)), "f64") + \
+        2.0 ** -23 * np.abs(ref) + 1e-30
+    assert np.all(np.abs(y.cpu().numpy() - ref) <= bound)
+    assert torch.equal(r2, y)
+
+
+def _layer_case(name, H):
+    w = dataclasses.replace(W.WORKLOADS[name], num_heads=H)
+    t, seq_lens, table, _ = build_layer(w)
+    p = W.make_layer_weights(w, 0, "cuda")
+    return w, t, seq_lens, table, p
+
+
+@pytest.mark.parametrize("name,H", [("ragged_f32_b6", 16), ("ragged_f32_b6", 40),
+                                    ("b256_s2048", 16), ("b256_s2048_h64", 64)])
+def test_decoder_layer_parity(name, H):
+    import torch
+    dah = _dah()
+    w, t, seq_lens, table, p = _layer_case(name, H)
+    _print(f"[layer] {name} H={H}")
+    sample = sample_batch(seq_lens, 6)
+    snap = host_snapshot(t, seq_lens, table, sample)
+    weights = {n: p[n] for n in dah.LAYER_WEIGHTS}
+    y = dah.decoder_layer_step(p["x"], weights, t["k_pool"], t["v_pool"], t["block_table"],
+                               t["seq_lens"], int(seq_lens.max()), rope_theta=w.rope_theta)
+    torch.cuda.synchronize()
+    wnp = {n: (_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy())
+           for n, v in weights.items()}
+    ref = L.decoder_layer(p["x"].cpu().numpy()[sample], wnp, snap["k_pool"], snap["v_pool"],
+                          snap["block_table"], snap["seq_lens"], w.cache_dtype, num_heads=H,
+                          theta=w.rope_theta)
+    tol = 1e-4 if w.cache_dtype == "f32" else 2e-2
+    e_abs, e_rel = gates(y[sample].cpu().numpy().astype(np.float64), ref["y"], None, tol,
+                         label=f"{name} y")
+    _print(f"  y max abs {e_abs:.2e}  rel-to-max {e_rel:.2e}")
+
+
+def test_layer_rejects_before_launching():
+    """Bad attention arguments are caught before the first kernel: the output
+    buffer stays untouched."""
+    import torch
+    dah = _dah()
+    w, t, seq_lens, table, p = _layer_case("tiny_f32_b2", 16)
+    weights = {n: p[n] for n in dah.LAYER_WEIGHTS}
+    y = torch.full_like(p["x"], 7.0)
+    with pytest.raises(dah.DahError):
+        dah.decoder_layer_step(p["x"], weights, t["k_pool"], t["v_pool"], t["block_table"],
+                               t["seq_lens"], 10_000, y=y)    # max_seq_len past the table
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
