@@ -19,6 +19,9 @@ The JSON line reports
 workload's lengths counting them), under "chunk": HIP-graph-replayed time,
 K/V bytes (each cached position once per sequence) and attention flops.
 
+--layer also times decoder_layer_step (input_norm, the block with its
+projections, residuals, SwiGLU MLP) on the same batch, graph-replayed.
+
 --block also times the projections on either side of the block (attn.qkv_proj
 before the step, attn.o_proj after it) on the same batch and reports them under
 "block": per-launch durations (HIP events), their bytes and flops, and the
@@ -65,6 +68,8 @@ def parse():
                     help="skip the streaming-read probe (practical bandwidth ceiling)")
     ap.add_argument("--chunk", type=int, default=0, metavar="N",
                     help="also time chunk_attn_step with N new tokens per sequence")
+    ap.add_argument("--layer", action="store_true",
+                    help="also time decoder_layer_step on the same batch")
     ap.add_argument("--block", action="store_true",
                     help="also time qkv_proj and o_proj around the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -192,6 +197,32 @@ def time_block(dah, torch, w, t, L, ws, stream, args):
             "note": "x [B,hidden] f32, bf16 weights; block = qkv_proj + decode_attn_step + o_proj"}
 
 
+def time_layer(dah, torch, w, t, L, args):
+    """decoder_layer_step on the workload's batch, graph-replayed; the cache
+    is restored afterwards (each call appends)."""
+    p = W.make_layer_weights(w, 0, t["q"].device)
+    weights = {n: p[n] for n in dah.LAYER_WEIGHTS}
+    inter = p["w_down"].shape[1]
+    ws = torch.empty(dah.layer_workspace_bytes(w.batch, w.hidden, inter, L, args.num_splits,
+                                               w.num_heads, w.cache_dtype),
+                     dtype=torch.uint8, device=t["q"].device)
+    y = torch.empty_like(p["x"])
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+
+    def run():
+        dah.decoder_layer_step(p["x"], weights, t["k_pool"], t["v_pool"], t["block_table"],
+                               t["seq_lens"], L, rope_theta=w.rope_theta,
+                               num_splits=args.num_splits, y=y, workspace=ws)
+    us = _graph_us(torch, run, 10)
+    t["k_pool"].copy_(k0)
+    t["v_pool"].copy_(v0)
+    H, hid = w.num_heads, w.hidden
+    weight_bytes = 2 * hid * ((H + 16) * 128 + H * 128 + 3 * inter)
+    return {"us": round(us, 2), "tokens_per_s": round(w.batch / (us * 1e-6), 1),
+            "hidden": hid, "inter": inter, "weight_bytes": weight_bytes,
+            "timing": "HIP graph replay of 10 calls, mean per call"}
+
+
 def time_chunk(dah, torch, w, seq_lens, num_pages, n):
     """chunk_attn_step with n new tokens per sequence of the workload (its
     seq_lens count them), bf16 cache, graph-replayed."""
@@ -315,6 +346,7 @@ def main():
 
     block = time_block(dah, torch, w, t, L, ws, stream, args) if args.block else None
     chunk = time_chunk(dah, torch, w, seq_lens, num_pages, args.chunk) if args.chunk > 0 else None
+    layer = time_layer(dah, torch, w, t, L, args) if args.layer else None
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -368,6 +400,8 @@ def main():
         line["block"] = block
     if chunk is not None:
         line["chunk"] = chunk
+    if layer is not None:
+        line["layer"] = layer
     print(json.dumps(line), flush=True)
 
 
