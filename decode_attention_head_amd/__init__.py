@@ -277,6 +277,12 @@ def linear(x, w, *, y=None, stream=None):
     return y
 
 
+def linear_kernel(T: int, N: int, K: int) -> int:
+    """Which kernel dah_linear launches for a T x N x K product (host only):
+    0 split-k, 1..5 the LDS tile shapes, -1 for an invalid shape."""
+    return int(lib().dah_linear_kernel(int(T), int(N), int(K)))
+
+
 def qkv_proj(x, w_qkv, num_heads: int = NUM_HEADS, *, q=None, k=None, v=None, stream=None):
     """attn.qkv_proj: x [T,hidden] float32, w_qkv [H*128 + 2048, hidden] bfloat16
     (q_proj, k_proj, v_proj rows stacked) -> (q [T,H,128], k [T,8,128],

@@ -10,13 +10,15 @@
 // bfloat16 terms, hi = RNE(x) and lo = RNE(x - hi), so the product carries x
 // to 2^-18 relative; w is exact.  Accumulation is float32.
 //
-// At decode sizes (T <= a few hundred tokens, K and N ~ 1-10 thousand) the
-// product is a few microseconds of data movement, so what matters is
-// latency: few dependent round trips to memory per wave and enough
-// workgroups.  linear_splitk_kernel gives each of a workgroup's 8 waves an
-// eighth of k with operands loaded straight into registers (four k steps in
-// flight), sums the partial tiles in LDS, and picks the tile width so that
-// the grid has at least 256 workgroups.
+// For decode's few rows (T < 32) the product is a few microseconds of data
+// movement, so what matters is latency: few dependent round trips to memory
+// per wave and enough workgroups.  linear_splitk_kernel gives each of a
+// workgroup's 8 waves an eighth of k with operands loaded straight into
+// registers (four k steps in flight), sums the partial tiles in LDS, and
+// picks the tile width so that the grid has at least 256 workgroups.  From a
+// few dozen rows on, every weight tile is shared by several row tiles, and
+// linear_lds_kernel stages coalesced x and w tiles in LDS so that each is
+// read from L2 once per tile instead of once per wave.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -229,29 +231,256 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
   }
 }
 
+// ---------------------------------------------------------------- LDS tiles
+
+constexpr int kLdsThreads = 256;   // 4 waves
+
+// For larger T, where every weight tile is shared by several row tiles and
+// every x row by many column tiles, a workgroup of 4 waves computes a
+// kBM x kBN output tile and walks k in chunks of kBK = 32 kKS kWK.  Per
+// chunk the 256 threads load the x and w tiles with coalesced 16-byte loads
+// (kDepth chunks ahead: the loads of the next kDepth chunks are in flight
+// while this one is multiplied, since one chunk's round trip to L2 takes
+// longer than its products), split x into its two bfloat16 terms once, and
+// write hi, lo and w to LDS in
+// the operand layout; wave (wm, wn, wk) then multiplies its
+// (kBM / kWM) x (kBN / kWN) sub-tile over kKS 32-wide k steps of the chunk.
+// With kWK > 1 the waves of a sub-tile take different k steps and their
+// partial tiles are added in LDS, in a fixed order, at the end.
+template <int kBM, int kBN, int kWM, int kWN, int kWK, int kKS, int kDepth>
+__global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
+  static_assert(kWM * kWN * kWK == kLdsThreads / kWave, "4 waves");
+  constexpr int kBK = 32 * kKS * kWK;
+  constexpr int kSM = kBM / kWM / 16, kSN = kBN / kWN / 16;   // 16 x 16 blocks per wave
+  static_assert(kSM * kWM * 16 == kBM && kSN * kWN * 16 == kBN, "tile split");
+  constexpr int kRow = kBK + 8;   // bfloat16 per LDS row: 16 bytes of padding
+  constexpr int kX4 = kBM * kBK / 4 / kLdsThreads;   // float4 loads of x per thread
+  constexpr int kW8 = kBN * kBK / 8 / kLdsThreads;   // 16-byte loads of w per thread
+  static_assert(kX4 * 4 * kLdsThreads == kBM * kBK && kW8 * 8 * kLdsThreads == kBN * kBK,
+                "whole loads");
+  __shared__ __attribute__((aligned(16))) uint16_t xh[kBM][kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t xl[kBM][kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[kBN][kRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % kWM, wn = (wave / kWM) % kWN, wk = wave / (kWM * kWN);
+  const int r = lane >> 4, c = lane & 15;
+  const int n_tiles = a.N / kBN;
+  const int n0 = (blockIdx.x % n_tiles) * kBN;
+  const int m0 = (blockIdx.x / n_tiles) * kBM;
+  const int chunks = a.K / kBK;
+
+  // Coalesced tile loads: consecutive threads take consecutive 16 bytes of
+  // a row.  Rows of x past T read as zero.
+  const float* xsrc[kX4];
+  bool xok[kX4];
+#pragma unroll
+  for (int i = 0; i < kX4; ++i) {
+    const int idx = tid + kLdsThreads * i;
+    const int row = idx / (kBK / 4), t = m0 + row;
+    xok[i] = t < a.T;
+    xsrc[i] = a.x + (size_t)(xok[i] ? t : 0) * a.K + 4 * (idx % (kBK / 4));
+  }
+  const uint16_t* wsrc[kW8];
+#pragma unroll
+  for (int i = 0; i < kW8; ++i) {
+    const int idx = tid + kLdsThreads * i;
+    wsrc[i] = a.w + (size_t)(n0 + idx / (kBK / 8)) * a.K + 8 * (idx % (kBK / 8));
+  }
+  struct Chunk {
+    float4 x[kX4];
+    u32x4 w[kW8];
+  };
+  auto load = [&](Chunk& b, int chunk) {
+    const int k = chunk * kBK;
+#pragma unroll
+    for (int i = 0; i < kX4; ++i)
+      b.x[i] = xok[i] ? *reinterpret_cast<const float4*>(xsrc[i] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kW8; ++i) b.w[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + k);
+  };
+  auto stage = [&](const Chunk& b) {
+#pragma unroll
+    for (int i = 0; i < kX4; ++i) {
+      const int idx = tid + kLdsThreads * i;
+      const int row = idx / (kBK / 4), col = 4 * (idx % (kBK / 4));
+      const float4 v = b.x[i];
+      const uint32_t h0 = pack2(v.x, v.y), h1 = pack2(v.z, v.w);
+      const uint32_t l0 = pack2(v.x - lo_half(h0), v.y - hi_half(h0));
+      const uint32_t l1 = pack2(v.z - lo_half(h1), v.w - hi_half(h1));
+      *reinterpret_cast<uint2*>(&xh[row][col]) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(&xl[row][col]) = make_uint2(l0, l1);
+    }
+#pragma unroll
+    for (int i = 0; i < kW8; ++i) {
+      const int idx = tid + kLdsThreads * i;
+      *reinterpret_cast<u32x4*>(&ws[idx / (kBK / 8)][8 * (idx % (kBK / 8))]) = b.w[i];
+    }
+  };
+
+  f32x4 acc[kSM][kSN];
+#pragma unroll
+  for (int mb = 0; mb < kSM; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kSN; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int arow = wm * (kBM / kWM) + c, brow = wn * (kBN / kWN) + c;
+
+  auto multiply = [&]() {
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+      const int kk = 32 * (wk * kKS + s) + 8 * r;
+      u32x4 b[kSN];
+#pragma unroll
+      for (int nb = 0; nb < kSN; ++nb) b[nb] = *reinterpret_cast<const u32x4*>(&ws[brow + 16 * nb][kk]);
+#pragma unroll
+      for (int mb = 0; mb < kSM; ++mb) {
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&xh[arow + 16 * mb][kk]);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&xl[arow + 16 * mb][kk]);
+#pragma unroll
+        for (int nb = 0; nb < kSN; ++nb) acc[mb][nb] = mfma(hi, b[nb], acc[mb][nb]);
+#pragma unroll
+        for (int nb = 0; nb < kSN; ++nb) acc[mb][nb] = mfma(lo, b[nb], acc[mb][nb]);
+      }
+    }
+  };
+
+  // A ring of kDepth register buffers; buffer i always holds chunks
+  // congruent to i mod kDepth, so every index is a compile-time constant.
+  Chunk buf[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i)
+    if (i < chunks) load(buf[i], i);
+  for (int c0 = 0; c0 < chunks; c0 += kDepth) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      const int chunk = c0 + i;
+      if (chunk < chunks) {
+        __syncthreads();   // the previous chunk's products are done with LDS
+        stage(buf[i]);
+        __syncthreads();
+        if (chunk + kDepth < chunks) load(buf[i], chunk + kDepth);
+        multiply();
+      }
+    }
+  }
+
+  const Segment sg = segment_of(a, n0);
+  if constexpr (kWK == 1) {
+#pragma unroll
+    for (int mb = 0; mb < kSM; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kSN; ++nb)
+        store_block(a, sg, m0 + wm * (kBM / kWM) + 16 * mb, n0 + wn * (kBN / kWN) + 16 * nb,
+                    acc[mb][nb], lane);
+  } else {
+    __shared__ f32x4 part[kWK][kWM * kWN * kSM * kSN][kWave];
+    const int sub = wm + kWM * wn;
+#pragma unroll
+    for (int mb = 0; mb < kSM; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kSN; ++nb) part[wk][(sub * kSM + mb) * kSN + nb][lane] = acc[mb][nb];
+    __syncthreads();
+    for (int job = wave; job < kWM * kWN * kSM * kSN; job += kLdsThreads / kWave) {
+      f32x4 t = part[0][job][lane];
+#pragma unroll
+      for (int q = 1; q < kWK; ++q) t += part[q][job][lane];
+      const int js = job / (kSM * kSN), mb = (job / kSN) % kSM, nb = job % kSN;
+      store_block(a, sg, m0 + (js % kWM) * (kBM / kWM) + 16 * mb,
+                  n0 + (js / kWM) * (kBN / kWN) + 16 * nb, t, lane);
+    }
+  }
+}
+
 struct LinearConfig {
+  int lds;          // 0: linear_splitk_kernel<mb, nb, mw>; else an LDS tile shape, by id
   int mb, nb, mw;
 };
 
-// Tile shape: the widest of 64, 32, 16 columns (32 rows per tile) that
-// still gives kLinMinGroups workgroups, else 16 x 16 tiles.  Swept on MI355X
-// over 12 shapes (rows per wave 1-2, columns 1-4 blocks, 1-4 row groups) at
-// T = 2 .. 256 and N x K = 4096 x 1024, 1024 x 2048 (graph-replayed launch
-// times): this rule picks the fastest shape or one within 3% of it in every
-// case.  What the time follows is the traffic from L2: x is read once per
-// column tile and w once per row tile, at ~6 TB/s.
-LinearConfig pick_config(int T, int N) {
-#ifdef DAH_LINEAR_CONFIG
-  (void)T; (void)N;
-  return LinearConfig{DAH_LINEAR_CONFIG};
+// An LDS tile shape needs N, and every output segment's first column, to be
+// multiples of its width, and k to be a multiple of its chunk.
+bool lds_fits(const LinearArgs& a, int bn, int bk) {
+  if (a.N % bn != 0 || a.K % bk != 0) return false;
+  for (int i = 0; i < a.nseg; ++i)
+    if (a.seg[i].begin % bn != 0) return false;
+  return true;
+}
+
+// The instantiated LDS tile shapes (launch_lds_shape):
+//   1: 64 x 128, 2 x 2 waves, k chunks of 64     2: 64 x 64, 2 x 2 waves, chunks of 64
+//   3: 32 x 64, 1 x 2 waves x 2 k slices, 64     4: 32 x 32, 4 k slices, chunks of 128
+//   5: 32 x 32, 4 k slices, chunks of 256, two chunks in flight
+//
+// Tile choice: the largest tile that still gives 512 workgroups (two per
+// compute unit), else 32 x 32 with the k steps split over the waves (the
+// deep-chunk form for long k at up to 256 rows) while that gives 128
+// workgroups, else the split-k kernel; T < 32 always takes the split-k
+// kernel, which is built for decode's few rows.  Swept on MI355X over
+// T = 32 .. 4096 and (N, K) = (4096, 1024), (1024, 2048), (6144, 1024),
+// (1024, 3072), (10240, 1024), (1024, 8192) (graph-replayed launch times):
+// this rule picks the fastest or one within 5% of it in every case.
+int pick_lds(const LinearArgs& a) {
+  if (a.T < 32) return 0;
+  auto groups = [&](int bm, int bn) { return (long long)((a.T + bm - 1) / bm) * (a.N / bn); };
+  if (lds_fits(a, 128, 64) && groups(64, 128) >= 512) return 1;
+  if (lds_fits(a, 64, 64) && groups(64, 64) >= 512) return 2;
+  if (lds_fits(a, 64, 64) && groups(32, 64) >= 512) return 3;
+  if (lds_fits(a, 32, 128) && groups(32, 32) >= 128)
+    return (a.K >= 2048 && a.T <= 256 && lds_fits(a, 32, 256)) ? 5 : 4;
+  return 0;
+}
+
+// Split-k tile shape (T < 32, or too few LDS tiles): the widest of 64, 32,
+// 16 columns (32 rows per tile) that still gives kLinMinGroups workgroups,
+// else 16 x 16 tiles.  Swept on MI355X over 12 shapes (rows per wave 1-2,
+// columns 1-4 blocks, 1-4 row groups) at T = 2 .. 256 and N x K =
+// 4096 x 1024, 1024 x 2048 (graph-replayed launch times): this rule picks
+// the fastest shape or one within 3% of it in every case.
+LinearConfig pick_config(const LinearArgs& a) {
+#if defined(DAH_LINEAR_CONFIG)
+  (void)a;
+  return LinearConfig{0, DAH_LINEAR_CONFIG};
+#elif defined(DAH_LINEAR_LDS)
+  (void)a;
+  return LinearConfig{DAH_LINEAR_LDS, 0, 0, 0};
 #else
-  if (T > 16) {
-    const int m_tiles = (T + 31) / 32;
+  const int lds = pick_lds(a);
+  if (lds != 0) return {lds, 0, 0, 0};
+  if (a.T > 16) {
+    const int m_tiles = (a.T + 31) / 32;
     for (int nb = 4; nb >= 1; nb /= 2)
-      if (m_tiles * (N / (16 * nb)) >= kLinMinGroups) return {2, nb, 1};
+      if (m_tiles * (a.N / (16 * nb)) >= kLinMinGroups) return {0, 2, nb, 1};
   }
-  return {1, 1, 1};
+  return {0, 1, 1, 1};
 #endif
+}
+
+template <int kBM, int kBN, int kWM, int kWN, int kWK, int kKS, int kDepth>
+int launch_lds(const LinearArgs& a, hipStream_t stream) {
+  if (!lds_fits(a, kBN, 32 * kKS * kWK))
+    return dah::set_error(DAH_ERR_SHAPE, "linear: tile %dx%d does not divide N=%d, K=%d", kBM,
+                          kBN, a.N, a.K);
+  const long long groups = (long long)((a.T + kBM - 1) / kBM) * (a.N / kBN);
+  if (groups > INT32_MAX) return dah::set_error(DAH_ERR_SHAPE, "linear: grid too large");
+  linear_lds_kernel<kBM, kBN, kWM, kWN, kWK, kKS, kDepth>
+      <<<dim3((unsigned)groups), kLdsThreads, 0, stream>>>(a);
+  return DAH_OK;
+}
+
+int launch_lds_shape(int id, const LinearArgs& a, hipStream_t stream) {
+  switch (id) {
+#ifdef DAH_LINEAR_LDS_SHAPES
+    DAH_LINEAR_LDS_SHAPES
+#else
+    case 1: return launch_lds<64, 128, 2, 2, 1, 2, 1>(a, stream);
+    case 2: return launch_lds<64, 64, 2, 2, 1, 2, 1>(a, stream);
+    case 3: return launch_lds<32, 64, 1, 2, 2, 1, 1>(a, stream);
+    case 4: return launch_lds<32, 32, 1, 1, 4, 1, 1>(a, stream);
+    case 5: return launch_lds<32, 32, 1, 1, 4, 2, 2>(a, stream);
+#endif
+    default: return dah::set_error(DAH_ERR_HIP, "linear: no LDS tile shape %d", id);
+  }
 }
 
 template <int kMB, int kNB, int kMW>
@@ -262,7 +491,11 @@ void launch_cfg(const LinearArgs& a, hipStream_t stream) {
 }
 
 int launch_linear(LinearArgs& a, hipStream_t stream) {
-  const LinearConfig c = pick_config(a.T, a.N);
+  const LinearConfig c = pick_config(a);
+  if (c.lds != 0) {
+    const int st = launch_lds_shape(c.lds, a, stream);
+    if (st != DAH_OK) return st;
+  } else {
   // The instantiated shapes; N is a multiple of 64, so every column tiling divides it.
 #define DAH_LIN_CASE(MB, NB, MW) \
   if (c.mb == MB && c.nb == NB && c.mw == MW) launch_cfg<MB, NB, MW>(a, stream); else
@@ -282,6 +515,7 @@ int launch_linear(LinearArgs& a, hipStream_t stream) {
 #endif
   return dah::set_error(DAH_ERR_HIP, "linear: no kernel for tile %d/%d/%d", c.mb, c.nb, c.mw);
 #undef DAH_LIN_CASE
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return dah::set_error(DAH_ERR_HIP, "linear kernel launch failed: %s", hipGetErrorString(e));
@@ -291,6 +525,16 @@ int launch_linear(LinearArgs& a, hipStream_t stream) {
 }  // namespace
 
 extern "C" {
+
+int dah_linear_kernel(int T, int N, int K) {
+  if (T < 1 || N < 64 || N % 64 != 0 || K < 256 || K % 256 != 0) return -1;
+  LinearArgs a = {};
+  a.T = T;
+  a.N = N;
+  a.K = K;
+  a.nseg = 1;
+  return pick_config(a).lds;
+}
 
 int dah_linear(const float* x, const void* w, int T, int N, int K, float* y, void* stream) {
   int st = dah::validate_linear(x, w, T, N, K, y);

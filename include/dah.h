@@ -337,6 +337,15 @@ int dah_linear_residual(const float* x, const void* w, const float* residual, in
                         int K, float* y, void* stream);
 
 /*
+ * dah_linear_kernel -- host only, no device call: which kernel dah_linear
+ *   (and the projections built on it) launches for a T x N x K product:
+ *   0 = the split-k kernel (decode's few rows), 1..5 = the LDS-tiled kernel
+ *   with tiles 64x128, 64x64, 32x64, 32x32, 32x32 with 256-wide k chunks;
+ *   -1 if the shape is invalid.  For tests and benchmarks.
+ */
+int dah_linear_kernel(int T, int N, int K);
+
+/*
  * dah_rmsnorm -- rows of a hidden-size RMSNorm (the input_norm,
  *   post_attn_norm and final_norm rows of the Model Spec page:
  *   y = x / sqrt(sum x^2 / H + eps) * w, H = width): x, y [T][width]

@@ -356,3 +356,26 @@ def test_projection_entry_points_reject():
     assert lib.attn_qkv_proj(A, A, 4, 1000, 16, A, A, A, None) == 2
     assert lib.attn_o_proj(A, A, 4, 48, 1024, A, None) == 2
     assert lib.attn_o_proj(A, A, 4, 16, 1000, A, None) == 2
+
+
+def test_linear_kernel_choice():
+    """The tile rule of dah_linear (host only): decode's few rows take the
+    split-k kernel, the measured projection shapes at B = 256 the tiles the
+    sweep found fastest, invalid shapes -1; and the GPU parity cases of
+    dah_linear reach every kernel."""
+    lib = _lib()
+    assert lib.dah_linear_kernel(1, 4096, 1024) == 0
+    assert lib.dah_linear_kernel(16, 6144, 1024) == 0
+    assert lib.dah_linear_kernel(48, 1024, 2048) == 0          # few tiles: split-k
+    assert lib.dah_linear_kernel(256, 4096, 1024) == 3         # qkv at 16 heads
+    assert lib.dah_linear_kernel(256, 1024, 2048) == 5         # o_proj
+    assert lib.dah_linear_kernel(256, 6144, 1024) == 3         # gate_up
+    assert lib.dah_linear_kernel(256, 1024, 3072) == 5         # down
+    assert lib.dah_linear_kernel(256, 10240, 1024) == 2        # qkv at 64 heads
+    assert lib.dah_linear_kernel(4096, 4096, 1024) == 1        # prefill-sized
+    assert lib.dah_linear_kernel(1000, 192, 256) == 4          # N not a multiple of 128
+    for bad in ((0, 64, 256), (4, 96, 256), (4, 64, 128), (4, 0, 256)):
+        assert lib.dah_linear_kernel(*bad) == -1
+    import test_gpu_projections as tp
+    reached = {lib.dah_linear_kernel(T, N, K) for T in tp.LINEAR_T for N, K in tp.LINEAR_NK}
+    assert reached == {0, 1, 2, 3, 4, 5}

@@ -72,7 +72,8 @@ def test_silu_mul_parity(T, inter):
     assert np.all(err <= 2e-6 * np.abs(ref) + 1e-30), float(np.max(err / (np.abs(ref) + 1e-30)))
 
 
-@pytest.mark.parametrize("T,N,K", [(1, 1024, 2048), (48, 1024, 3072), (256, 1024, 3072)])
+@pytest.mark.parametrize("T,N,K", [(1, 1024, 2048), (48, 1024, 3072), (256, 1024, 3072),
+                                   (300, 6144, 1024), (1000, 4096, 1024)])
 def test_linear_residual_parity(T, N, K):
     import torch
     dah = _dah()

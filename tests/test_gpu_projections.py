@@ -57,13 +57,19 @@ def _rand(shape, seed, scale=1.0, dtype=None):
     return t if dtype is None else t.to(dtype)
 
 
-@pytest.mark.parametrize("N,K", [(4096, 1024), (1024, 2048), (192, 256)])
-@pytest.mark.parametrize("T", [1, 7, 16, 17, 48, 64, 65, 128, 256, 300])
+LINEAR_T = [1, 7, 16, 17, 33, 48, 64, 65, 128, 256, 300, 511, 1000]
+LINEAR_NK = [(4096, 1024), (1024, 2048), (192, 256)]
+
+
+@pytest.mark.parametrize("N,K", LINEAR_NK)
+@pytest.mark.parametrize("T", LINEAR_T)
 def test_linear_parity(T, N, K):
-    """Both kernels (T <= 64: split-k skinny; T > 64: tiled), ragged row
+    """Every kernel and tile shape the product picks (the split-k kernel and
+    the five LDS tiles: the cases cover all six, see test_abi), ragged row
     tails, three shapes; a guard row after the output stays untouched."""
     import torch
     dah = _dah()
+    kernel = dah.linear_kernel(T, N, K)
     x = _rand((T, K), 100 + T)
     w = _rand((N, K), 200 + N, 1.0 / np.sqrt(K), torch.bfloat16)
     y_all = torch.full((T + 1, N), float("nan"), device="cuda")
@@ -71,7 +77,8 @@ def test_linear_parity(T, N, K):
     torch.cuda.synchronize()
     assert torch.isnan(y_all[T]).all(), "wrote past the output"
     worst, rel = _check(y.cpu().numpy(), x.cpu().numpy(), _bits(w), f"T={T} N={N} K={K}")
-    _print(f"[linear] T={T} N={N} K={K}: {worst:.3f} of bound, rel-to-max {rel:.2e}")
+    _print(f"[linear] T={T} N={N} K={K} kernel {kernel}: {worst:.3f} of bound, "
+           f"rel-to-max {rel:.2e}")
 
 
 @pytest.mark.parametrize("H,hidden", [(16, 1024), (32, 2560), (40, 5120), (64, 5120)])
