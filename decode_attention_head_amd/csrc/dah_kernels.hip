@@ -1656,6 +1656,196 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void chunk_attn_kerne
   }
 }
 
+// Chunks of several tiles (prefill, longer verification): the tiles of one
+// KV head share each K/V page through LDS.  A workgroup of 8 waves takes one
+// sequence, kHG = 8 / kTG KV heads and kTG consecutive token tiles, one
+// (head, tile) per wave -- 8 tiles of one head for long chunks, 2 tiles of 4
+// heads for chunks of two tiles, so that every wave has work.  Per page the
+// 512 threads load the kHG heads' K and V tiles (4 KB each, 16 bytes per
+// thread and head, 8 / kHG pages ahead in registers: always 8 pieces in
+// flight) and write them to one of two LDS stages -- K with its 16-byte
+// pieces XOR-swizzled by position, so that the score product's reads (16
+// positions at one dim offset) fall on distinct banks; each wave then reads
+// its register tiles from LDS and attends as chunk_attn_kernel does.  The
+// cache is read once per kTG tiles instead of once per tile, and the
+// workgroups of one KV head (for kTG = 8) are consecutive modulo 8, which
+// keeps them on one XCD, where they share the pages through L2.
+
+constexpr int kChunkWaves = kDecodeWavesPerBlock;  // (head, tile) pairs per workgroup
+constexpr int kChunkRing = 8;                      // 16-byte pieces in flight per thread
+#ifndef DAH_CHUNK_PREFILL_MIN_TILES
+#define DAH_CHUNK_PREFILL_MIN_TILES 2
+#endif
+constexpr int kChunkPrefillMinTiles = DAH_CHUNK_PREFILL_MIN_TILES;  // from this many tiles on
+
+template <int kG, int kTG>
+__global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(ChunkArgs a) {
+  constexpr int kH = kG * kKvHeads;
+  constexpr int kTpt = 16 / kG;  // tokens per tile
+  constexpr int kHG = kChunkWaves / kTG;   // KV heads per workgroup
+  constexpr int kDepth = kChunkRing / kHG; // pages in flight
+  using TileV = Tile<DAH_BF16>;
+  constexpr int kTileBytes = (int)TileV::kTileBytes;
+  constexpr int kHeadBytes = 2 * kTileBytes;  // K and V of one head in a stage
+  static_assert(kHG * kTG == kChunkWaves && kKvHeads % kHG == 0, "heads x tiles = 8 waves");
+  static_assert(kWave * kChunkWaves * 16 == kHeadBytes, "one 16-byte piece per thread and head");
+  static_assert(kDepth >= 2 && kDepth % 2 == 0, "stages alternate within the unrolled ring");
+  __shared__ __attribute__((aligned(16))) char stage[2][kHG * kHeadBytes];  // [stage][head][K|V]
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = wave / kTG, tw = wave - hw * kTG;   // the wave's local head and tile
+  const int row = lane >> 4, col = lane & 15;
+  const int groups = (a.tiles + kTG - 1) / kTG;
+  constexpr int kHeadGroups = kKvHeads / kHG;
+  const int gh = blockIdx.x % kHeadGroups;
+  const int bg = blockIdx.x / kHeadGroups;
+  const int b = bg / groups;
+  const int grp = bg - b * groups;
+  const int g = gh * kHG + hw;   // the wave's KV head
+  const int t0 = min(max(a.cu_tokens[b], 0), a.total);
+  const int t1 = min(max(a.cu_tokens[b + 1], t0), a.total);
+  const int n = t1 - t0;
+  const int tile0 = grp * kTG;
+  if (tile0 * kTpt >= n) return;  // the whole workgroup
+  const int tile = tile0 + tw;
+  const int i0 = tile * kTpt;
+  const bool live = i0 < n;       // wave-uniform
+  const int seq_len = a.seq_lens[b];
+  if (n > a.max_chunk || seq_len < n || seq_len > a.max_seq_len) {
+    // Outside the preconditions: NaN for the wave's tokens (and, from tile
+    // 0, for tokens past the tiles), nothing read from the cache.
+    auto poison = [&](int from, int to) {
+      for (int i = from; i < to; ++i)
+        for (int h = 0; h < kG; ++h)
+          reinterpret_cast<float2*>(a.o + (((size_t)t0 + i) * kH + g * kG + h) * kHeadDim)[lane] =
+              make_float2(NAN, NAN);
+    };
+    if (live && tile < a.tiles) poison(i0, min(n, i0 + kTpt));
+    if (tile == 0) poison(a.tiles * kTpt, n);
+    return;  // the whole workgroup (the condition is uniform)
+  }
+
+  // Within the preconditions every live tile is below a.tiles.
+  const int ntok = live ? min(kTpt, n - i0) : 1;
+  const int pos0 = seq_len - n + i0;  // position of the wave's first token
+  const int pmax = pos0 + ntok - 1;
+  const int wave_last = live ? pmax / kPage : -1;  // last page this wave attends
+  const int first_masked = (pos0 + 1) / kPage;
+  const int group_tokens = min(n, (tile0 + kTG) * kTpt);
+  const int last = (seq_len - n + group_tokens - 1) / kPage;  // last page of any wave
+  const int ti = col / kG, hh = col - ti * kG;
+  const bool col_live = live && ti < ntok;
+  const int climit_pos = pos0 + (col_live ? ti : ntok - 1);
+  const size_t qrow = ((size_t)t0 + (live ? i0 : 0) + (col_live ? ti : 0)) * kH + g * kG +
+                      (col_live ? hh : 0);
+
+  typedef const __attribute__((address_space(4))) int32_t* ConstI32;
+  const ConstI32 bt = (ConstI32)(a.block_table + (size_t)b * a.max_pages_per_seq);
+  const int64_t page_bytes = (int64_t)kKvHeads * kTileBytes;
+  // This thread's 16-byte piece of every page and head: K pieces for threads
+  // 0..255, V pieces for 256..511; its place in the stage (K swizzled).
+  const int kv = tid >> 8, piece = tid & 255;
+  const char* src = (kv ? a.v_cache : a.k_cache) + (int64_t)gh * kHG * kTileBytes + 16 * piece;
+  const int ppos = piece >> 4, pc = piece & 15;
+  const int dst = kv ? kTileBytes + 16 * piece : 256 * ppos + 16 * (pc ^ ppos);
+  bool bad_page = false;
+  auto fetch = [&](u32x4 (&out)[kHG], int p) {
+    const int id = bt[p];
+    const bool ok = id >= 0 && id < a.num_pages;
+    bad_page |= !ok && p <= wave_last;
+    const char* at = src + (int64_t)(ok ? id : 0) * page_bytes;
+#pragma unroll
+    for (int h = 0; h < kHG; ++h) out[h] = *reinterpret_cast<const u32x4*>(at + h * kTileBytes);
+  };
+  u32x4 ring[kDepth][kHG];
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i)
+    if (i <= last) fetch(ring[i], i);
+
+  float qv[4][8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) load8(a.q + qrow * kHeadDim + 32 * kk + 8 * row, qv[kk]);
+  const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  u32x4 qb[4][3];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[kk][e] *= qscale;
+    split3(qv[kk], qb[kk]);
+  }
+  if (!col_live) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) qb[kk][t] = u32x4{0u, 0u, 0u, 0u};
+  }
+  MfmaState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int kpos = 4 * (col & 3) + (col >> 2);  // sigma(col): the score product's K row
+  for (int p0 = 0; p0 <= last; p0 += kDepth) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      const int p = p0 + i;
+      if (p <= last) {
+        // Stage i & 1 was last read two pages ago, before the previous
+        // barrier.
+#pragma unroll
+        for (int h = 0; h < kHG; ++h)
+          *reinterpret_cast<u32x4*>(&stage[i & 1][h * kHeadBytes + dst]) = ring[i][h];
+        __syncthreads();
+        if (p + kDepth <= last) fetch(ring[i], p + kDepth);
+        if (p <= wave_last) {
+          const char* sk = &stage[i & 1][hw * kHeadBytes];
+          KTileMfma K;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            K.w[kk] = *reinterpret_cast<const u32x4*>(sk + 256 * kpos + 16 * ((row + 4 * kk) ^ kpos));
+          TileV V;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            V.w[j] = *reinterpret_cast<const u32x4*>(sk + kTileBytes + 16 * (lane + kWave * j));
+          if (p < first_masked) {
+            attend_page_mfma<false>(K, V, qb, st, lane, kPage);
+          } else {
+            attend_page_mfma<true, true>(K, V, qb, st, lane, pmax - kPage * p + 1,
+                                         climit_pos - kPage * p + 1);
+          }
+        }
+      }
+    }
+  }
+  if (!live) return;
+
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int j = 4 * row + v;   // accumulator row: column j = (token j / G, head j % G)
+    const float lj = __shfl(l, j);
+    const int tj = j / kG, hj = j - tj * kG;
+    if (tj >= ntok) continue;
+    float o8[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) o8[nb] = st.acc[nb][v];
+    store8(a.o + (((size_t)t0 + i0 + tj) * kH + g * kG + hj) * kHeadDim + 8 * col, o8,
+           bad_page ? NAN : 1.0f / lj);
+  }
+}
+
+template <int kG, int kTG>
+void launch_chunk_prefill(const ChunkArgs& c, int B, hipStream_t stream) {
+  const long long groups = (c.tiles + kTG - 1) / kTG;
+  const long long heads = kKvHeads / (kChunkWaves / kTG);
+  chunk_prefill_kernel<kG, kTG>
+      <<<dim3((unsigned)((long long)B * groups * heads)), kWave * kChunkWaves, 0, stream>>>(c);
+}
+
 // ------------------------------------------------------------ host side
 
 std::atomic<int> g_cu_count[64];
@@ -1777,9 +1967,21 @@ int launch_chunk(const float* q, const float* k_new, const float* v_new, const f
     st = check_launch("norm_rope_append_chunk_kernel");
     if (st != DAH_OK) return;
     c.tiles = (max_chunk + kTpt - 1) / kTpt;
-    chunk_attn_kernel<kG><<<dim3((unsigned)((long long)B * c.tiles)),
-                            kWave * kDecodeWavesPerBlock, 0, stream>>>(c);
-    st = check_launch("chunk_attn_kernel");
+    if (c.tiles >= kChunkPrefillMinTiles) {
+      // Tiles per workgroup: 2 or 4 for chunks of that many tiles (4 or 2
+      // KV heads per workgroup), else 8 of one head.
+      if (c.tiles <= 2)
+        launch_chunk_prefill<kG, 2>(c, B, stream);
+      else if (c.tiles <= 4)
+        launch_chunk_prefill<kG, 4>(c, B, stream);
+      else
+        launch_chunk_prefill<kG, 8>(c, B, stream);
+      st = check_launch("chunk_prefill_kernel");
+    } else {
+      chunk_attn_kernel<kG><<<dim3((unsigned)((long long)B * c.tiles)),
+                              kWave * kDecodeWavesPerBlock, 0, stream>>>(c);
+      st = check_launch("chunk_attn_kernel");
+    }
   });
   return st;
 }

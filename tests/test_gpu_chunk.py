@@ -207,22 +207,29 @@ def test_later_tokens_leave_earlier_outputs_bit_identical():
     assert not torch.equal(o2[12], o1[12]) and not torch.equal(o2[21], o1[21])
 
 
-def test_out_of_domain_sequences():
-    """seq_len < n_b or > max_seq_len: NaN outputs, nothing appended; an
-    empty chunk: nothing; other sequences unaffected."""
+@pytest.mark.parametrize("c,over", [(3, False), (20, True)])
+def test_out_of_domain_sequences(c, over):
+    """seq_len < n_b or > max_seq_len (and n_b > max_chunk): NaN outputs,
+    nothing appended; an empty chunk: nothing; other sequences unaffected.
+    Chunks of 3 tokens take the one-tile kernel, of 20 the shared-page one
+    (10 tiles in two workgroups per KV head)."""
     import torch
-    lens_old, chunks = [20, 20, 20, 20], [3, 3, 0, 3]
+    lens_old = [20, 20, 20, 20] + ([20] if over else [])
+    chunks = [c, c, 0, c] + ([c + 4] if over else [])
     t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, chunks, 16, "bf16", 13, "cuda",
-                                                 pool_pages=16)
-    t["seq_lens"][1] = 2           # cannot hold its 3-token chunk
-    t["seq_lens"][3] = 60          # past max_seq_len = 23 below
+                                                 pool_pages=32)
+    max_seq_len = 20 + c
+    t["seq_lens"][1] = 2                    # cannot hold its chunk
+    t["seq_lens"][3] = max_seq_len + 37     # past max_seq_len
     k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
     dah = _dah()
     q_out, o = dah.chunk_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
-                                   t["cu_tokens"], 3, 23)
+                                   t["cu_tokens"], c, max_seq_len)
     torch.cuda.synchronize()
-    assert torch.isfinite(o[0:3]).all()
-    assert torch.isnan(o[3:6]).all() and torch.isnan(o[6:9]).all()
+    assert torch.isfinite(o[0:c]).all()
+    assert torch.isnan(o[c:2 * c]).all() and torch.isnan(o[2 * c:3 * c]).all()
+    if over:   # sequence 4 holds c + 4 > max_chunk tokens: all of them NaN
+        assert torch.isnan(o[3 * c:]).all() and o.shape[0] == 4 * c + 4
     changed = (t["k_pool"] != k0).any(dim=3) | (t["v_pool"] != v0).any(dim=3)
-    assert int(changed.sum()) == 3 * 8       # sequence 0's three slots, 8 heads each
+    assert int(changed.sum()) == c * 8       # sequence 0's slots, 8 heads each
