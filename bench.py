@@ -5,7 +5,9 @@
 A step is one pass of the whole hot path over the batch: one call of
 decode_attn_step (q/k RMSNorm, RoPE, cache append and split-S decodeGQA, in
 one kernel launch when one split suffices, plus the log-sum-exp combine
-otherwise).  HIP events recorded on the launch stream bracket every step.
+otherwise) per layer of the workload -- one for every workload but
+stack28_b128, whose step runs its 28 layers, each with its own cache and
+gains.  HIP events recorded on the launch stream bracket every layer's call.
 Inputs are synthetic, seeded and resident in HBM before timing starts.
 
 The JSON line reports
@@ -263,48 +265,57 @@ def main():
     import decode_attention_head_amd as dah
 
     w = W.WORKLOADS[args.workload]
-    if w.num_layers != 1:
-        sys.exit(f"{w.name} has {w.num_layers} layers; the bench times one-layer workloads")
+    nl = w.num_layers
+    if nl > 1 and (args.block or args.layer or args.chunk):
+        sys.exit("--block, --layer and --chunk time one-layer workloads")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     seq_lens = W.make_seq_lens(w)
     table, num_pages = W.make_block_table(w, seq_lens)
-    t = W.make_layer(w, 0, dev, table=table, num_pages=num_pages, seq_lens=seq_lens)
+    layers = [W.make_layer(w, layer, dev, table=table, num_pages=num_pages, seq_lens=seq_lens)
+              for layer in range(nl)]
+    t = layers[0]
     B = w.batch
     L = int(seq_lens.max())
     H = w.num_heads
     plan = dah.plan_decode(B, L, args.num_splits, num_heads=H, cache_dtype=w.cache_dtype)
     ws_bytes = dah.workspace_bytes(B, L, args.num_splits, num_heads=H, cache_dtype=w.cache_dtype)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    q_out = torch.empty_like(t["q"])
+    q_outs = [torch.empty_like(t["q"]) for _ in range(nl)]
+    q_out = q_outs[0]
     o = torch.empty_like(t["q"])
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
-                             t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L,
-                             rope_theta=w.rope_theta, num_splits=args.num_splits, q_out=q_out,
-                             o=o, workspace=ws)
+    def step(layer):
+        tl = layers[layer]
+        dah.decode_attn_step(tl["q"], tl["k_new"], tl["v_new"], tl["q_gain"], tl["k_gain"],
+                             tl["k_pool"], tl["v_pool"], tl["block_table"], tl["seq_lens"], L,
+                             rope_theta=w.rope_theta, num_splits=args.num_splits,
+                             q_out=q_outs[layer], o=o, workspace=ws)
 
-    def decode():
-        dah.paged_decode_gqa(q_out, t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L,
-                             num_splits=args.num_splits, o=o, workspace=ws)
+    def decode(layer):
+        tl = layers[layer]
+        dah.paged_decode_gqa(q_outs[layer], tl["k_pool"], tl["v_pool"], tl["block_table"],
+                             tl["seq_lens"], L, num_splits=args.num_splits, o=o, workspace=ws)
 
     run = decode if args.decode_only else step
     if args.decode_only:
-        step()
+        for layer in range(nl):
+            step(layer)
     for _ in range(args.warmup):
-        run()
+        for layer in range(nl):
+            run(layer)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nl)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nl)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
-        run()
-        ends[i].record(stream)
+        for layer in range(nl):
+            starts[i * nl + layer].record(stream)
+            run(layer)
+            ends[i * nl + layer].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
@@ -339,8 +350,8 @@ def main():
             best = max(best, 10 * src.numel() / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9)
         probe_gbs = round(best, 1)
 
-    kv_bytes = W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)
-    gbs = kv_bytes / (ms_step * 1e-3) / 1e9
+    kv_bytes = W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)   # per layer
+    gbs = nl * kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (launch_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name) if (args.num_splits == 0 and not args.decode_only) else None
 
@@ -371,10 +382,12 @@ def main():
             "seq_len": "fixed 2048" if w.name.startswith("b256_s2048") else f"max {L}",
             "heads": f"{H} q / 8 kv, D=128, page 16",
             "rope_theta": w.rope_theta,
-            "kv_bytes_per_step": kv_bytes,
+            "layers": nl,
+            "kv_bytes_per_step": nl * kv_bytes,
             "plan": plan["mode"],
             "workgroups": plan["workgroups"],
-            "step": "paged_decode_gqa" if args.decode_only else "decode_attn_step",
+            "step": ("paged_decode_gqa" if args.decode_only else "decode_attn_step") +
+                    (f" x {nl} layers" if nl > 1 else ""),
         },
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(B / (ms_step * 1e-3), 1),
