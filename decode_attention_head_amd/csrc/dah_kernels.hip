@@ -1656,41 +1656,145 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void chunk_attn_kerne
   }
 }
 
+// The weighted V sum of the shared-page kernel, transposed: D = V^T W^T with
+// rows = dims and columns = the wave's 16 score columns, on
+// v_mfma_f32_16x16x32_bf16 (lane (r, c): A row c / B column c, k 8r .. 8r+7;
+// D rows 4r + v, column c), so that every lane keeps its own column's
+// accumulators and the rescale needs no other lane.  The 32 contraction
+// slots of lane row r are the page positions whose scores the lane holds
+// (4e + r, e = 0..3) twice over: for the two pages of a step (one product
+// per bfloat16 term of the weights), or, with one page per step, for the
+// two terms.  A (16 dims x those positions of V) comes straight from the
+// staged page with ds_read_b64_tr_b16, whose result in lane i of each
+// 16-lane group is element i mod 4 of the 8-byte pieces at the addresses of
+// lanes i/4 + {0, 4, 8, 12} of the group: lane (r, j) points at position
+// 4 (j / 4) + r, dims 16 nb + 4 (j mod 4) .. +3, which makes lane (r, c)
+// hold V[4e + r][16 nb + c], e = 0..3.  (The 16x16x16 form would take the
+// same matrix-core cycles per instruction for half the work.)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* LdsS16x4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct PrefillState {
+  float m, l;      // per column (m equal across rows; l the lane's share)
+  f32x4 acc[8];    // acc[nb][v]: dim 16 nb + 4 r + v of column c
+};
+
+// The V stage's swizzle: 16-byte piece q of position P sits in slot
+// q ^ (2 vswz(P)), so that the transpose reads of one instruction (8
+// positions x 2 pieces per 32 lanes) fall on distinct banks.
+__device__ __forceinline__ int vswz(int P) { return (P >> 2) + 4 * (P & 1); }
+
+__device__ __forceinline__ u32x2 read_v_tr(const char* base, int off) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4)(const_cast<char*>(base) + off)));
+}
+
+// One step of kP pages (1 or 2) of the shared-page kernel: K[j] holds page
+// j's K tile, vpage[j] its staged V (vaddr: this lane's transpose-read
+// offsets).  kMasked: column c sees only the positions of page j below
+// climit[j] (per lane; 0 = none of the page); the stage holds zeros for
+// positions past the sequence, so V needs no clearing.
+template <int kP, bool kMasked>
+__device__ __forceinline__ void attend_step_prefill(const KTileMfma (&K)[kP],
+                                                    const char* const (&vpage)[kP],
+                                                    const int (&vaddr)[8],
+                                                    const u32x4 (&qb)[4][3], PrefillState& st,
+                                                    int lane, const int (&climit)[kP]) {
+  const int r = lane >> 4;
+  f32x4 s[kP];
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    s[j] = page_scores(K[j], qb);
+    if (kMasked) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[j][v] = 4 * v + r < climit[j] ? s[j][v] : -INFINITY;
+    }
+  }
+  float pmax = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+  if constexpr (kP == 2) pmax = fmaxf(pmax, fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  const float pm = max_over_rows(pmax);
+  const bool move = pm > st.m + kMaxLag;
+  if (__builtin_amdgcn_ballot_w64(move) != 0) {
+    const float mn = move ? pm : st.m;
+    const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) st.acc[nb] *= alpha;
+  }
+  const float mu = st.m == -INFINITY ? 0.0f : st.m;
+  uint32_t hw[kP][2], lw[kP][2];
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    float p[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[j][v] - mu);
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+    hw[j][0] = pack_bf16x2(p[0], p[1]);
+    hw[j][1] = pack_bf16x2(p[2], p[3]);
+    lw[j][0] = pack_bf16x2(p[0] - bf16_lo(hw[j][0]), p[1] - bf16_hi(hw[j][0]));
+    lw[j][1] = pack_bf16x2(p[2] - bf16_lo(hw[j][1]), p[3] - bf16_hi(hw[j][1]));
+  }
+  if constexpr (kP == 2) {
+    const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{hw[0][0], hw[0][1], hw[1][0], hw[1][1]});
+    const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{lw[0][0], lw[0][1], lw[1][0], lw[1][1]});
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const u32x2 t0 = read_v_tr(vpage[0], vaddr[nb]);
+      const u32x2 t1 = read_v_tr(vpage[1], vaddr[nb]);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{t0[0], t0[1], t1[0], t1[1]});
+      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, st.acc[nb], 0, 0, 0);
+      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, st.acc[nb], 0, 0, 0);
+    }
+  } else {
+    const bf16x8 bw = __builtin_bit_cast(bf16x8, u32x4{hw[0][0], hw[0][1], lw[0][0], lw[0][1]});
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const u32x2 t0 = read_v_tr(vpage[0], vaddr[nb]);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{t0[0], t0[1], t0[0], t0[1]});
+      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, st.acc[nb], 0, 0, 0);
+    }
+  }
+}
+
 // Chunks of several tiles (prefill, longer verification): the tiles of one
 // KV head share each K/V page through LDS.  A workgroup of 8 waves takes one
 // sequence, kHG = 8 / kTG KV heads and kTG consecutive token tiles, one
 // (head, tile) per wave -- 8 tiles of one head for long chunks, 2 tiles of 4
-// heads for chunks of two tiles, so that every wave has work.  Per page the
-// 512 threads load the kHG heads' K and V tiles (4 KB each, 16 bytes per
-// thread and head, 8 / kHG pages ahead in registers: always 8 pieces in
-// flight) and write them to one of two LDS stages -- K with its 16-byte
-// pieces XOR-swizzled by position, so that the score product's reads (16
-// positions at one dim offset) fall on distinct banks; each wave then reads
-// its register tiles from LDS and attends as chunk_attn_kernel does.  The
-// cache is read once per kTG tiles instead of once per tile, and the
-// workgroups of one KV head (for kTG = 8) are consecutive modulo 8, which
-// keeps them on one XCD, where they share the pages through L2.
+// heads for chunks of two tiles, so that every wave has work.  Pages go in
+// steps of kP (2, or 1 with 4 heads): per step the 512 threads load the
+// heads' K and V tiles of the step's pages (16 bytes per thread, page and
+// head, 8 pieces in flight per thread) and write them to one of two LDS
+// stages -- K with its 16-byte pieces XOR-swizzled by position, so that the
+// score product's reads (16 positions at one dim offset) fall on distinct
+// banks, V swizzled for the transpose reads (vswz) and zero past the
+// sequence (or past the last page); each wave then scores the step's pages
+// as chunk_attn_kernel does and sums V with attend_step_prefill.  The cache
+// is read once per kTG tiles, and the workgroups of one KV head (for
+// kTG = 8) are consecutive modulo 8, which keeps them on one XCD, where they
+// share the pages through L2.
 
 constexpr int kChunkWaves = kDecodeWavesPerBlock;  // (head, tile) pairs per workgroup
 constexpr int kChunkRing = 8;                      // 16-byte pieces in flight per thread
-#ifndef DAH_CHUNK_PREFILL_MIN_TILES
-#define DAH_CHUNK_PREFILL_MIN_TILES 2
-#endif
-constexpr int kChunkPrefillMinTiles = DAH_CHUNK_PREFILL_MIN_TILES;  // from this many tiles on
+constexpr int kChunkPrefillMinTiles = 2;           // chunks of this many tiles share pages
 
 template <int kG, int kTG>
 __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(ChunkArgs a) {
   constexpr int kH = kG * kKvHeads;
   constexpr int kTpt = 16 / kG;  // tokens per tile
   constexpr int kHG = kChunkWaves / kTG;   // KV heads per workgroup
-  constexpr int kDepth = kChunkRing / kHG; // pages in flight
+  constexpr int kP = kHG == 4 ? 1 : 2;     // pages per step
+  constexpr int kDepth = kChunkRing / (kHG * kP);  // steps in flight
   using TileV = Tile<DAH_BF16>;
   constexpr int kTileBytes = (int)TileV::kTileBytes;
-  constexpr int kHeadBytes = 2 * kTileBytes;  // K and V of one head in a stage
+  constexpr int kHeadBytes = 2 * kTileBytes;  // K and V of one head and page in a stage
+  constexpr int kPageBytes = kHG * kHeadBytes;
   static_assert(kHG * kTG == kChunkWaves && kKvHeads % kHG == 0, "heads x tiles = 8 waves");
   static_assert(kWave * kChunkWaves * 16 == kHeadBytes, "one 16-byte piece per thread and head");
   static_assert(kDepth >= 2 && kDepth % 2 == 0, "stages alternate within the unrolled ring");
-  __shared__ __attribute__((aligned(16))) char stage[2][kHG * kHeadBytes];  // [stage][head][K|V]
+  __shared__ __attribute__((aligned(16))) char stage[2][kP * kPageBytes];  // [stage][page][head][K|V]
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1744,24 +1848,36 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   const ConstI32 bt = (ConstI32)(a.block_table + (size_t)b * a.max_pages_per_seq);
   const int64_t page_bytes = (int64_t)kKvHeads * kTileBytes;
   // This thread's 16-byte piece of every page and head: K pieces for threads
-  // 0..255, V pieces for 256..511; its place in the stage (K swizzled).
+  // 0..255, V pieces for 256..511; its place in the stage (K and V swizzled).
   const int kv = tid >> 8, piece = tid & 255;
   const char* src = (kv ? a.v_cache : a.k_cache) + (int64_t)gh * kHG * kTileBytes + 16 * piece;
   const int ppos = piece >> 4, pc = piece & 15;
-  const int dst = kv ? kTileBytes + 16 * piece : 256 * ppos + 16 * (pc ^ ppos);
+  const int dst = kv ? kTileBytes + 256 * ppos + 16 * (pc ^ (2 * vswz(ppos)))
+                     : 256 * ppos + 16 * (pc ^ ppos);
   bool bad_page = false;
-  auto fetch = [&](u32x4 (&out)[kHG], int p) {
-    const int id = bt[p];
-    const bool ok = id >= 0 && id < a.num_pages;
-    bad_page |= !ok && p <= wave_last;
-    const char* at = src + (int64_t)(ok ? id : 0) * page_bytes;
+  // The pieces of step s's pages (zeros for pages past `last`, which are not read).
+  auto fetch = [&](u32x4 (&out)[kP][kHG], int s) {
 #pragma unroll
-    for (int h = 0; h < kHG; ++h) out[h] = *reinterpret_cast<const u32x4*>(at + h * kTileBytes);
+    for (int j = 0; j < kP; ++j) {
+      const int p = kP * s + j;
+      if (p <= last) {
+        const int id = bt[p];
+        const bool ok = id >= 0 && id < a.num_pages;
+        bad_page |= !ok && p <= wave_last;
+        const char* at = src + (int64_t)(ok ? id : 0) * page_bytes;
+#pragma unroll
+        for (int h = 0; h < kHG; ++h) out[j][h] = *reinterpret_cast<const u32x4*>(at + h * kTileBytes);
+      } else {
+#pragma unroll
+        for (int h = 0; h < kHG; ++h) out[j][h] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
   };
-  u32x4 ring[kDepth][kHG];
+  const int steps = (last + kP) / kP;
+  u32x4 ring[kDepth][kP][kHG];
 #pragma unroll
   for (int i = 0; i < kDepth; ++i)
-    if (i <= last) fetch(ring[i], i);
+    if (i < steps) fetch(ring[i], i);
 
   float qv[4][8];
 #pragma unroll
@@ -1780,40 +1896,66 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
 #pragma unroll
       for (int t = 0; t < 3; ++t) qb[kk][t] = u32x4{0u, 0u, 0u, 0u};
   }
-  MfmaState st;
+  PrefillState st;
   st.m = -INFINITY;
   st.l = 0.0f;
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int kpos = 4 * (col & 3) + (col >> 2);  // sigma(col): the score product's K row
-  for (int p0 = 0; p0 <= last; p0 += kDepth) {
+  int kaddr[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kaddr[kk] = hw * kHeadBytes + 256 * kpos + 16 * ((row + 4 * kk) ^ kpos);
+  // Transpose-read offsets of V within a stage page: lane (row, col) points
+  // at position 4 (col / 4) + row, dims 16 nb + 4 (col mod 4) of its head.
+  int vaddr[8];
+  {
+    const int P = 4 * (col >> 2) + row;
+    const int base = hw * kHeadBytes + kTileBytes + 256 * P + 16 * ((col & 3) >> 1) + 8 * (col & 1);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) vaddr[nb] = base + 32 * (nb ^ vswz(P));
+  }
+
+  for (int s0 = 0; s0 < steps; s0 += kDepth) {
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) {
-      const int p = p0 + i;
-      if (p <= last) {
-        // Stage i & 1 was last read two pages ago, before the previous
-        // barrier.
+      const int s = s0 + i;
+      if (s < steps) {
+        // Stage i & 1 was last read two steps ago, before the previous
+        // barrier.  V rows past the sequence (never written) are staged as
+        // zeros.
 #pragma unroll
-        for (int h = 0; h < kHG; ++h)
-          *reinterpret_cast<u32x4*>(&stage[i & 1][h * kHeadBytes + dst]) = ring[i][h];
+        for (int j = 0; j < kP; ++j) {
+          const bool past = kv && kPage * (kP * s + j) + ppos >= seq_len;
+#pragma unroll
+          for (int h = 0; h < kHG; ++h)
+            *reinterpret_cast<u32x4*>(&stage[i & 1][j * kPageBytes + h * kHeadBytes + dst]) =
+                past ? u32x4{0u, 0u, 0u, 0u} : ring[i][j][h];
+        }
         __syncthreads();
-        if (p + kDepth <= last) fetch(ring[i], p + kDepth);
-        if (p <= wave_last) {
-          const char* sk = &stage[i & 1][hw * kHeadBytes];
-          KTileMfma K;
+        if (s + kDepth < steps) fetch(ring[i], s + kDepth);
+        const int p0 = kP * s;
+        if (p0 <= wave_last) {
+          KTileMfma K[kP];
+          const char* vpage[kP];
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            K.w[kk] = *reinterpret_cast<const u32x4*>(sk + 256 * kpos + 16 * ((row + 4 * kk) ^ kpos));
-          TileV V;
+          for (int j = 0; j < kP; ++j) {
+            const char* sp = &stage[i & 1][j * kPageBytes];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            V.w[j] = *reinterpret_cast<const u32x4*>(sk + kTileBytes + 16 * (lane + kWave * j));
-          if (p < first_masked) {
-            attend_page_mfma<false>(K, V, qb, st, lane, kPage);
+            for (int kk = 0; kk < 4; ++kk) K[j].w[kk] = *reinterpret_cast<const u32x4*>(sp + kaddr[kk]);
+            vpage[j] = sp;
+          }
+          if (p0 + kP - 1 < first_masked && p0 + kP - 1 <= wave_last) {
+            const int cl[kP] = {};
+            attend_step_prefill<kP, false>(K, vpage, vaddr, qb, st, lane, cl);
           } else {
-            attend_page_mfma<true, true>(K, V, qb, st, lane, pmax - kPage * p + 1,
-                                         climit_pos - kPage * p + 1);
+            int cl[kP];
+#pragma unroll
+            for (int j = 0; j < kP; ++j) {
+              const int p = p0 + j;
+              cl[j] = p > wave_last ? 0 : p < first_masked ? kPage : climit_pos - kPage * p + 1;
+            }
+            attend_step_prefill<kP, true>(K, vpage, vaddr, qb, st, lane, cl);
           }
         }
       }
@@ -1821,21 +1963,19 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   }
   if (!live) return;
 
+  // Column col = (token ti, head hh): its sum over the four rows, then dims
+  // 16 nb + 4 row .. +3 of its output row from this lane.
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  if (ti >= ntok) return;
+  const float scale = bad_page ? NAN : 1.0f / l;
+  float* orow = a.o + (((size_t)t0 + i0 + ti) * kH + g * kG + hh) * kHeadDim + 4 * row;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int j = 4 * row + v;   // accumulator row: column j = (token j / G, head j % G)
-    const float lj = __shfl(l, j);
-    const int tj = j / kG, hj = j - tj * kG;
-    if (tj >= ntok) continue;
-    float o8[8];
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) o8[nb] = st.acc[nb][v];
-    store8(a.o + (((size_t)t0 + i0 + tj) * kH + g * kG + hj) * kHeadDim + 8 * col, o8,
-           bad_page ? NAN : 1.0f / lj);
-  }
+  for (int nb = 0; nb < 8; ++nb)
+    *reinterpret_cast<float4*>(orow + 16 * nb) =
+        make_float4(st.acc[nb][0] * scale, st.acc[nb][1] * scale, st.acc[nb][2] * scale,
+                    st.acc[nb][3] * scale);
 }
 
 template <int kG, int kTG>

@@ -438,13 +438,6 @@ int pick_lds(const LinearArgs& a) {
 // 4096 x 1024, 1024 x 2048 (graph-replayed launch times): this rule picks
 // the fastest shape or one within 3% of it in every case.
 LinearConfig pick_config(const LinearArgs& a) {
-#if defined(DAH_LINEAR_CONFIG)
-  (void)a;
-  return LinearConfig{0, DAH_LINEAR_CONFIG};
-#elif defined(DAH_LINEAR_LDS)
-  (void)a;
-  return LinearConfig{DAH_LINEAR_LDS, 0, 0, 0};
-#else
   const int lds = pick_lds(a);
   if (lds != 0) return {lds, 0, 0, 0};
   if (a.T > 16) {
@@ -453,7 +446,6 @@ LinearConfig pick_config(const LinearArgs& a) {
       if (m_tiles * (a.N / (16 * nb)) >= kLinMinGroups) return {0, 2, nb, 1};
   }
   return {0, 1, 1, 1};
-#endif
 }
 
 template <int kBM, int kBN, int kWM, int kWN, int kWK, int kKS, int kDepth>
@@ -470,15 +462,11 @@ int launch_lds(const LinearArgs& a, hipStream_t stream) {
 
 int launch_lds_shape(int id, const LinearArgs& a, hipStream_t stream) {
   switch (id) {
-#ifdef DAH_LINEAR_LDS_SHAPES
-    DAH_LINEAR_LDS_SHAPES
-#else
     case 1: return launch_lds<64, 128, 2, 2, 1, 2, 1>(a, stream);
     case 2: return launch_lds<64, 64, 2, 2, 1, 2, 1>(a, stream);
     case 3: return launch_lds<32, 64, 1, 2, 2, 1, 1>(a, stream);
     case 4: return launch_lds<32, 32, 1, 1, 4, 1, 1>(a, stream);
     case 5: return launch_lds<32, 32, 1, 1, 4, 2, 2>(a, stream);
-#endif
     default: return dah::set_error(DAH_ERR_HIP, "linear: no LDS tile shape %d", id);
   }
 }
@@ -503,16 +491,6 @@ int launch_linear(LinearArgs& a, hipStream_t stream) {
   DAH_LIN_CASE(2, 1, 1)
   DAH_LIN_CASE(2, 2, 1)
   DAH_LIN_CASE(2, 4, 1)
-#ifdef DAH_LINEAR_CONFIG
-  DAH_LIN_CASE(1, 1, 2)
-  DAH_LIN_CASE(1, 2, 2)
-  DAH_LIN_CASE(1, 4, 2)
-  DAH_LIN_CASE(2, 1, 2)
-  DAH_LIN_CASE(2, 2, 2)
-  DAH_LIN_CASE(2, 4, 2)
-  DAH_LIN_CASE(2, 2, 4)
-  DAH_LIN_CASE(1, 4, 4)
-#endif
   return dah::set_error(DAH_ERR_HIP, "linear: no kernel for tile %d/%d/%d", c.mb, c.nb, c.mw);
 #undef DAH_LIN_CASE
   }
