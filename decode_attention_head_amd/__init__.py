@@ -333,7 +333,7 @@ def chunk_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_tab
     b's chunk (rows cu_tokens[b] .. cu_tokens[b+1]-1) sits at position
     seq_lens[b] - n_b + i; norm, RoPE, append, then causal decodeGQA.
     q [N,H,128], k_new/v_new [N,8,128] float32, cu_tokens int32 [B+1];
-    bfloat16 cache.  Returns (q_out, o), both [N,H,128] float32."""
+    bfloat16 or float32 cache.  Returns (q_out, o), both [N,H,128] float32."""
     torch = _torch()
     N, H = q.shape[0], _heads(q)
     B = seq_lens.shape[0]

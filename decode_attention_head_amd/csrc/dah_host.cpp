@@ -183,9 +183,6 @@ int validate_chunk(const void* q, const void* k_new, const void* v_new, const vo
                            num_heads, q_out);
   if (st != DAH_OK) return st;
   if (!cu_tokens || !o) return set_error(DAH_ERR_NULL, "chunk_attn_step: cu_tokens or o is NULL");
-  if (cache_dtype != DAH_BF16)
-    return set_error(DAH_ERR_DTYPE, "chunk_attn_step: needs a bfloat16 cache (the matrix-core "
-                                    "kernel)");
   if (total_tokens < 1) return set_error(DAH_ERR_SHAPE, "total_tokens = %d, need >= 1", total_tokens);
   if (max_chunk < 1 || max_chunk > total_tokens)
     return set_error(DAH_ERR_SHAPE, "max_chunk = %d, need 1 <= max_chunk <= total_tokens (%d)",

@@ -407,16 +407,18 @@ __device__ void step_q_out_only(const DecodeArgs& a, int b, int seq_len, int g, 
 // (write_q: this range also writes q_out), and the range holding the
 // sequence's last page norms and rotates the new key, folds the new token in
 // from registers and stores the new key and value in the cache.
+// qb: the row block of q and o (the sequence b for a decode; a chunk
+// token, attending over its own prefix of sequence b's pages, for chunks).
 template <int kDtype, bool kStep, int kG>
-__device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int seq_len, int npages,
-                                             int p0, int p1, bool write_q, bool to_o,
+__device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb, int seq_len,
+                                             int npages, int p0, int p1, bool write_q, bool to_o,
                                              size_t part_base, int part_stride, int g, int lane,
                                              StepStash<kG>& stash) {
   constexpr int kH = kG * kKvHeads;
   const int wave = g;
   const int row = lane >> 4;
   const int col = lane & 15;
-  const size_t qrow0 = (size_t)b * kH + g * kG;  // first query head row of this KV head
+  const size_t qrow0 = (size_t)qb * kH + g * kG;  // first query head row of this KV head
 
   // The block table is read-only for the whole launch: reading it through the
   // constant address space makes every (uniform) read a scalar load, counted
@@ -1099,7 +1101,7 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
                                  part_base, a.splits, g, lane, stash);
   } else {
     __shared__ StepStash<kG> stash;
-    decode_range<kDtype, kStep, kG>(a, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
+    decode_range<kDtype, kStep, kG>(a, b, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
                                     part_base, a.splits, g, lane, stash);
   }
 }
@@ -1189,7 +1191,7 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
       decode_range_mfma<kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
                                    (size_t)(b + k) * kH, 1, g, lane_i, stash);
     else
-      decode_range<kDtype, kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
+      decode_range<kDtype, kStep, kG>(a, b, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
                                       (size_t)(b + k) * kH, 1, g, lane_i, stash);
     s = seg_end;
     if (s >= e) break;
@@ -1656,6 +1658,43 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void chunk_attn_kerne
   }
 }
 
+// Chunks with a float32 cache (strict-parity runs): every chunk token is a
+// decode over positions 0 .. its own on the VALU decode path -- one
+// workgroup (8 waves = 8 KV heads) per (sequence, chunk token), each reading
+// its own prefix of the sequence's pages, so the cache is read once per
+// token: meant for verification-sized chunks.
+template <int kG>
+__global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void chunk_valu_kernel(
+    DecodeArgs a, const int32_t* __restrict__ cu_tokens, int total, int max_chunk) {
+  constexpr int kH = kG * kKvHeads;
+  __shared__ StepStash<kG> stash;  // decode_range's signature; unused without the step
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head
+  const int b = blockIdx.x / max_chunk;
+  const int i = blockIdx.x - b * max_chunk;
+  const int t0 = min(max(cu_tokens[b], 0), total);
+  const int t1 = min(max(cu_tokens[b + 1], t0), total);
+  const int n = t1 - t0;
+  if (i >= n) return;
+  const int seq_len = a.seq_lens[b];
+  if (n > max_chunk || seq_len < n || seq_len > a.max_seq_len) {
+    // Outside the preconditions: NaN for this token (and, from token 0, for
+    // tokens past max_chunk), nothing read from the cache.
+    const int last = i == 0 ? n : i + 1;
+    for (int j = i; j < last; ++j) {
+      if (i == 0 && j >= 1 && j < max_chunk) continue;  // owned by another workgroup
+      for (int h = 0; h < kG; ++h)
+        reinterpret_cast<float2*>(a.o + (((size_t)t0 + j) * kH + g * kG + h) * kHeadDim)[lane] =
+            make_float2(NAN, NAN);
+    }
+    return;
+  }
+  const int len = seq_len - n + i + 1;  // positions 0 .. the token's own
+  const int npages = (len + kPage - 1) / kPage;
+  decode_range<DAH_F32, false, kG>(a, b, t0 + i, len, npages, 0, npages, false, true, 0, 0, g,
+                                   lane, stash);
+}
+
 // The weighted V sum of the shared-page kernel, transposed: D = V^T W^T with
 // rows = dims and columns = the wave's 16 score columns, on
 // v_mfma_f32_16x16x32_bf16 (lane (r, c): A row c / B column c, k 8r .. 8r+7;
@@ -2064,7 +2103,8 @@ int launch_append(const float* q, const float* k_new, const float* v_new, const 
 // causal attention of the chunks (two launches).
 int launch_chunk(const float* q, const float* k_new, const float* v_new, const float* q_gain,
                  const float* k_gain, float eps, float rope_theta, void* k_cache, void* v_cache,
-                 int64_t num_pages, const int32_t* block_table, int max_pages_per_seq,
+                 int cache_dtype, int64_t num_pages, const int32_t* block_table,
+                 int max_pages_per_seq,
                  const int32_t* seq_lens, const int32_t* cu_tokens, int B, int total,
                  int max_chunk, int max_seq_len, int num_heads, float* q_out, float* o,
                  hipStream_t stream) {
@@ -2098,6 +2138,35 @@ int launch_chunk(const float* q, const float* k_new, const float* v_new, const f
   c.max_seq_len = max_seq_len;
   c.o = o;
   int st = DAH_OK;
+  if (cache_dtype == DAH_F32) {
+    DecodeArgs d = {};
+    d.q = q_out;
+    d.k_cache = static_cast<const char*>(k_cache);
+    d.v_cache = static_cast<const char*>(v_cache);
+    d.num_pages = static_cast<int>(num_pages);
+    d.block_table = block_table;
+    d.max_pages_per_seq = max_pages_per_seq;
+    d.seq_lens = seq_lens;
+    d.B = B;
+    d.max_seq_len = max_seq_len;
+    d.splits = 1;
+    d.grid_splits = 1;
+    d.pages_per_split = max_pages_per_seq;
+    d.o = o;
+    with_group(num_heads, [&](auto grp) {
+      constexpr int kG = decltype(grp)::value;
+      norm_rope_append_chunk_kernel<DAH_F32, kG>
+          <<<dim3((unsigned)((long long)B * max_chunk)), 512, 0, stream>>>(a, cu_tokens, max_chunk,
+                                                                           total);
+      st = check_launch("norm_rope_append_chunk_kernel");
+      if (st != DAH_OK) return;
+      chunk_valu_kernel<kG><<<dim3((unsigned)((long long)B * max_chunk)),
+                              kWave * kDecodeWavesPerBlock, 0, stream>>>(d, cu_tokens, total,
+                                                                         max_chunk);
+      st = check_launch("chunk_valu_kernel");
+    });
+    return st;
+  }
   with_group(num_heads, [&](auto grp) {
     constexpr int kG = decltype(grp)::value;
     constexpr int kTpt = 16 / kG;
@@ -2364,7 +2433,7 @@ int chunk_attn_step(const float* q, const float* k_new, const float* v_new, cons
                                q_out, o);
   if (st != DAH_OK) return st;
   return launch_chunk(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
-                      num_pages, block_table, max_pages_per_seq, seq_lens, cu_tokens, B,
+                      cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, cu_tokens, B,
                       total_tokens, max_chunk, max_seq_len, num_heads, q_out, o,
                       static_cast<hipStream_t>(stream));
 }

@@ -280,10 +280,15 @@ size_t dah_workspace_bytes_ex(int B, int num_heads, int cache_dtype, int max_seq
  *   cu_tokens    [device] int32 [B+1], non-decreasing, cu_tokens[B] = total_tokens
  *   max_chunk    host bound on every n_b (1 .. total_tokens); the grids are sized by it
  *   max_seq_len  host bound on every seq_lens[b] (<= max_pages_per_seq * 16)
- *   num_heads    16, 32, 40 or 64; the cache must be DAH_BF16 (matrix-core kernel)
- *   other arguments as in decode_attn_step.
+ *   num_heads    16, 32, 40 or 64
+ *   other arguments as in decode_attn_step (cache DAH_BF16 or DAH_F32).
  *
- * Two launches (append, attention), no workspace.  A sequence with
+ * Two launches (append, attention), no workspace.  A bfloat16 cache runs on
+ * the matrix cores, each cached page read once per tile of 16/G tokens (or
+ * once per 8 such tiles, shared through LDS, for longer chunks); a float32
+ * cache runs every token as its own decode on the VALU path (each token
+ * reads its prefix: meant for verification-sized chunks and strict-parity
+ * runs).  A sequence with
  * seq_lens[b] < n_b, seq_lens[b] > max_seq_len or n_b > max_chunk gets NaN
  * outputs and no append; a page id outside the pool gives NaN for the tokens
  * that read it.

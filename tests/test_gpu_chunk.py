@@ -2,9 +2,11 @@
 within the chunk: chunked prefill and verification of drafted tokens),
 through the C ABI, against the oracle's chunk_step.
 
-The kernel reads a bfloat16 cache on the matrix cores (q as three bf16
+With a bfloat16 cache the kernels run on the matrix cores (q as three bf16
 terms, weights as two), so the gates are the bf16 ones: max abs error 2e-2,
-relative-to-max <= 1e-4, and q_out within 1e-5.  The appended keys must be
+relative-to-max <= 1e-4, and q_out within 1e-5.  A float32 cache runs every
+token as a VALU decode and gets the strict float32 gates: o and q_out within
+1e-5, appended keys within 1e-5 of the exact values.  The appended keys must be
 the round-to-nearest-even of the exact value (or its neighbour within float32
 error of a midpoint) and the values exact.
 
@@ -18,7 +20,7 @@ between the two oracle results.
 import numpy as np
 import pytest
 
-from dah_testlib import bf16_alternative, check_rounded, cuda_available, pool_to_numpy
+from dah_testlib import bf16_alternative, check_rounded, cuda_available, gates, pool_to_numpy
 from inputs import workloads as W
 from oracle import decode_attention as O
 
@@ -64,12 +66,13 @@ def _snapshot(t, table, seq_lens, cu, seqs):
         "v_new": t["v_new"].index_select(0, sel).cpu().numpy(),
         "q_gain": t["q_gain"].cpu().numpy(), "k_gain": t["k_gain"].cpu().numpy(),
         "tokens": tok,
+        "cache_dtype": "f32" if t["k_pool"].dtype == torch.float32 else "bf16",
     }
 
 
 def _oracle(s, theta=1e6, k_stored=None):
     return O.chunk_step(s["q"], s["k_new"], s["v_new"], s["q_gain"], s["k_gain"], s["k_pool"],
-                        s["v_pool"], s["block_table"], s["seq_lens"], s["cu"], "bf16", theta=theta,
+                        s["v_pool"], s["block_table"], s["seq_lens"], s["cu"], s["cache_dtype"], theta=theta,
                         k_stored=k_stored)
 
 
@@ -143,6 +146,29 @@ def test_small_chunks_every_token(H, theta):
            f"({nflag} near-midpoint keys)")
 
 
+@pytest.mark.parametrize("H", [16, 40, 64])
+def test_f32_cache_chunks_every_token(H):
+    """A float32 cache (every token a decode over its own prefix): the same
+    ragged chunks as above, against the oracle at the float32 gates."""
+    lens_old, chunks = [0, 3, 16, 30, 100, 9], [1, 4, 7, 16, 19, 33]
+    t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, chunks, H, "f32", 21 + H, "cuda",
+                                                 pool_pages=64)
+    seqs = list(range(len(chunks)))
+    snap = _snapshot(t, table, seq_lens, cu, seqs)
+    q_out, o = _run(t, cu, seq_lens, max(chunks))
+    ref = _oracle(snap)
+    e_q = float(np.max(np.abs(q_out.cpu().numpy() - ref["q_out"])))
+    assert e_q <= 1e-5, f"q_out {e_q:.3g}"
+    k_slot, v_slot = _slots(t, table, seq_lens, cu, seqs)
+    _, k_exact = O.norm_rope(snap["q"], snap["k_new"], snap["q_gain"], snap["k_gain"],
+                             np.array(ref["pos"]) + 1)
+    assert np.max(np.abs(k_slot - k_exact)) <= 1e-5
+    assert np.array_equal(v_slot, ref["v_slot"])
+    e_abs, e_rel = gates(o.cpu().numpy().astype(np.float64), ref["o"], None, 1e-5,
+                         label=f"f32 H={H}")
+    _print(f"[chunk f32] H={H}: q_out {e_q:.2e}  o {e_abs:.2e} rel {e_rel:.2e}")
+
+
 @pytest.mark.parametrize("name,lens_old,chunk,B,H", [
     ("verify", 2044, 4, 64, 16), ("verify", 2044, 4, 64, 64),
     ("prefill", 0, 1024, 4, 16), ("prefill_after_context", 3000, 512, 4, 40)])
@@ -207,16 +233,18 @@ def test_later_tokens_leave_earlier_outputs_bit_identical():
     assert not torch.equal(o2[12], o1[12]) and not torch.equal(o2[21], o1[21])
 
 
-@pytest.mark.parametrize("c,over", [(3, False), (20, True)])
-def test_out_of_domain_sequences(c, over):
+@pytest.mark.parametrize("c,over,dt", [(3, False, "bf16"), (20, True, "bf16"),
+                                       (3, False, "f32"), (20, True, "f32")])
+def test_out_of_domain_sequences(c, over, dt):
     """seq_len < n_b or > max_seq_len (and n_b > max_chunk): NaN outputs,
     nothing appended; an empty chunk: nothing; other sequences unaffected.
-    Chunks of 3 tokens take the one-tile kernel, of 20 the shared-page one
-    (10 tiles in two workgroups per KV head)."""
+    With a bfloat16 cache, chunks of 3 tokens take the one-tile kernel, of 20
+    the shared-page one (10 tiles in two workgroups per KV head); a float32
+    cache takes the per-token kernel."""
     import torch
     lens_old = [20, 20, 20, 20] + ([20] if over else [])
     chunks = [c, c, 0, c] + ([c + 4] if over else [])
-    t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, chunks, 16, "bf16", 13, "cuda",
+    t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, chunks, 16, dt, 13, "cuda",
                                                  pool_pages=32)
     max_seq_len = 20 + c
     t["seq_lens"][1] = 2                    # cannot hold its chunk
