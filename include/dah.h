@@ -17,7 +17,10 @@
  * positions).
  *
  * Fixed sizes (spec constants): 16 query heads, 8 KV heads, head dim 128,
- * page size 16.  Query head h reads KV head h / 2.
+ * page size 16.  Query head h reads KV head h / 2.  The *_ex calls (and
+ * chunk_attn_step, the projections and the layer) also take the family's
+ * other head counts -- 32, 40 or 64 query heads over the same 8 KV heads,
+ * query head h reading KV head h / (H / 8).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
