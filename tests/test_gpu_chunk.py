@@ -261,3 +261,53 @@ def test_out_of_domain_sequences(c, over, dt):
         assert torch.isnan(o[3 * c:]).all() and o.shape[0] == 4 * c + 4
     changed = (t["k_pool"] != k0).any(dim=3) | (t["v_pool"] != v0).any(dim=3)
     assert int(changed.sum()) == c * 8       # sequence 0's slots, 8 heads each
+
+
+@pytest.mark.parametrize("chunk,H,dt", [(4, 16, "bf16"), (16, 16, "bf16"), (64, 64, "bf16"),
+                                        (4, 40, "f32")])
+def test_chunk_under_graph_replay(chunk, H, dt):
+    """chunk_attn_step captured in one HIP graph -- the one-tile kernel, the
+    shared-page kernel with 4 heads and with 1 head per workgroup, and the
+    float32 path: every replay, with eager work and synchronisations between
+    replays, equals the eager result bit for bit.  The cache is restored
+    before each run, since the step appends to it."""
+    import torch
+    dah = _dah()
+    B = 8
+    lens_old = [100 + 37 * b for b in range(B)]
+    t, table, seq_lens, cu = W.make_chunk_inputs(lens_old, [chunk] * B, H, dt, 31, "cuda")
+    L = int(np.max(seq_lens))
+    q_out, o = torch.empty_like(t["q"]), torch.empty_like(t["q"])
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+
+    def step():
+        dah.chunk_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                            t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                            t["cu_tokens"], chunk, L, q_out=q_out, o=o)
+
+    def restore():
+        t["k_pool"].copy_(k0)
+        t["v_pool"].copy_(v0)
+
+    step()
+    torch.cuda.synchronize()
+    want_o, want_q, want_k = o.clone(), q_out.clone(), t["k_pool"].clone()
+    restore()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        restore()
+        o.zero_()
+        q_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, want_o), f"replay {i}: o differs"
+        assert torch.equal(q_out, want_q), f"replay {i}: q_out differs"
+        assert torch.equal(t["k_pool"], want_k), f"replay {i}: cache differs"
+        _ = (t["q"] * 2).sum().item()   # eager work between replays

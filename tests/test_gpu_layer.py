@@ -140,3 +140,50 @@ def test_layer_rejects_before_launching():
                                t["seq_lens"], 10_000, y=y)    # max_seq_len past the table
     torch.cuda.synchronize()
     assert bool((y == 7.0).all())
+
+
+@pytest.mark.parametrize("name", ["b256_s2048", "ragged_b32"])
+def test_layer_under_graph_replay(name):
+    """decoder_layer_step captured in one HIP graph (per-sequence plan at
+    B=256; fixed splits with the combine launch at B=32 ragged): every
+    replay, with eager work and synchronisations between replays, equals the
+    eager result bit for bit.  The cache is restored before each run."""
+    import torch
+    dah = _dah()
+    w, t, seq_lens, table, p = _layer_case(name, 16)
+    L = int(seq_lens.max())
+    weights = {n: p[n] for n in dah.LAYER_WEIGHTS}
+    inter = p["w_down"].shape[1]
+    ws = torch.empty(dah.layer_workspace_bytes(w.batch, w.hidden, inter, L), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty_like(p["x"])
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+
+    def layer():
+        dah.decoder_layer_step(p["x"], weights, t["k_pool"], t["v_pool"], t["block_table"],
+                               t["seq_lens"], L, y=y, workspace=ws)
+
+    def restore():
+        t["k_pool"].copy_(k0)
+        t["v_pool"].copy_(v0)
+
+    layer()
+    torch.cuda.synchronize()
+    want_y, want_k = y.clone(), t["k_pool"].clone()
+    restore()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            layer()
+    torch.cuda.synchronize()
+    for i in range(3):
+        restore()
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want_y), f"replay {i}: y differs"
+        assert torch.equal(t["k_pool"], want_k), f"replay {i}: cache differs"
+        _ = (p["x"] * 2).sum().item()   # eager work between replays
