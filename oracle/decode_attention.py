@@ -337,7 +337,7 @@ def rel_to_max_err(impl: np.ndarray, ref: np.ndarray) -> float:
 
 def chunk_step(q, k_new, v_new, q_gain, k_gain, k_pool, v_pool, block_table, seq_lens,
                cu_tokens, cache_dtype: str, eps: float = RMS_EPS, theta: float = ROPE_THETA,
-               batch_indices=None, k_stored=None):
+               batch_indices=None, k_stored=None, only=None):
     """Sequence b owns tokens cu_tokens[b] .. cu_tokens[b+1]-1 (n_b of them);
     seq_lens[b] counts the cache after the chunk, so token i of the chunk
     sits at position seq_lens[b] - n_b + i and attends to positions 0 .. that
@@ -352,7 +352,12 @@ def chunk_step(q, k_new, v_new, q_gain, k_gain, k_pool, v_pool, block_table, seq
     k_stored, if given ([n,8,128] over the same tokens), replaces the stored
     keys of the chunk: a caller that knows a key value lies within rounding
     error of a bf16 midpoint can evaluate the step with the other admissible
-    rounding."""
+    rounding.
+
+    only, if given ({b: chunk indices i}), evaluates o for those tokens
+    alone (for chunks too long to attend every token here): o and pos then
+    hold the selected tokens in order, q_out, k_slot and v_slot still every
+    token."""
     q = np.asarray(q)
     cu = np.asarray(cu_tokens, dtype=np.int64)
     idx = range(len(cu) - 1) if batch_indices is None else list(batch_indices)
@@ -381,11 +386,13 @@ def chunk_step(q, k_new, v_new, q_gain, k_gain, k_pool, v_pool, block_table, seq
             np.empty((0, NUM_KV_HEADS, HEAD_DIM))
         k_all = np.concatenate([k_old, k_slot], axis=0)
         v_all = np.concatenate([v_old, v_slot], axis=0)
-        for i in range(n):
+        chosen = range(n) if only is None else [int(i) for i in only.get(b, [])]
+        for i in chosen:
             p = old + i
             res["o"].append(decode_gqa_dense(q_out[i], k_all[:p + 1], v_all[:p + 1]))
+            res["pos"].append(p)
         res["q_out"].extend(q_out)
         res["k_slot"].extend(k_slot)
         res["v_slot"].extend(v_slot)
-        res["pos"].extend(pos.astype(np.int64))
-    return {key: np.stack(val) if val else np.zeros((0,)) for key, val in res.items()}
+    return {key: (np.array(val, dtype=np.int64) if key == "pos" else np.stack(val))
+            if val else np.zeros((0,)) for key, val in res.items()}

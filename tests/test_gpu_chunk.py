@@ -311,3 +311,47 @@ def test_chunk_under_graph_replay(chunk, H, dt):
         assert torch.equal(q_out, want_q), f"replay {i}: q_out differs"
         assert torch.equal(t["k_pool"], want_k), f"replay {i}: cache differs"
         _ = (t["q"] * 2).sum().item()   # eager work between replays
+
+
+@pytest.mark.parametrize("lens_old,chunk,B,H", [(0, 40960, 1, 16), (32768, 8192, 2, 64)])
+def test_domain_maximum_chunks(lens_old, chunk, B, H):
+    """The shape domain's largest chunks (Model Spec page, "At a glance": up
+    to 40,960 new tokens and 40,960 positions): a whole 40,960-token prefill,
+    and 8,192 tokens after 32,768 cached at 64 heads.  Every q_out against
+    the oracle; o at sampled tokens (first, page edges, middle, last), the
+    oracle evaluating those tokens alone, with the admissible-rounding
+    spread of the module docstring."""
+    import torch
+    rng = np.random.default_rng(chunk + H)
+    t, table, seq_lens, cu = W.make_chunk_inputs([lens_old] * B, [chunk] * B, H, "bf16",
+                                                 300 + H, "cuda")
+    seqs = list(range(B))
+    snap = _snapshot(t, table, seq_lens, cu, seqs)
+    q_out, o = _run(t, cu, seq_lens, chunk)
+    picks = sorted({0, 1, 15, 16, chunk // 2, chunk - 17, chunk - 2, chunk - 1} |
+                   {int(x) for x in rng.integers(0, chunk, 4)})
+    only = {b: picks for b in seqs}
+    ref = O.chunk_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"],
+                       snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
+                       snap["cu"], "bf16", only=only)
+    e_q = float(np.max(np.abs(q_out.cpu().numpy()[snap["tokens"]] - ref["q_out"])))
+    assert e_q <= 1e-5, f"q_out {e_q:.3g}"
+    _, k_exact = O.norm_rope(snap["q"], snap["k_new"], snap["q_gain"], snap["k_gain"],
+                             np.repeat(seq_lens[seqs] - chunk, chunk) + np.tile(np.arange(chunk), B)
+                             + 1)
+    _, k_alt, flagged = bf16_alternative(k_exact)
+    spread = np.zeros(len(ref["o"]))
+    if flagged.any():
+        alt = O.chunk_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"],
+                           snap["k_gain"], snap["k_pool"], snap["v_pool"], snap["block_table"],
+                           snap["seq_lens"], snap["cu"], "bf16", k_stored=k_alt, only=only)
+        spread = np.max(np.abs(alt["o"] - ref["o"]), axis=(1, 2))
+    rows = np.concatenate([int(cu[b]) + np.asarray(picks) for b in seqs])
+    o_gpu = o.cpu().numpy()[rows].astype(np.float64)
+    scale = float(np.max(np.abs(ref["o"])))
+    err = np.max(np.abs(o_gpu - ref["o"]), axis=(1, 2))
+    assert np.all(np.isfinite(o_gpu))
+    assert np.all(err <= 1e-4 * scale + spread), (err / scale)
+    assert float(np.max(err)) <= 2e-2
+    _print(f"[chunk max] B={B} n={chunk} H={H}: q_out {e_q:.2e}  o rel-to-max "
+           f"{float(np.max(err)) / scale:.2e} ({int(flagged.sum())} near-midpoint keys)")

@@ -164,3 +164,18 @@ def test_chunk_brute_force_50_digits():
             want = np.array([float(sum(e[s] * vs[s][d] for s in range(len(ks))) / tot)
                              for d in range(128)])
             assert np.max(np.abs(res["o"][i, h] - want)) <= 1e-13 * max(1.0, np.max(np.abs(want)))
+
+
+def test_token_subset_matches_the_full_evaluation():
+    """`only` evaluates o for chosen tokens: exactly the full step's rows for
+    them (same arithmetic), with q_out and the stored slots of every token."""
+    c = _case(9, [5, 0, 40], [7, 12, 3], "bf16")
+    full = _chunk(c, "bf16")
+    only = {0: [0, 6], 1: [11], 2: [1, 2]}
+    part = _chunk(c, "bf16", only=only)
+    rows = [0, 6, 7 + 11, 19 + 1, 19 + 2]
+    assert np.array_equal(part["o"], full["o"][rows])
+    assert np.array_equal(part["pos"], full["pos"][rows])
+    for key in ("q_out", "k_slot", "v_slot"):
+        assert np.array_equal(part[key], full[key])
+    assert list(part["pos"]) == [5, 11, 11, 41, 42]
