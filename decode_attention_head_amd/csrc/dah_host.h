@@ -48,7 +48,7 @@ int validate_append(const void* q, const void* k_new, const void* v_new, const v
                     int num_heads, const void* q_out);
 
 // chunk_attn_step: the append checks, plus cu_tokens, the token count, the
-// chunk bound, max_seq_len and a bfloat16 cache.
+// chunk bound and max_seq_len.
 int validate_chunk(const void* q, const void* k_new, const void* v_new, const void* q_gain,
                    const void* k_gain, float eps, float rope_theta, const void* k_cache,
                    const void* v_cache, int cache_dtype, int64_t num_pages,
@@ -63,5 +63,11 @@ int validate_decode(const void* q, const void* k_cache, const void* v_cache, int
                     int64_t num_pages, const void* block_table, int max_pages_per_seq,
                     const void* seq_lens, int B, int num_heads, int max_seq_len, int num_splits,
                     const void* o);
+
+// attn_qkv_proj, with the input row RMS-normed first (gain x_gain, eps) when
+// x_gain is not NULL -- the decoder layer's input_norm folded into the
+// product (dah_linear.hip).
+int qkv_proj(const float* x, const float* x_gain, float eps, const void* w_qkv, int T, int hidden,
+             int num_heads, float* q, float* k, float* v, void* stream);
 
 }  // namespace dah

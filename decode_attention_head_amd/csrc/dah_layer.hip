@@ -5,10 +5,11 @@
 //   append, decodeGQA); x1 = x + o_proj(o); h2 = post_attn_norm(x1);
 //   y = x1 + down(silu(gate) * up),  [gate | up] = gate_up(h2)
 //
-// The products run on the matrix cores (dah_linear.hip; the residual adds
-// are folded into the stores of o_proj and down), the attention step in
-// dah_kernels.hip; this file holds the two elementwise nodes (the hidden-size
-// RMSNorm and the SwiGLU activation) and the composition.
+// The products run on the matrix cores (dah_linear.hip), which also take the
+// hidden-size RMSNorms on their input rows and the residual adds in their
+// stores; the attention step runs in dah_kernels.hip.  This file holds the
+// composition, the SwiGLU activation's kernel and the RMSNorm as a
+// standalone call (dah_rmsnorm).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -83,7 +84,7 @@ size_t round_up(size_t n) { return (n + 255) / 256 * 256; }
 
 // Workspace of the layer: intermediates, then the attention's own workspace.
 struct LayerBuffers {
-  size_t h, q, k, v, q_out, o, x1, gu, act, attn, total;
+  size_t q, k, v, q_out, o, x1, gu, act, attn, total;
 };
 
 LayerBuffers layer_buffers(int B, int hidden, int inter, int num_heads, size_t attn_ws) {
@@ -95,7 +96,6 @@ LayerBuffers layer_buffers(int B, int hidden, int inter, int num_heads, size_t a
     at += round_up(bytes);
     return here;
   };
-  L.h = take((size_t)B * hidden * f);
   L.q = take((size_t)B * num_heads * dah::kHeadDim * f);
   L.k = take((size_t)B * dah::kKvHeads * dah::kHeadDim * f);
   L.v = take((size_t)B * dah::kKvHeads * dah::kHeadDim * f);
@@ -185,7 +185,6 @@ int decoder_layer_step(const float* x, const dah_layer_weights* w, int hidden, i
     return dah::set_error(DAH_ERR_WORKSPACE, "decoder_layer_step: workspace of %zu bytes, need %zu",
                           workspace_bytes, L.total);
   char* ws = static_cast<char*>(workspace);
-  float* h = reinterpret_cast<float*>(ws + L.h);
   float* q = reinterpret_cast<float*>(ws + L.q);
   float* k = reinterpret_cast<float*>(ws + L.k);
   float* v = reinterpret_cast<float*>(ws + L.v);
@@ -197,15 +196,18 @@ int decoder_layer_step(const float* x, const dah_layer_weights* w, int hidden, i
   void* attn_ws = attn > 0 ? ws + L.attn : nullptr;
   const int qdim = num_heads * dah::kHeadDim;
 
-  st = dah_rmsnorm(x, w->w_in, eps, B, hidden, h, stream);
-  if (st == DAH_OK) st = attn_qkv_proj(h, w->w_qkv, B, hidden, num_heads, q, k, v, stream);
+  // Six launches: input_norm folded into qkv_proj and post_attn_norm into
+  // gate_up (the products norm their input rows as they stream them), the
+  // residual adds into the stores of o_proj and down.  mlp.act keeps its own
+  // kernel: folded into down it would be redone once per column tile.
+  st = dah::qkv_proj(x, w->w_in, eps, w->w_qkv, B, hidden, num_heads, q, k, v, stream);
   if (st == DAH_OK)
     st = decode_attn_step_ex(q, k, v, w->q_gain, w->k_gain, eps, rope_theta, k_cache, v_cache,
                              cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
                              num_heads, max_seq_len, num_splits, q_out, o, attn_ws, attn, stream);
   if (st == DAH_OK) st = dah_linear_residual(o, w->w_o, x, B, hidden, qdim, x1, stream);
-  if (st == DAH_OK) st = dah_rmsnorm(x1, w->w_post, eps, B, hidden, h, stream);
-  if (st == DAH_OK) st = dah_linear(h, w->w_gate_up, B, 2 * inter, hidden, gu, stream);
+  if (st == DAH_OK)
+    st = dah_rmsnorm_linear(x1, w->w_post, eps, w->w_gate_up, B, 2 * inter, hidden, gu, stream);
   if (st == DAH_OK) st = dah_silu_mul(gu, B, inter, act, stream);
   if (st == DAH_OK) st = dah_linear_residual(act, w->w_down, x1, B, hidden, inter, y, stream);
   return st;

@@ -74,7 +74,34 @@ struct LinearArgs {
   int T, N, K;
   int nseg;
   Segment seg[3];
+  int x_stride;         // floats per row of x
+  const float* x_gain;  // kNorm: the norm's gain [K]
+  float eps;            // kNorm
 };
+
+// What the products read as their input row x[t] (the kernels' kXMode):
+//   kPlain  x as stored;
+//   kNorm   the row RMS-normed, x[t][k] / sqrt(sum_j x[t][j]^2 / K + eps) *
+//           gain[k] (the rmsnorm rows input_norm and post_attn_norm): x * gain
+//           enters the product and each output row is scaled by the inverse
+//           RMS, whose sum of squares is accumulated while the row streams
+//           through (every workgroup reads all of k for its rows).  Each
+//           column tile redoes this per element work, which stays cheap (a
+//           multiply and a multiply-add); the SwiGLU activation, an exp and a
+//           division per element, cost more redone per tile than a launch of
+//           its own (measured) and stays a separate kernel.
+enum XMode { kPlain = 0, kNorm = 1 };
+
+__device__ __forceinline__ float4 mul4(const float4& a, const float4& b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ float sumsq4(const float4& v, float acc) {
+  return fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, acc))));
+}
+// The inverse RMS of a row from its sum of squares over K.
+__device__ __forceinline__ float inv_rms(float ss, int K, float eps) {
+  return 1.0f / sqrtf(ss / (float)K + eps);
+}
 
 __device__ __forceinline__ Segment segment_of(const LinearArgs& a, int n0) {
   Segment s = a.seg[0];
@@ -84,9 +111,11 @@ __device__ __forceinline__ Segment segment_of(const LinearArgs& a, int n0) {
 }
 
 // Stores one 16 x 16 accumulator block (D layout: lane (r, c) holds rows
-// 4r + v, column c) whose top-left output is (m, n).
+// 4r + v, column c) whose top-left output is (m, n), row 4r + v scaled by
+// scale[v].
 __device__ __forceinline__ void store_block(const LinearArgs& a, const Segment& s, int m, int n,
-                                            const f32x4& acc, int lane) {
+                                            const f32x4& acc, int lane,
+                                            const float (&scale)[4] = {1.f, 1.f, 1.f, 1.f}) {
   const int r = lane >> 4, c = lane & 15;
   float* col = s.y + (n - s.begin) + c;
   const float* rcol = s.res != nullptr ? s.res + (n - s.begin) + c : nullptr;
@@ -95,12 +124,27 @@ __device__ __forceinline__ void store_block(const LinearArgs& a, const Segment& 
     const int t = m + 4 * r + v;
     if (t < a.T) {
       const size_t at = (size_t)t * s.width;
-      col[at] = rcol != nullptr ? acc[v] + rcol[at] : acc[v];
+      const float y = acc[v] * scale[v];
+      col[at] = rcol != nullptr ? y + rcol[at] : y;
     }
   }
 }
 
 // ---------------------------------------------------------------- split-k
+
+// One 32-wide k step of the split-k kernel's operands, per input mode (the
+// norm's gain for kNorm).
+template <int kMB, int kNB, int kXMode>
+struct LinStep {
+  float4 x[kMB][2];
+  u32x4 w[kNB];
+};
+template <int kMB, int kNB>
+struct LinStep<kMB, kNB, kNorm> {
+  float4 x[kMB][2];
+  float4 g[2];
+  u32x4 w[kNB];
+};
 
 constexpr int kLinWaves = 8;        // waves per workgroup, each an eighth of k
 constexpr int kLinMinGroups = 256;  // aim: one workgroup per compute unit or more
@@ -111,11 +155,12 @@ constexpr int kLinMinGroups = 256;  // aim: one workgroup per compute unit or mo
 // (up to four 32-wide k steps in flight); the kKS partial tiles of each row
 // group are added in LDS.  The weight tile is read once per row tile (by the
 // kMW row groups together, from L1/L2 after the first).
-template <int kMB, int kNB, int kMW>
+template <int kMB, int kNB, int kMW, int kXMode>
 __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(LinearArgs a) {
   constexpr int kKS = kLinWaves / kMW;
   static_assert(kLinWaves % kMW == 0, "row groups must divide the waves");
   __shared__ f32x4 part[kLinWaves][kMB * kNB][kWave];
+  __shared__ float rowss[kLinWaves][kMB][16];  // kNorm: sums of squares per wave and row
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,29 +182,36 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
   for (int mb = 0; mb < kMB; ++mb) {
     const int t = m0 + 16 * mb + c;
     ok[mb] = t < a.T;
-    xp[mb] = a.x + (size_t)(ok[mb] ? t : 0) * a.K + k_begin + 8 * r;
+    xp[mb] = a.x + (size_t)(ok[mb] ? t : 0) * a.x_stride + k_begin + 8 * r;
   }
+  const float* gp = a.x_gain + k_begin + 8 * r;  // kNorm
   const uint16_t* wp[kNB];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) wp[nb] = a.w + (size_t)(n0 + 16 * nb + c) * a.K + k_begin + 8 * r;
 
-  struct Step {
-    float4 x[kMB][2];
-    u32x4 w[kNB];
-  };
+  using Step = LinStep<kMB, kNB, kXMode>;
   // Ordinary (cacheable) loads: row tiles that share a weight tile find it
   // in L2.
   auto load = [&](Step& st, int s) {
     const int k = 32 * s;
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) st.w[nb] = *reinterpret_cast<const u32x4*>(wp[nb] + k);
+    // (Zeros as prvalues: a named zero would make the selects pick between
+    // addresses and put the zero in scratch memory.)
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
       const float4* q = reinterpret_cast<const float4*>(xp[mb] + k);
       st.x[mb][0] = ok[mb] ? q[0] : make_float4(0.f, 0.f, 0.f, 0.f);
       st.x[mb][1] = ok[mb] ? q[1] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if constexpr (kXMode == kNorm) {
+      st.g[0] = *reinterpret_cast<const float4*>(gp + k);
+      st.g[1] = *reinterpret_cast<const float4*>(gp + k + 4);
+    }
   };
+  float ss[kMB];  // kNorm: this lane's share of its rows' sums of squares
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) ss[mb] = 0.0f;
   f32x4 acc[kMB][kNB];
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
@@ -168,8 +220,14 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
   auto consume = [&](const Step& st) {
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) {
+      float4 x0 = st.x[mb][0], x1 = st.x[mb][1];
+      if constexpr (kXMode == kNorm) {
+        ss[mb] = sumsq4(x1, sumsq4(x0, ss[mb]));
+        x0 = mul4(x0, st.g[0]);
+        x1 = mul4(x1, st.g[1]);
+      }
       u32x4 hi, lo;
-      split8(st.x[mb][0], st.x[mb][1], hi, lo);
+      split8(x0, x1, hi, lo);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = mfma(hi, st.w[nb], acc[mb][nb]);
 #pragma unroll
@@ -217,6 +275,16 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) part[wave][mb * kNB + nb][lane] = acc[mb][nb];
+  if constexpr (kXMode == kNorm) {
+    // Lanes c, c+16, c+32, c+48 hold row c's k values 8r..8r+7 of each step.
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      float v = ss[mb];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (r == 0) rowss[wave][mb][c] = v;
+    }
+  }
   __syncthreads();
   // (row group g, block blk) pairs spread over the waves; slice q of row
   // group g is wave g + kMW q.
@@ -227,7 +295,19 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
     f32x4 t = part[g][blk][lane];
 #pragma unroll
     for (int q = 1; q < kKS; ++q) t += part[g + kMW * q][blk][lane];
-    store_block(a, sg, m_base + 16 * kMB * g + 16 * (blk / kNB), n0 + 16 * (blk % kNB), t, lane);
+    float scale[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (kXMode == kNorm) {
+      const int mb = blk / kNB;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kKS; ++q) sum += rowss[g + kMW * q][mb][4 * r + v];
+        scale[v] = inv_rms(sum, a.K, a.eps);
+      }
+    }
+    store_block(a, sg, m_base + 16 * kMB * g + 16 * (blk / kNB), n0 + 16 * (blk % kNB), t, lane,
+                scale);
   }
 }
 
@@ -247,7 +327,7 @@ constexpr int kLdsThreads = 256;   // 4 waves
 // (kBM / kWM) x (kBN / kWN) sub-tile over kKS 32-wide k steps of the chunk.
 // With kWK > 1 the waves of a sub-tile take different k steps and their
 // partial tiles are added in LDS, in a fixed order, at the end.
-template <int kBM, int kBN, int kWM, int kWN, int kWK, int kKS, int kDepth>
+template <int kBM, int kBN, int kWM, int kWN, int kWK, int kKS, int kDepth, int kXMode>
 __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
   static_assert(kWM * kWN * kWK == kLdsThreads / kWave, "4 waves");
   constexpr int kBK = 32 * kKS * kWK;
@@ -281,7 +361,7 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
     const int idx = tid + kLdsThreads * i;
     const int row = idx / (kBK / 4), t = m0 + row;
     xok[i] = t < a.T;
-    xsrc[i] = a.x + (size_t)(xok[i] ? t : 0) * a.K + 4 * (idx % (kBK / 4));
+    xsrc[i] = a.x + (size_t)(xok[i] ? t : 0) * a.x_stride + 4 * (idx % (kBK / 4));
   }
   const uint16_t* wsrc[kW8];
 #pragma unroll
@@ -291,22 +371,33 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
   }
   struct Chunk {
     float4 x[kX4];
+    float4 g[kXMode == kNorm ? kX4 : 1];  // kNorm: the gain
     u32x4 w[kW8];
   };
   auto load = [&](Chunk& b, int chunk) {
     const int k = chunk * kBK;
 #pragma unroll
-    for (int i = 0; i < kX4; ++i)
+    for (int i = 0; i < kX4; ++i) {
       b.x[i] = xok[i] ? *reinterpret_cast<const float4*>(xsrc[i] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (kXMode == kNorm)
+        b.g[i] = *reinterpret_cast<const float4*>(a.x_gain + k + 4 * ((tid + kLdsThreads * i) % (kBK / 4)));
+    }
 #pragma unroll
     for (int i = 0; i < kW8; ++i) b.w[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + k);
   };
+  float ss[kX4];  // kNorm: this thread's share of its rows' sums of squares
+#pragma unroll
+  for (int i = 0; i < kX4; ++i) ss[i] = 0.0f;
   auto stage = [&](const Chunk& b) {
 #pragma unroll
     for (int i = 0; i < kX4; ++i) {
       const int idx = tid + kLdsThreads * i;
       const int row = idx / (kBK / 4), col = 4 * (idx % (kBK / 4));
-      const float4 v = b.x[i];
+      float4 v = b.x[i];
+      if constexpr (kXMode == kNorm) {
+        ss[i] = sumsq4(v, ss[i]);
+        v = mul4(v, b.g[i]);
+      }
       const uint32_t h0 = pack2(v.x, v.y), h1 = pack2(v.z, v.w);
       const uint32_t l0 = pack2(v.x - lo_half(h0), v.y - hi_half(h0));
       const uint32_t l1 = pack2(v.z - lo_half(h1), v.w - hi_half(h1));
@@ -367,13 +458,40 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
   }
 
   const Segment sg = segment_of(a, n0);
+  // kNorm: the rows' inverse RMS.  The kBK / 4 consecutive threads that stage
+  // one row's chunk hold its sum of squares between them.
+  __shared__ float row_scale[kXMode == kNorm ? kBM : 1];
+  if constexpr (kXMode == kNorm) {
+#pragma unroll
+    for (int i = 0; i < kX4; ++i) {
+      float v = ss[i];
+#pragma unroll
+      for (int off = 1; off < kBK / 4; off <<= 1) v += __shfl_xor(v, off);
+      const int idx = tid + kLdsThreads * i;
+      if (idx % (kBK / 4) == 0) row_scale[idx / (kBK / 4)] = inv_rms(v, a.K, a.eps);
+    }
+    __syncthreads();
+  }
+  auto scales = [&](int mrow) {  // scales of rows mrow + 4r + v (local rows)
+    f32x4 sc = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (kXMode == kNorm) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[v] = row_scale[mrow + 4 * r + v];
+    }
+    return sc;
+  };
   if constexpr (kWK == 1) {
 #pragma unroll
     for (int mb = 0; mb < kSM; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kSN; ++nb)
-        store_block(a, sg, m0 + wm * (kBM / kWM) + 16 * mb, n0 + wn * (kBN / kWN) + 16 * nb,
-                    acc[mb][nb], lane);
+      for (int nb = 0; nb < kSN; ++nb) {
+        const int mrow = wm * (kBM / kWM) + 16 * mb;
+        float sc[4];
+        const auto s4 = scales(mrow);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[v] = s4[v];
+        store_block(a, sg, m0 + mrow, n0 + wn * (kBN / kWN) + 16 * nb, acc[mb][nb], lane, sc);
+      }
   } else {
     __shared__ f32x4 part[kWK][kWM * kWN * kSM * kSN][kWave];
     const int sub = wm + kWM * wn;
@@ -387,8 +505,12 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
 #pragma unroll
       for (int q = 1; q < kWK; ++q) t += part[q][job][lane];
       const int js = job / (kSM * kSN), mb = (job / kSN) % kSM, nb = job % kSN;
-      store_block(a, sg, m0 + (js % kWM) * (kBM / kWM) + 16 * mb,
-                  n0 + (js / kWM) * (kBN / kWN) + 16 * nb, t, lane);
+      const int mrow = (js % kWM) * (kBM / kWM) + 16 * mb;
+      float sc[4];
+      const auto s4 = scales(mrow);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sc[v] = s4[v];
+      store_block(a, sg, m0 + mrow, n0 + (js / kWM) * (kBN / kWN) + 16 * nb, t, lane, sc);
     }
   }
 }
@@ -437,70 +559,118 @@ int pick_lds(const LinearArgs& a) {
 // columns 1-4 blocks, 1-4 row groups) at T = 2 .. 256 and N x K =
 // 4096 x 1024, 1024 x 2048 (graph-replayed launch times): this rule picks
 // the fastest shape or one within 3% of it in every case.
-LinearConfig pick_config(const LinearArgs& a) {
+// With the norm folded in (kNorm) the split-k tiles stop at 32 columns: the
+// gain in flight leaves no registers for 64.
+LinearConfig pick_config(const LinearArgs& a, int x_mode = kPlain) {
   const int lds = pick_lds(a);
   if (lds != 0) return {lds, 0, 0, 0};
   if (a.T > 16) {
     const int m_tiles = (a.T + 31) / 32;
-    for (int nb = 4; nb >= 1; nb /= 2)
+    for (int nb = x_mode == kPlain ? 4 : 2; nb >= 1; nb /= 2)
       if (m_tiles * (a.N / (16 * nb)) >= kLinMinGroups) return {0, 2, nb, 1};
   }
   return {0, 1, 1, 1};
 }
 
-template <int kBM, int kBN, int kWM, int kWN, int kWK, int kKS, int kDepth>
+template <int kBM, int kBN, int kWM, int kWN, int kWK, int kKS, int kDepth, int kXMode>
 int launch_lds(const LinearArgs& a, hipStream_t stream) {
   if (!lds_fits(a, kBN, 32 * kKS * kWK))
     return dah::set_error(DAH_ERR_SHAPE, "linear: tile %dx%d does not divide N=%d, K=%d", kBM,
                           kBN, a.N, a.K);
   const long long groups = (long long)((a.T + kBM - 1) / kBM) * (a.N / kBN);
   if (groups > INT32_MAX) return dah::set_error(DAH_ERR_SHAPE, "linear: grid too large");
-  linear_lds_kernel<kBM, kBN, kWM, kWN, kWK, kKS, kDepth>
+  linear_lds_kernel<kBM, kBN, kWM, kWN, kWK, kKS, kDepth, kXMode>
       <<<dim3((unsigned)groups), kLdsThreads, 0, stream>>>(a);
   return DAH_OK;
 }
 
+template <int kXMode>
 int launch_lds_shape(int id, const LinearArgs& a, hipStream_t stream) {
   switch (id) {
-    case 1: return launch_lds<64, 128, 2, 2, 1, 2, 1>(a, stream);
-    case 2: return launch_lds<64, 64, 2, 2, 1, 2, 1>(a, stream);
-    case 3: return launch_lds<32, 64, 1, 2, 2, 1, 1>(a, stream);
-    case 4: return launch_lds<32, 32, 1, 1, 4, 1, 1>(a, stream);
-    case 5: return launch_lds<32, 32, 1, 1, 4, 2, 2>(a, stream);
+    case 1: return launch_lds<64, 128, 2, 2, 1, 2, 1, kXMode>(a, stream);
+    case 2: return launch_lds<64, 64, 2, 2, 1, 2, 1, kXMode>(a, stream);
+    case 3: return launch_lds<32, 64, 1, 2, 2, 1, 1, kXMode>(a, stream);
+    case 4: return launch_lds<32, 32, 1, 1, 4, 1, 1, kXMode>(a, stream);
+    case 5: return launch_lds<32, 32, 1, 1, 4, 2, 2, kXMode>(a, stream);
     default: return dah::set_error(DAH_ERR_HIP, "linear: no LDS tile shape %d", id);
   }
 }
 
-template <int kMB, int kNB, int kMW>
+template <int kMB, int kNB, int kMW, int kXMode>
 void launch_cfg(const LinearArgs& a, hipStream_t stream) {
   const int rows = 16 * kMB * kMW;
   const dim3 grid(((a.T + rows - 1) / rows) * (a.N / (16 * kNB)));
-  linear_splitk_kernel<kMB, kNB, kMW><<<grid, kWave * kLinWaves, 0, stream>>>(a);
+  linear_splitk_kernel<kMB, kNB, kMW, kXMode><<<grid, kWave * kLinWaves, 0, stream>>>(a);
 }
 
-int launch_linear(LinearArgs& a, hipStream_t stream) {
-  const LinearConfig c = pick_config(a);
-  if (c.lds != 0) {
-    const int st = launch_lds_shape(c.lds, a, stream);
-    if (st != DAH_OK) return st;
-  } else {
+template <int kXMode>
+int launch_mode(const LinearArgs& a, const LinearConfig& c, hipStream_t stream) {
+  if (c.lds != 0) return launch_lds_shape<kXMode>(c.lds, a, stream);
   // The instantiated shapes; N is a multiple of 64, so every column tiling divides it.
 #define DAH_LIN_CASE(MB, NB, MW) \
-  if (c.mb == MB && c.nb == NB && c.mw == MW) launch_cfg<MB, NB, MW>(a, stream); else
+  if (c.mb == MB && c.nb == NB && c.mw == MW) { launch_cfg<MB, NB, MW, kXMode>(a, stream); return DAH_OK; }
   DAH_LIN_CASE(1, 1, 1)
   DAH_LIN_CASE(2, 1, 1)
   DAH_LIN_CASE(2, 2, 1)
-  DAH_LIN_CASE(2, 4, 1)
-  return dah::set_error(DAH_ERR_HIP, "linear: no kernel for tile %d/%d/%d", c.mb, c.nb, c.mw);
-#undef DAH_LIN_CASE
+  if constexpr (kXMode == kPlain) {
+    DAH_LIN_CASE(2, 4, 1)
   }
+#undef DAH_LIN_CASE
+  return dah::set_error(DAH_ERR_HIP, "linear: no kernel for tile %d/%d/%d", c.mb, c.nb, c.mw);
+}
+
+// x_mode: kPlain or kNorm (a.x_gain, a.eps set); sets a.x_stride.
+int launch_linear(LinearArgs& a, hipStream_t stream, int x_mode = kPlain) {
+  a.x_stride = a.K;
+  const LinearConfig c = pick_config(a, x_mode);
+  const int st = x_mode == kNorm ? launch_mode<kNorm>(a, c, stream)
+                                 : launch_mode<kPlain>(a, c, stream);
+  if (st != DAH_OK) return st;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return dah::set_error(DAH_ERR_HIP, "linear kernel launch failed: %s", hipGetErrorString(e));
   return DAH_OK;
 }
 
+int check_norm(const float* gain, float eps, const char* who) {
+  if (!gain) return dah::set_error(DAH_ERR_NULL, "%s: the norm gain is NULL", who);
+  if (reinterpret_cast<uintptr_t>(gain) % 16 != 0)
+    return dah::set_error(DAH_ERR_ALIGN, "%s: the norm gain needs 16-byte alignment", who);
+  if (!(eps >= 0.0f)) return dah::set_error(DAH_ERR_SHAPE, "%s: eps must be >= 0", who);
+  return DAH_OK;
+}
+
 }  // namespace
+
+namespace dah {
+
+int qkv_proj(const float* x, const float* x_gain, float eps, const void* w_qkv, int T, int hidden,
+             int num_heads, float* q, float* k, float* v, void* stream) {
+  if (!q || !k || !v) return set_error(DAH_ERR_NULL, "attn_qkv_proj: an output is NULL");
+  if (!valid_heads(num_heads))
+    return set_error(DAH_ERR_SHAPE, "num_heads = %d, need 16, 32, 40 or 64", num_heads);
+  const int nq = num_heads * kHeadDim, nkv = kKvHeads * kHeadDim;
+  int st = x_gain ? check_norm(x_gain, eps, "attn_qkv_proj") : DAH_OK;
+  if (st == DAH_OK) st = validate_linear(x, w_qkv, T, nq + 2 * nkv, hidden, q);
+  if (st != DAH_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) % 16 != 0)
+    return set_error(DAH_ERR_ALIGN, "attn_qkv_proj: k and v need 16-byte alignment");
+  LinearArgs a = {};
+  a.x = x;
+  a.w = static_cast<const uint16_t*>(w_qkv);
+  a.T = T;
+  a.N = nq + 2 * nkv;
+  a.K = hidden;
+  a.nseg = 3;
+  a.seg[0] = Segment{q, 0, nq, nullptr};
+  a.seg[1] = Segment{k, nq, nkv, nullptr};
+  a.seg[2] = Segment{v, nq + nkv, nkv, nullptr};
+  a.x_gain = x_gain;
+  a.eps = eps;
+  return launch_linear(a, static_cast<hipStream_t>(stream), x_gain ? kNorm : kPlain);
+}
+
+}  // namespace dah
 
 extern "C" {
 
@@ -548,25 +718,25 @@ int dah_linear_residual(const float* x, const void* w, const float* residual, in
 
 int attn_qkv_proj(const float* x, const void* w_qkv, int T, int hidden, int num_heads, float* q,
                   float* k, float* v, void* stream) {
-  if (!q || !k || !v) return dah::set_error(DAH_ERR_NULL, "attn_qkv_proj: an output is NULL");
-  if (!dah::valid_heads(num_heads))
-    return dah::set_error(DAH_ERR_SHAPE, "num_heads = %d, need 16, 32, 40 or 64", num_heads);
-  const int nq = num_heads * dah::kHeadDim, nkv = dah::kKvHeads * dah::kHeadDim;
-  int st = dah::validate_linear(x, w_qkv, T, nq + 2 * nkv, hidden, q);
+  return dah::qkv_proj(x, nullptr, 0.0f, w_qkv, T, hidden, num_heads, q, k, v, stream);
+}
+
+int dah_rmsnorm_linear(const float* x, const float* x_gain, float eps, const void* w, int T,
+                       int N, int K, float* y, void* stream) {
+  int st = check_norm(x_gain, eps, "dah_rmsnorm_linear");
+  if (st == DAH_OK) st = dah::validate_linear(x, w, T, N, K, y);
   if (st != DAH_OK) return st;
-  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) % 16 != 0)
-    return dah::set_error(DAH_ERR_ALIGN, "attn_qkv_proj: k and v need 16-byte alignment");
   LinearArgs a = {};
   a.x = x;
-  a.w = static_cast<const uint16_t*>(w_qkv);
+  a.w = static_cast<const uint16_t*>(w);
   a.T = T;
-  a.N = nq + 2 * nkv;
-  a.K = hidden;
-  a.nseg = 3;
-  a.seg[0] = Segment{q, 0, nq, nullptr};
-  a.seg[1] = Segment{k, nq, nkv, nullptr};
-  a.seg[2] = Segment{v, nq + nkv, nkv, nullptr};
-  return launch_linear(a, static_cast<hipStream_t>(stream));
+  a.N = N;
+  a.K = K;
+  a.nseg = 1;
+  a.seg[0] = Segment{y, 0, N, nullptr};
+  a.x_gain = x_gain;
+  a.eps = eps;
+  return launch_linear(a, static_cast<hipStream_t>(stream), kNorm);
 }
 
 int attn_o_proj(const float* o, const void* w_o, int T, int num_heads, int hidden, float* y,

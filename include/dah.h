@@ -345,6 +345,21 @@ int dah_linear_residual(const float* x, const void* w, const float* residual, in
                         int K, float* y, void* stream);
 
 /*
+ * A product with the RMSNorm before it folded in (the decoder layer's
+ * input_norm / post_attn_norm + linear rows of the "Qwen3-0.6B" Model Spec
+ * page, "Compute-graph nodes"):
+ *
+ * dah_rmsnorm_linear -- y = rmsnorm(x) . w^T, rmsnorm(x)[t][k] =
+ *   x[t][k] / sqrt(sum_j x[t][j]^2 / K + eps) * x_gain[k]; shapes as
+ *   dah_linear, x_gain [K] float32 (16-byte aligned), eps >= 0.  The sum of
+ *   squares is accumulated as x streams through the product and 1/rms scales
+ *   each output row; the normed rows are never stored.  Errors as
+ *   dah_linear (and DAH_ERR_NULL for a NULL gain).
+ */
+int dah_rmsnorm_linear(const float* x, const float* x_gain, float eps, const void* w, int T,
+                       int N, int K, float* y, void* stream);
+
+/*
  * dah_linear_kernel -- host only, no device call: which kernel dah_linear
  *   (and the projections built on it) launches for a T x N x K product:
  *   0 = the split-k kernel (decode's few rows), 1..5 = the LDS-tiled kernel

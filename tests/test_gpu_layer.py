@@ -1,5 +1,7 @@
 """GPU parity of the decoder layer's pieces and of the whole layer step
-(decoder_layer_step) against the float64 oracle (oracle/layer.py).
+(decoder_layer_step) against the float64 oracle (oracle/layer.py): the
+standalone RMSNorm and silu*up, the product with the norm folded into its
+input (as the layer runs it), the residual product, and the layer.
 
 Gates: the hidden-size RMSNorm and silu*up elementwise within float32
 rounding (rel 1e-6 of the row / element); the residual product within the
@@ -94,6 +96,35 @@ def test_linear_residual_parity(T, N, K):
         2.0 ** -23 * np.abs(ref) + 1e-30
     assert np.all(np.abs(y.cpu().numpy() - ref) <= bound)
     assert torch.equal(r2, y)
+
+
+@pytest.mark.parametrize("N,K", [(6144, 1024), (4096, 2560), (192, 256)])
+@pytest.mark.parametrize("T", [1, 7, 17, 33, 256, 300, 1000])
+def test_rmsnorm_linear_parity(T, N, K):
+    """dah_rmsnorm_linear: the product of the RMS-normed rows (sum of squares
+    accumulated in the product, 1/rms on the output rows) against the
+    oracle's rmsnorm then linear, on both product kernels.  Gate: the
+    product bound of the normed input plus float32 rounding of the norm."""
+    import torch
+    dah = _dah()
+    x = _rand((T, K), 3 * T + K, 2.0)
+    g = 1.0 + 0.1 * _rand((K,), K)
+    w = (_rand((N, K), N + K) / np.sqrt(K)).to(torch.bfloat16)
+    y = torch.full((T + 1, N), float("nan"), device="cuda")
+    lib = dah.lib()
+    dah.check(lib.dah_rmsnorm_linear(x.data_ptr(), g.data_ptr(), 1e-6, w.data_ptr(), T, N, K,
+                                     y.data_ptr(), None), "dah_rmsnorm_linear")
+    torch.cuda.synchronize()
+    assert torch.isnan(y[T]).all(), "wrote past the output"
+    xn = L.rmsnorm(x.cpu().numpy(), g.cpu().numpy())
+    wb = _bits(w)
+    ref = P.linear(xn, wb)
+    absw = np.abs(O.bf16_bits_to_f64(wb))
+    bound = (2.0 ** -16 + 2e-6) * P.linear(np.abs(xn), absw, "f64") + 1e-30
+    err = np.abs(y[:T].cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= bound), float(np.max(err / bound))
+    _print(f"[rmsnorm_linear] T={T} N={N} K={K} kernel {dah.linear_kernel(T, N, K)}: "
+           f"{float(np.max(err / bound)):.3f} of bound")
 
 
 def _layer_case(name, H):
