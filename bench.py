@@ -134,6 +134,7 @@ def cpu_baseline(w, t, seq_lens, table, budget_s):
         "unit": "GB/s",
         "seqs_per_s": done / elapsed,
         "cores": int(threads),
+        "host_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{done} of {len(seq_lens)} sequences of {w.name}, full decode step each "
                   f"(float64 NumPy, {elapsed:.1f} s)",
