@@ -1725,6 +1725,13 @@ struct PrefillState {
 // positions x 2 pieces per 32 lanes) fall on distinct banks.
 __device__ __forceinline__ int vswz(int P) { return (P >> 2) + 4 * (P & 1); }
 
+// The K stage's swizzle: piece q of position P sits in slot q ^ kswz(P).
+// The score product's reads put positions sigma(c) = 4 (c mod 4) + c / 4 of
+// lanes c = 0..7 (and 8..15) at one piece index; kswz takes distinct values
+// modulo 8 on each such group of 8 positions (and is a bijection on 0..15),
+// so 8 lanes of 16 bytes -- 32 banks -- never share a bank.
+__device__ __forceinline__ int kswz(int P) { return (P >> 2) | ((P & 1) << 2) | ((P & 2) << 2); }
+
 __device__ __forceinline__ u32x2 read_v_tr(const char* base, int off) {
   return __builtin_bit_cast(
       u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4)(const_cast<char*>(base) + off)));
@@ -1806,9 +1813,9 @@ __device__ __forceinline__ void attend_step_prefill(const KTileMfma (&K)[kP],
 // steps of kP (2, or 1 with 4 heads): per step the 512 threads load the
 // heads' K and V tiles of the step's pages (16 bytes per thread, page and
 // head, 8 pieces in flight per thread) and write them to one of two LDS
-// stages -- K with its 16-byte pieces XOR-swizzled by position, so that the
-// score product's reads (16 positions at one dim offset) fall on distinct
-// banks, V swizzled for the transpose reads (vswz) and zero past the
+// stages -- K with its 16-byte pieces XOR-swizzled by position (kswz), so
+// that the score product's reads (16 positions at one dim offset) fall on
+// distinct banks, V swizzled for the transpose reads (vswz) and zero past the
 // sequence (or past the last page); each wave then scores the step's pages
 // as chunk_attn_kernel does and sums V with attend_step_prefill.  The cache
 // is read once per kTG tiles, and the workgroups of one KV head (for
@@ -1892,7 +1899,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   const char* src = (kv ? a.v_cache : a.k_cache) + (int64_t)gh * kHG * kTileBytes + 16 * piece;
   const int ppos = piece >> 4, pc = piece & 15;
   const int dst = kv ? kTileBytes + 256 * ppos + 16 * (pc ^ (2 * vswz(ppos)))
-                     : 256 * ppos + 16 * (pc ^ ppos);
+                     : 256 * ppos + 16 * (pc ^ kswz(ppos));
   bool bad_page = false;
   // The pieces of step s's pages (zeros for pages past `last`, which are not read).
   auto fetch = [&](u32x4 (&out)[kP][kHG], int s) {
@@ -1944,7 +1951,8 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   const int kpos = 4 * (col & 3) + (col >> 2);  // sigma(col): the score product's K row
   int kaddr[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) kaddr[kk] = hw * kHeadBytes + 256 * kpos + 16 * ((row + 4 * kk) ^ kpos);
+  for (int kk = 0; kk < 4; ++kk)
+    kaddr[kk] = hw * kHeadBytes + 256 * kpos + 16 * ((row + 4 * kk) ^ kswz(kpos));
   // Transpose-read offsets of V within a stage page: lane (row, col) points
   // at position 4 (col / 4) + row, dims 16 nb + 4 (col mod 4) of its head.
   int vaddr[8];
