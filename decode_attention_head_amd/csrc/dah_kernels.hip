@@ -670,6 +670,27 @@ constexpr float kMaxLag = 8.0f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Stores of the matrix-core decode's outputs (o, q_out, the new cache slot).
+// With 4+ query heads per KV head every workgroup ends by storing 8+ rows of
+// o and q_out per wave (8-16 MB per launch at B = 256); streaming them past
+// the L2 with non-temporal stores finished such launches 4-14 us sooner on
+// MI355X.  At 2 heads per KV head (4 MB) they gained nothing, so kNt is
+// kG >= 4.
+template <bool kNt, class V>
+__device__ __forceinline__ void store_out(V* dst, const V& v) {
+  if constexpr (kNt)
+    __builtin_nontemporal_store(v, dst);
+  else
+    *dst = v;
+}
+
+template <bool kNt>
+__device__ __forceinline__ void store8_out(float* dst, const float (&v)[8], float scale) {
+  f32x4* d = reinterpret_cast<f32x4*>(dst);
+  store_out<kNt>(d, f32x4{v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale});
+  store_out<kNt>(d + 1, f32x4{v[4] * scale, v[5] * scale, v[6] * scale, v[7] * scale});
+}
+
 // Two floats -> two bfloat16 (round to nearest even; v_cvt_pk_bf16_f32),
 // `lo` in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -821,6 +842,7 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
                                                   int g, int lane, MfmaStash<kG>& stash) {
   static_assert(kG <= 16, "one score column per query head");
   constexpr int kH = kG * kKvHeads;
+  constexpr bool kNt = kG >= 4;  // see store_out
   using TileV = Tile<DAH_BF16>;
   const int wave = g;
   const int row = lane >> 4;
@@ -849,16 +871,21 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
 
   // Small loads first (see decode_range).  Without the step, q arrives
   // normed: the lane reads its B-operand slice (head qh, dims 32kk + 8r ..)
-  // directly.  With the step, it reads the raw rows in the row layout.
+  // directly.  With the step, it reads raw rows in the row layout, each
+  // 16-lane row its own heads: row r takes heads r, r + 4, ... (kJ of them),
+  // so the norm and rotation cost kJ rows of work per lane instead of kG.
+  // Entries past kG repeat head kG - 1 and are not used.
+  constexpr int kJ = (kG + 3) / 4;
   float qv[kStep ? 1 : 4][8];
-  float qr[kStep ? kG : 1][8];
+  float qr[kStep ? kJ : 1][8];
   float qw[8], kx[8], vx[8], kw8[8];
   if constexpr (!kStep) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) load8(a.q + (qrow0 + qh) * kHeadDim + 32 * kk + 8 * row, qv[kk]);
   } else {
 #pragma unroll
-    for (int h = 0; h < kG; ++h) load8(a.q + (qrow0 + h) * kHeadDim + 8 * col, qr[h]);
+    for (int j = 0; j < kJ; ++j)
+      load8(a.q + (qrow0 + min(row + 4 * j, kG - 1)) * kHeadDim + 8 * col, qr[j]);
     load8(a.q_gain + 8 * col, qw);
     if (holds_last) {
       load8(a.k_new + ((size_t)b * kKvHeads + g) * kHeadDim + 8 * col, kx);
@@ -900,24 +927,31 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
       unpack_slot<DAH_BF16>(kw, kf);  // the new token as the cache holds it
       unpack_slot<DAH_BF16>(vw, vf);
     }
-    float s_new = -INFINITY;  // the new token's score for head `col`
+    float sc_new[kJ];  // the new token's score for head row + 4j (whole row)
 #pragma unroll
-    for (int h = 0; h < kG; ++h) {
-      norm_rope_row(qr[h], qw, a.eps, cr, sr, col);
-      if (row_writes(row, h)) {
+    for (int j = 0; j < kJ; ++j) {
+      const int h = row + 4 * j;
+      norm_rope_row(qr[j], qw, a.eps, cr, sr, col);
+      if (h < kG) {
         float4* d = reinterpret_cast<float4*>(&stash.q[wave][h][8 * col]);
-        d[0] = make_float4(qr[h][0], qr[h][1], qr[h][2], qr[h][3]);
-        d[1] = make_float4(qr[h][4], qr[h][5], qr[h][6], qr[h][7]);
+        d[0] = make_float4(qr[j][0], qr[j][1], qr[j][2], qr[j][3]);
+        d[1] = make_float4(qr[j][4], qr[j][5], qr[j][6], qr[j][7]);
       }
       if (holds_last) {
         float sc = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc = fmaf(qr[h][e], kf[e], sc);
-        sc = row_sum16(sc) * qscale;
-        s_new = col == h ? sc : s_new;
+        for (int e = 0; e < 8; ++e) sc = fmaf(qr[j][e], kf[e], sc);
+        sc_new[j] = row_sum16(sc) * qscale;
       }
     }
     if (holds_last) {
+      // Column c's head c was scored by row c mod 4, entry c / 4.
+      float s_new = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const float v = __shfl(sc_new[j], 16 * (col & 3) + col);
+        s_new = (col >> 2) == j ? v : s_new;
+      }
       // Start the state with the new token: reference = its score, weight 1
       // (counted once, in row 0), value = v_new for every head of this KV head.
       st.m = col < kG ? s_new : 0.0f;
@@ -1008,7 +1042,7 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) o8[nb] = st.acc[nb][v];
     if (to_o) {
-      store8(a.o + (qrow0 + h) * kHeadDim + 8 * col, o8, bad_page ? NAN : 1.0f / lh);
+      store8_out<kNt>(a.o + (qrow0 + h) * kHeadDim + 8 * col, o8, bad_page ? NAN : 1.0f / lh);
     } else {
       const size_t part = part_base + (size_t)(g * kG + h) * part_stride;
       store8(a.part_acc + part * kHeadDim + 8 * col, o8, bad_page ? NAN : 1.0f);
@@ -1024,8 +1058,8 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
       for (int h0 = 0; h0 < kG; h0 += 2) {
         const int h = h0 + half;
         if (h < kG)
-          reinterpret_cast<float4*>(a.q_out + (qrow0 + h) * kHeadDim)[q4] =
-              reinterpret_cast<const float4*>(&stash.q[wave][h][0])[q4];
+          store_out<kNt>(reinterpret_cast<f32x4*>(a.q_out + (qrow0 + h) * kHeadDim) + q4,
+                         reinterpret_cast<const f32x4*>(&stash.q[wave][h][0])[q4]);
       }
     }
     if (holds_last && row == 0) {
@@ -1033,8 +1067,8 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
       if (id >= 0 && id < a.num_pages) {
         const int64_t slot_off = (int64_t)id * page_bytes + head_bytes +
                                  (int64_t)(tail - 1) * (TileV::kTileBytes / kPage);
-        reinterpret_cast<u32x4*>(a.k_cache_w + slot_off)[col] = stash.kv[wave][0][col];
-        reinterpret_cast<u32x4*>(a.v_cache_w + slot_off)[col] = stash.kv[wave][1][col];
+        store_out<kNt>(reinterpret_cast<u32x4*>(a.k_cache_w + slot_off) + col, stash.kv[wave][0][col]);
+        store_out<kNt>(reinterpret_cast<u32x4*>(a.v_cache_w + slot_off) + col, stash.kv[wave][1][col]);
       }
     }
   }
