@@ -6,7 +6,10 @@ summaries kept under profiles/.
         --copy-mib 1024 --out FILE --cmd "..."
 
 `trace` lists per-kernel call counts and durations from a --kernel-trace
---stats run.  `traffic` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
+--stats run.  `counters` lists the mean per dispatch of every counter in
+one or more --pmc runs for the kernels named by --kernel (substrings), with
+a few ratios (waves, instructions per wave, LDS bank-conflict cycles per LDS
+instruction).  `traffic` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
 two separate --pmc runs) into HBM bytes per decode launch, each counter
 scaled by what it reads for the probe copy kernel, whose traffic is known
 exactly (copy-mib MiB read and the same written).  The summary records a
@@ -96,6 +99,42 @@ def traffic_summary(fetch_dir: str, write_dir: str, copy_mib: int) -> str:
     return "\n".join(lines)
 
 
+def _all_counter_means(d: str):
+    """{kernel name: {counter: mean value per dispatch}} of one --pmc run."""
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in rows:
+        agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+
+def counters_summary(dirs, kernels) -> str:
+    out = [f"kernel_source_sha256_16: {source_digest()}"]
+    for key in kernels:
+        merged = {}
+        name = None
+        for d in dirs:
+            hits = {k: v for k, v in _all_counter_means(d).items() if key in k}
+            if len(hits) != 1:
+                raise ValueError(f"{d}: expected one kernel matching {key!r}, found {len(hits)}")
+            (name, vals), = hits.items()
+            merged.update(vals)
+        out.append(f"[{_short(name)}]")
+        for c in sorted(merged):
+            out.append(f"  {c:32s} {merged[c]:20.3f}")
+        waves = merged.get("SQ_WAVES")
+        if waves:
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD",
+                      "SQ_INSTS_SALU"):
+                if c in merged:
+                    out.append(f"  {c + ' per wave':32s} {merged[c] / waves:20.1f}")
+        if merged.get("SQ_INSTS_LDS"):
+            if "SQ_LDS_BANK_CONFLICT" in merged:
+                out.append(f"  {'bank-conflict cycles per LDS instr':32s} "
+                           f"{merged['SQ_LDS_BANK_CONFLICT'] / merged['SQ_INSTS_LDS']:20.4f}")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -105,14 +144,22 @@ def main():
     c.add_argument("fetch_dir")
     c.add_argument("write_dir")
     c.add_argument("--copy-mib", type=int, required=True)
-    for p in (t, c):
+    n = sub.add_parser("counters")
+    n.add_argument("dirs", nargs="+")
+    n.add_argument("--kernel", action="append", required=True,
+                   help="substring naming one kernel in every run (repeatable)")
+    for p in (t, c, n):
         p.add_argument("--out", required=True)
         p.add_argument("--cmd", action="append", default=[],
                        help="command that produced the data (repeatable)")
         p.add_argument("--note", default="")
     a = ap.parse_args()
-    body = trace_summary(a.dir) if a.mode == "trace" else \
-        traffic_summary(a.fetch_dir, a.write_dir, a.copy_mib)
+    if a.mode == "trace":
+        body = trace_summary(a.dir)
+    elif a.mode == "traffic":
+        body = traffic_summary(a.fetch_dir, a.write_dir, a.copy_mib)
+    else:
+        body = counters_summary(a.dirs, a.kernel)
     head = [f"# rocprofv3 {a.mode} summary"]
     head += [f"# command: {c}" for c in a.cmd]
     if a.note:
