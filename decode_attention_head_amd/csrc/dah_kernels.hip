@@ -1239,13 +1239,15 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
 // partial results (weighted V sum acc_s, running max m_s in log2 units, sum
 // l_s):  M = max_s m_s,  w_s = 2^(m_s - M),  o = sum_s w_s acc_s / sum_s w_s l_s.
 // Thread t owns dims 4(t mod 32) .. +3 and every 8th partial starting at
-// t / 32, so 8 partials are read in parallel for each dim; LDS merges the 8
-// groups.  The partials' lists are independent loads, so a long list costs
-// bandwidth, not a chain of latencies.
+// t / 32.  One pass: each thread folds its partials into a running (max,
+// sum, weighted V sum), rescaling when the max moves (the same result by
+// softmax_shift), and LDS merges the 8 groups the same way.  The loads of
+// kMergeChunk partials per thread are issued before any is used.
 constexpr int kCombineThreads = 256;
 constexpr int kCombineGroups = kCombineThreads / 32;
+constexpr int kMergeChunk = 8;
 
-// Partial i of a row: split layout (row-major splits, all present).
+// Partial i of a row: split layout (row-major splits; the first n present).
 struct SplitParts {
   size_t base;  // (b * H + h) * splits
   __device__ size_t slot(int i) const { return base + i; }
@@ -1264,44 +1266,67 @@ struct BalancedParts {
   }
 };
 
+// Running state of one thread (or group) of the merge.
+struct MergeState {
+  float m = -INFINITY, l = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  // Fold in (m2, l2, acc2 * s2) where acc2 is scaled by s2 = 1 on entry.
+  __device__ void fold(float m2, float l2, const float4& v) {
+    const float mn = fmaxf(m, m2);
+    const float s1 = m == -INFINITY ? 0.0f : fast_exp2(m - mn);
+    const float s2 = m2 == -INFINITY ? 0.0f : fast_exp2(m2 - mn);
+    m = mn;
+    l = l * s1 + l2 * s2;
+    acc.x = acc.x * s1 + v.x * s2;
+    acc.y = acc.y * s1 + v.y * s2;
+    acc.z = acc.z * s1 + v.z * s2;
+    acc.w = acc.w * s1 + v.w * s2;
+  }
+};
+
+// Merges the present partials among i < n of a row (slots i < n_slots are
+// read: they must lie inside the partial buffers) and writes the row, or
+// `fill` in every element when !ok (a sequence outside the domain).
 template <class Parts>
 __device__ __forceinline__ void merge_parts(const float* __restrict__ part_acc,
                                             const float* __restrict__ part_ml, const Parts& parts,
-                                            int n, float* __restrict__ out_row) {
-  __shared__ float red_m[kCombineThreads / kWave];
+                                            int n_slots, int n, bool ok, float fill,
+                                            float* __restrict__ out_row) {
+  __shared__ float red_m[kCombineGroups];
   __shared__ float4 red_acc[kCombineGroups][32];
   __shared__ float red_l[kCombineGroups];
   const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
   const int grp = t >> 5, dim4 = t & 31;
   const float2* ml = reinterpret_cast<const float2*>(part_ml);
 
-  float M = -INFINITY;
-  for (int i = t; i < n; i += kCombineThreads)
-    if (parts.present(i)) M = fmaxf(M, ml[parts.slot(i)].x);
+  MergeState st;
+  for (int i0 = grp; i0 < n_slots; i0 += kCombineGroups * kMergeChunk) {
+    float2 m_l[kMergeChunk];
+    float4 v[kMergeChunk];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red_m[t >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  float L = 0.0f;
-#pragma unroll 4
-  for (int i = grp; i < n; i += kCombineGroups) {
-    if (!parts.present(i)) continue;
-    const size_t slot = parts.slot(i);
-    const float2 m_l = ml[slot];
-    const float4 v = reinterpret_cast<const float4*>(part_acc + slot * kHeadDim)[dim4];
-    const float w = fast_exp2(m_l.x - M);
-    L = fmaf(w, m_l.y, L);
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
+    for (int c = 0; c < kMergeChunk; ++c) {
+      const int i = i0 + kCombineGroups * c;
+      if (i < n_slots) {
+        const size_t slot = parts.slot(i);
+        m_l[c] = ml[slot];
+        v[c] = reinterpret_cast<const float4*>(part_acc + slot * kHeadDim)[dim4];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c) {
+      const int i = i0 + kCombineGroups * c;
+      if (i < n && parts.present(i)) st.fold(m_l[c].x, m_l[c].y, v[c]);
+    }
   }
-  red_acc[grp][dim4] = acc;
-  if (dim4 == 0) red_l[grp] = L;
+  // Merge the 8 groups: the reference max first, then the rescaled sums.
+  if (dim4 == 0) red_m[grp] = st.m;
+  __syncthreads();
+  float M = red_m[0];
+#pragma unroll
+  for (int g = 1; g < kCombineGroups; ++g) M = fmaxf(M, red_m[g]);
+  const float s = st.m == -INFINITY ? 0.0f : fast_exp2(st.m - M);
+  red_acc[grp][dim4] = make_float4(st.acc.x * s, st.acc.y * s, st.acc.z * s, st.acc.w * s);
+  if (dim4 == 0) red_l[grp] = st.l * s;
   __syncthreads();
   if (grp == 0) {
     float4 sum = red_acc[0][dim4];
@@ -1317,7 +1342,8 @@ __device__ __forceinline__ void merge_parts(const float* __restrict__ part_acc,
     }
     const float inv = 1.0f / Ls;
     reinterpret_cast<float4*>(out_row)[dim4] =
-        make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+        ok ? make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv)
+           : make_float4(fill, fill, fill, fill);
   }
 }
 
@@ -1329,7 +1355,8 @@ __device__ __forceinline__ void fill_row(float* out_row, int seq_len) {
   }
 }
 
-// DAH_PLAN_SPLIT: the non-empty splits of each (sequence, head).
+// DAH_PLAN_SPLIT: the non-empty splits of each (sequence, head); the row's
+// length decides how many of its `splits` slots count.
 __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, int B, int H, int max_seq_len, int splits,
@@ -1337,14 +1364,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
   const int unit = blockIdx.x;  // b * H + h
   const int b = unit / H;
   const int seq_len = seq_lens[b];
-  float* out_row = o + (size_t)unit * kHeadDim;
-  if (seq_len < 1 || seq_len > max_seq_len) {
-    fill_row(out_row, seq_len);
-    return;
-  }
-  const int npages = (seq_len + kPage - 1) / kPage;
+  const bool ok = seq_len >= 1 && seq_len <= max_seq_len;
+  const int npages = ok ? (seq_len + kPage - 1) / kPage : 0;
   const int nsplit = (npages + pages_per_split - 1) / pages_per_split;
-  merge_parts(part_acc, part_ml, SplitParts{(size_t)unit * splits}, nsplit, out_row);
+  merge_parts(part_acc, part_ml, SplitParts{(size_t)unit * splits}, splits, nsplit, ok,
+              seq_len < 1 ? 0.0f : NAN, o + (size_t)unit * kHeadDim);
 }
 
 // DAH_PLAN_BALANCED: sequence b owns pages [P_b, P_b + n_b) of the batch and
@@ -1390,7 +1414,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_balanced_kernel(
   const int k0 = (int)(((P + 1) * G - 1) / T);
   const int k1 = (int)(((last + 1) * G - 1) / T);
   if (k0 == k1) return;
-  merge_parts(part_acc, part_ml, BalancedParts{b, h, k0, H, T, (long long)G}, k1 - k0 + 1, out_row);
+  const int n = k1 - k0 + 1;
+  merge_parts(part_acc, part_ml, BalancedParts{b, h, k0, H, T, (long long)G}, n, n, true, 0.0f,
+              out_row);
 }
 
 // ------------------------------------------------------------ norm + RoPE + append
