@@ -465,6 +465,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
   }
 
   // First tile in flight before the prologue's arithmetic.
+  constexpr bool kPrefetch = !(kDtype == DAH_F32 && kG == 5);
   Tile<kDtype> K0, V0, K1, V1;
   int id1 = bt[min(p0 + 1, last)];
   int id2 = bt[min(p0 + 2, last)];
@@ -521,42 +522,59 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
   // eight loads together and ahead of the math on the other tile, so the wait
   // before a tile covers only its own loads.  The last one or two pages (the
   // only place a partial page, or the new token, can be) are finished after
-  // the loop.
-  int p = p0;
-  for (; p + 2 <= last; p += 2) {
-    const int64_t off1 = offset_of(id1);
-    K1.load(kbase + off1, lane);
-    V1.load(vbase + off1, lane);
-    const int id3 = bt[min(p + 3, last)];
-    __builtin_amdgcn_sched_barrier(0);
-    attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
-    __builtin_amdgcn_sched_barrier(0);
-    const int64_t off2 = offset_of(id2);
-    K0.load(kbase + off2, lane);
-    V0.load(vbase + off2, lane);
-    const int id4 = bt[min(p + 4, last)];
-    __builtin_amdgcn_sched_barrier(0);
-    attend_tile<kDtype, false, kG>(K1, V1, q, st, row, kPage);
-    __builtin_amdgcn_sched_barrier(0);
-    id1 = id3;
-    id2 = id4;
-  }
-  if (p + 1 <= last) {
-    const int64_t off1 = offset_of(id1);
-    K1.load(kbase + off1, lane);
-    V1.load(vbase + off1, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
-    __builtin_amdgcn_sched_barrier(0);
-    if (last_masked)
-      attend_tile<kDtype, true, kG>(K1, V1, q, st, row, last_valid);
-    else
-      attend_tile<kDtype, false, kG>(K1, V1, q, st, row, kPage);
+  // the loop.  A float32 cache with 5 query heads per KV head loads one tile
+  // at a time instead: there the second tile spills (the one-tile loop is 7%
+  // faster); at 8 heads both forms spill and the pipelined one is faster.
+  if constexpr (!kPrefetch) {
+    // One tile at a time: page p is loaded, then consumed.
+    for (int p = p0; p <= last; ++p) {
+      if (p > p0) {
+        const int64_t off = offset_of(bt[p]);
+        K0.load(kbase + off, lane);
+        V0.load(vbase + off, lane);
+      }
+      if (p == last && last_masked)
+        attend_tile<kDtype, true, kG>(K0, V0, q, st, row, last_valid);
+      else
+        attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
+    }
   } else {
-    if (last_masked)
-      attend_tile<kDtype, true, kG>(K0, V0, q, st, row, last_valid);
-    else
+    int p = p0;
+    for (; p + 2 <= last; p += 2) {
+      const int64_t off1 = offset_of(id1);
+      K1.load(kbase + off1, lane);
+      V1.load(vbase + off1, lane);
+      const int id3 = bt[min(p + 3, last)];
+      __builtin_amdgcn_sched_barrier(0);
       attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
+      __builtin_amdgcn_sched_barrier(0);
+      const int64_t off2 = offset_of(id2);
+      K0.load(kbase + off2, lane);
+      V0.load(vbase + off2, lane);
+      const int id4 = bt[min(p + 4, last)];
+      __builtin_amdgcn_sched_barrier(0);
+      attend_tile<kDtype, false, kG>(K1, V1, q, st, row, kPage);
+      __builtin_amdgcn_sched_barrier(0);
+      id1 = id3;
+      id2 = id4;
+    }
+    if (p + 1 <= last) {
+      const int64_t off1 = offset_of(id1);
+      K1.load(kbase + off1, lane);
+      V1.load(vbase + off1, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
+      __builtin_amdgcn_sched_barrier(0);
+      if (last_masked)
+        attend_tile<kDtype, true, kG>(K1, V1, q, st, row, last_valid);
+      else
+        attend_tile<kDtype, false, kG>(K1, V1, q, st, row, kPage);
+    } else {
+      if (last_masked)
+        attend_tile<kDtype, true, kG>(K0, V0, q, st, row, last_valid);
+      else
+        attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
+    }
   }
   if constexpr (kStep) {
     // The new token (slot tail - 1 of the last page, read from the cache
