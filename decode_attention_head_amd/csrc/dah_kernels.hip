@@ -1815,19 +1815,17 @@ __device__ __forceinline__ u32x2 read_v_tr(const char* base, int off) {
       u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsS16x4)(const_cast<char*>(base) + off)));
 }
 
-// One step of kP pages (1 or 2) of the shared-page kernel: K[j] holds page
-// j's K tile, vpage[j] its staged V (vaddr: this lane's transpose-read
-// offsets).  kMasked: column c sees only the positions of page j below
-// climit[j] (per lane; 0 = none of the page); the stage holds zeros for
-// positions past the sequence, so V needs no clearing.
+// One step of kP pages (1 or 2) of the shared-page kernel, in two halves
+// so that a wave can issue one step's score products and then work on the
+// previous step's weights while the matrix cores run them.
+//
+// step_scores: K[j] holds page j's K tile; lane (r, c) gets column c's
+// scores at positions 4v + r of each page.  kMasked: column c sees only the
+// positions of page j below climit[j] (per lane; 0 = none of the page).
 template <int kP, bool kMasked>
-__device__ __forceinline__ void attend_step_prefill(const KTileMfma (&K)[kP],
-                                                    const char* const (&vpage)[kP],
-                                                    const int (&vaddr)[8],
-                                                    const u32x4 (&qb)[4][3], PrefillState& st,
-                                                    int lane, const int (&climit)[kP]) {
+__device__ __forceinline__ void step_scores(const KTileMfma (&K)[kP], const u32x4 (&qb)[4][3],
+                                            int lane, const int (&climit)[kP], f32x4 (&s)[kP]) {
   const int r = lane >> 4;
-  f32x4 s[kP];
 #pragma unroll
   for (int j = 0; j < kP; ++j) {
     s[j] = page_scores(K[j], qb);
@@ -1836,6 +1834,16 @@ __device__ __forceinline__ void attend_step_prefill(const KTileMfma (&K)[kP],
       for (int v = 0; v < 4; ++v) s[j][v] = 4 * v + r < climit[j] ? s[j][v] : -INFINITY;
     }
   }
+}
+
+// step_weights_pv: the online softmax over a step's scores and the weighted
+// sum of its V pages, vpage[j] the staged V of page j (vaddr: this lane's
+// transpose-read offsets).  The stage holds zeros for positions past the
+// sequence, so V needs no clearing.
+template <int kP>
+__device__ __forceinline__ void step_weights_pv(const f32x4 (&s)[kP],
+                                                const char* const (&vpage)[kP],
+                                                const int (&vaddr)[8], PrefillState& st) {
   float pmax = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
   if constexpr (kP == 2) pmax = fmaxf(pmax, fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
   const float pm = max_over_rows(pmax);
@@ -1890,12 +1898,13 @@ __device__ __forceinline__ void attend_step_prefill(const KTileMfma (&K)[kP],
 // heads for chunks of two tiles, so that every wave has work.  Pages go in
 // steps of kP (2, or 1 with 4 heads): per step the 512 threads load the
 // heads' K and V tiles of the step's pages (16 bytes per thread, page and
-// head, 8 pieces in flight per thread) and write them to one of two LDS
+// head, 8 pieces in flight per thread) and write them to one of three LDS
 // stages -- K with its 16-byte pieces XOR-swizzled by position (kswz), so
 // that the score product's reads (16 positions at one dim offset) fall on
 // distinct banks, V swizzled for the transpose reads (vswz) and zero past the
 // sequence (or past the last page); each wave then scores the step's pages
-// as chunk_attn_kernel does and sums V with attend_step_prefill.  The cache
+// as chunk_attn_kernel does (step_scores) and, one step later, weighs them
+// and sums V (step_weights_pv).  The cache
 // is read once per kTG tiles, and the workgroups of one KV head (for
 // kTG = 8) are consecutive modulo 8, which keeps them on one XCD, where they
 // share the pages through L2.
@@ -1918,7 +1927,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   static_assert(kHG * kTG == kChunkWaves && kKvHeads % kHG == 0, "heads x tiles = 8 waves");
   static_assert(kWave * kChunkWaves * 16 == kHeadBytes, "one 16-byte piece per thread and head");
   static_assert(kDepth >= 2 && kDepth % 2 == 0, "stages alternate within the unrolled ring");
-  __shared__ __attribute__((aligned(16))) char stage[2][kP * kPageBytes];  // [stage][page][head][K|V]
+  __shared__ __attribute__((aligned(16))) char stage[3][kP * kPageBytes];  // [stage][page][head][K|V]
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2041,38 +2050,47 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
     for (int nb = 0; nb < 8; ++nb) vaddr[nb] = base + 32 * (nb ^ vswz(P));
   }
 
+  // Software pipeline across steps: after step s's barrier a wave issues
+  // the score products of step s, then the softmax and V sum of step s - 1
+  // (whose V is still in its stage), so the matrix cores work on one while
+  // the VALU works on the other.  Three stages: step s writes stage s mod 3,
+  // last read by step s - 3's K reads and step s - 2's V sum, both before
+  // barrier s - 1.
+  f32x4 sprev[kP];
+  bool prev_on = false;  // step s - 1 awaits its softmax and V sum
+  int cur = 0;           // stage of step s
+  int prev = 0;          // stage of step s - 1
   for (int s0 = 0; s0 < steps; s0 += kDepth) {
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) {
       const int s = s0 + i;
       if (s < steps) {
-        // Stage i & 1 was last read two steps ago, before the previous
-        // barrier.  V rows past the sequence (never written) are staged as
-        // zeros.
+        // V rows past the sequence (never written) are staged as zeros.
+        char* stg = &stage[cur][0];
 #pragma unroll
         for (int j = 0; j < kP; ++j) {
           const bool past = kv && kPage * (kP * s + j) + ppos >= seq_len;
 #pragma unroll
           for (int h = 0; h < kHG; ++h)
-            *reinterpret_cast<u32x4*>(&stage[i & 1][j * kPageBytes + h * kHeadBytes + dst]) =
+            *reinterpret_cast<u32x4*>(stg + j * kPageBytes + h * kHeadBytes + dst) =
                 past ? u32x4{0u, 0u, 0u, 0u} : ring[i][j][h];
         }
         __syncthreads();
         if (s + kDepth < steps) fetch(ring[i], s + kDepth);
         const int p0 = kP * s;
-        if (p0 <= wave_last) {
+        const bool on = p0 <= wave_last;
+        f32x4 scur[kP];
+        if (on) {
           KTileMfma K[kP];
-          const char* vpage[kP];
 #pragma unroll
           for (int j = 0; j < kP; ++j) {
-            const char* sp = &stage[i & 1][j * kPageBytes];
+            const char* sp = stg + j * kPageBytes;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) K[j].w[kk] = *reinterpret_cast<const u32x4*>(sp + kaddr[kk]);
-            vpage[j] = sp;
           }
           if (p0 + kP - 1 < first_masked && p0 + kP - 1 <= wave_last) {
             const int cl[kP] = {};
-            attend_step_prefill<kP, false>(K, vpage, vaddr, qb, st, lane, cl);
+            step_scores<kP, false>(K, qb, lane, cl, scur);
           } else {
             int cl[kP];
 #pragma unroll
@@ -2080,11 +2098,28 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
               const int p = p0 + j;
               cl[j] = p > wave_last ? 0 : p < first_masked ? kPage : climit_pos - kPage * p + 1;
             }
-            attend_step_prefill<kP, true>(K, vpage, vaddr, qb, st, lane, cl);
+            step_scores<kP, true>(K, qb, lane, cl, scur);
           }
         }
+        if (prev_on) {
+          const char* vpage[kP];
+#pragma unroll
+          for (int j = 0; j < kP; ++j) vpage[j] = &stage[prev][j * kPageBytes];
+          step_weights_pv<kP>(sprev, vpage, vaddr, st);
+        }
+#pragma unroll
+        for (int j = 0; j < kP; ++j) sprev[j] = scur[j];
+        prev_on = on;
+        prev = cur;
+        cur = cur == 2 ? 0 : cur + 1;
       }
     }
+  }
+  if (prev_on) {
+    const char* vpage[kP];
+#pragma unroll
+    for (int j = 0; j < kP; ++j) vpage[j] = &stage[prev][j * kPageBytes];
+    step_weights_pv<kP>(sprev, vpage, vaddr, st);
   }
   if (!live) return;
 
