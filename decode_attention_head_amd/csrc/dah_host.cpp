@@ -118,7 +118,10 @@ int plan_decode(int B, int num_heads, int cache_dtype, int max_seq_len, int num_
       p.pages_per_split = 0;
       p.grid_splits = 0;
       p.workgroups = num_cus * kBalancedGroupsPerCu;
-      p.workspace = partial_bytes(static_cast<long long>(B) + p.workgroups - 1, num_heads);
+      // partial slots, then the batch's page prefix sums (B + 1 int32) that
+      // the decode writes for the merge
+      p.workspace = partial_bytes(static_cast<long long>(B) + p.workgroups - 1, num_heads) +
+                    static_cast<size_t>(B + 1) * sizeof(int32_t);
       break;
     default: {
       const int pps = (max_pages + want - 1) / want;

@@ -349,6 +349,9 @@ struct DecodeArgs {
   // weighted V sum each, then one float2 (running max in log2 units, sum) each.
   float* part_acc;
   float* part_ml;
+  // DAH_PLAN_BALANCED: prefix[b] = pages of sequences < b (b <= B), written
+  // by workgroup 0 of the decode for the merge.
+  int32_t* prefix;
   // The fused step only: q above is the raw (pre-norm) query.
   const float* k_new;
   const float* v_new;
@@ -1206,6 +1209,8 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
     if (bb == a.B - 1) prefix[a.B] = run;
   }
   __syncthreads();
+  if (blockIdx.x == 0)  // for the merge launch
+    for (int bb = t; bb <= a.B; bb += blockDim.x) a.prefix[bb] = prefix[bb];
 
   if constexpr (kStep) {
     // Sequences with nothing to attend to still get q_out (workgroup 0).
@@ -1253,11 +1258,11 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
 
 // ------------------------------------------------------------ log-sum-exp merge
 //
-// One workgroup of 256 threads per (sequence, query head) merges that row's
-// partial results (weighted V sum acc_s, running max m_s in log2 units, sum
-// l_s):  M = max_s m_s,  w_s = 2^(m_s - M),  o = sum_s w_s acc_s / sum_s w_s l_s.
-// Thread t owns dims 4(t mod 32) .. +3 and every 8th partial starting at
-// t / 32.  One pass: each thread folds its partials into a running (max,
+// A row's partial results (weighted V sum acc_s, running max m_s in log2
+// units, sum l_s) merge as  M = max_s m_s,  w_s = 2^(m_s - M),
+// o = sum_s w_s acc_s / sum_s w_s l_s.  Fixed splits (merge_parts): one
+// workgroup of 256 threads per (sequence, query head); thread t owns dims
+// 4(t mod 32) .. +3 and every 8th partial starting at t / 32.  One pass: each thread folds its partials into a running (max,
 // sum, weighted V sum), rescaling when the max moves (the same result by
 // softmax_shift), and LDS merges the 8 groups the same way.  The loads of
 // kMergeChunk partials per thread are issued before any is used.
@@ -1393,48 +1398,55 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
 // workgroup k of G owns [floor(kT/G), floor((k+1)T/G)), so the workgroups
 // that saw b are owner(P_b) .. owner(P_b + n_b - 1) with
 // owner(x) = floor(((x+1)G - 1)/T), their partials in slots b + k.  A
-// sequence seen by one workgroup was written to o directly.
-__global__ __launch_bounds__(kCombineThreads) void combine_balanced_kernel(
+// sequence seen by one workgroup was written to o directly.  The decode
+// left the prefix sums P in the workspace.  One wave per (sequence, 2
+// heads): lane l merges dims 4(l mod 32) .. +3 of head 2 blockIdx + l / 32
+// over the (few) workgroups that saw the sequence.
+constexpr int kBalancedMergeThreads = 64;
+constexpr int kBalancedMergeRows = kBalancedMergeThreads / 32;  // heads per workgroup
+
+__global__ __launch_bounds__(kBalancedMergeThreads) void combine_balanced_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, int B, int H, int max_seq_len, int G,
-    float* __restrict__ o) {
-  __shared__ int red[2][kCombineThreads / kWave];
-  const int unit = blockIdx.x;  // b * H + h
-  const int b = unit / H;
-  const int h = unit - b * H;
+    const int32_t* __restrict__ prefix, const int32_t* __restrict__ seq_lens, int B, int H,
+    int max_seq_len, int G, float* __restrict__ o) {
+  const int groups = H / kBalancedMergeRows;
+  const int b = blockIdx.x / groups;
+  const int h = (blockIdx.x - b * groups) * kBalancedMergeRows + (threadIdx.x >> 5);
+  const int dim4 = threadIdx.x & 31;
   const int seq_len = seq_lens[b];
-  float* out_row = o + (size_t)unit * kHeadDim;
-  if (seq_len < 1 || seq_len > max_seq_len) {
-    fill_row(out_row, seq_len);
+  const long long P = prefix[b];
+  const int np = prefix[b + 1] - prefix[b];
+  const long long T = prefix[B];
+  float4* out = reinterpret_cast<float4*>(o + ((size_t)b * H + h) * kHeadDim) + dim4;
+  if (np == 0) {  // seq_len outside 1 .. max_seq_len
+    const float fill = seq_len < 1 ? 0.0f : NAN;
+    *out = make_float4(fill, fill, fill, fill);
     return;
   }
-  // P_b and T: page counts summed across the workgroup.
-  int before = 0, total = 0;
-  for (int i = threadIdx.x; i < B; i += kCombineThreads) {
-    const int n = seq_lens[i];
-    const int np = (n >= 1 && n <= max_seq_len) ? (n + kPage - 1) / kPage : 0;
-    total += np;
-    before += i < b ? np : 0;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    before += __shfl_xor(before, off);
-    total += __shfl_xor(total, off);
-  }
-  if ((threadIdx.x & (kWave - 1)) == 0) {
-    red[0][threadIdx.x >> 6] = before;
-    red[1][threadIdx.x >> 6] = total;
-  }
-  __syncthreads();
-  const long long P = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-  const long long T = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-  const long long last = P + (seq_len + kPage - 1) / kPage - 1;
   const int k0 = (int)(((P + 1) * G - 1) / T);
-  const int k1 = (int)(((last + 1) * G - 1) / T);
+  const int k1 = (int)(((P + np) * G - 1) / T);
   if (k0 == k1) return;
   const int n = k1 - k0 + 1;
-  merge_parts(part_acc, part_ml, BalancedParts{b, h, k0, H, T, (long long)G}, n, n, true, 0.0f,
-              out_row);
+  const BalancedParts parts{b, h, k0, H, T, (long long)G};
+  const float2* ml = reinterpret_cast<const float2*>(part_ml);
+  MergeState st;
+  for (int i0 = 0; i0 < n; i0 += kMergeChunk) {
+    float2 m_l[kMergeChunk];
+    float4 v[kMergeChunk];
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c) {
+      if (i0 + c < n) {
+        const size_t slot = parts.slot(i0 + c);
+        m_l[c] = ml[slot];
+        v[c] = reinterpret_cast<const float4*>(part_acc + slot * kHeadDim)[dim4];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMergeChunk; ++c)
+      if (i0 + c < n && parts.present(i0 + c)) st.fold(m_l[c].x, m_l[c].y, v[c]);
+  }
+  const float inv = 1.0f / st.l;
+  *out = make_float4(st.acc.x * inv, st.acc.y * inv, st.acc.z * inv, st.acc.w * inv);
 }
 
 // ------------------------------------------------------------ norm + RoPE + append
@@ -2394,10 +2406,18 @@ int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
   a.grid_splits = plan.mode == DAH_PLAN_SPLIT ? plan.grid_splits : 1;
   a.pages_per_split = plan.pages_per_split;
   a.o = o;
+  // Workspace: partial rows (128 floats each), their (max, sum) pairs, then
+  // for the balanced plan the page prefix sums.
   float* ws = static_cast<float*>(workspace);
-  const size_t rows = plan.workspace / ((kHeadDim + 2) * sizeof(float));  // partial rows
-  a.part_acc = plan.workspace > 0 ? ws : nullptr;
-  a.part_ml = plan.workspace > 0 ? ws + rows * kHeadDim : nullptr;
+  const size_t rows =
+      plan.mode == DAH_PLAN_BALANCED ? ((size_t)B + plan.workgroups - 1) * num_heads
+      : plan.mode == DAH_PLAN_SPLIT  ? (size_t)B * num_heads * plan.splits
+                                     : 0;
+  a.part_acc = rows > 0 ? ws : nullptr;
+  a.part_ml = rows > 0 ? ws + rows * kHeadDim : nullptr;
+  a.prefix = plan.mode == DAH_PLAN_BALANCED
+                 ? reinterpret_cast<int32_t*>(ws + rows * (kHeadDim + 2))
+                 : nullptr;
   if (step != nullptr) {
     a.k_new = step->k_new;
     a.v_new = step->v_new;
@@ -2420,9 +2440,10 @@ int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
   int st = check_launch("decode kernel");
   if (st != DAH_OK || plan.mode == DAH_PLAN_PER_SEQUENCE) return st;
   const int cblocks = B * num_heads;  // one workgroup per (sequence, head)
+  static_assert(kBalancedMergeRows == 2, "every head count is even");
   if (plan.mode == DAH_PLAN_BALANCED)
-    combine_balanced_kernel<<<cblocks, kCombineThreads, 0, stream>>>(
-        a.part_acc, a.part_ml, seq_lens, B, num_heads, max_seq_len, plan.workgroups, o);
+    combine_balanced_kernel<<<cblocks / kBalancedMergeRows, kBalancedMergeThreads, 0, stream>>>(
+        a.part_acc, a.part_ml, a.prefix, seq_lens, B, num_heads, max_seq_len, plan.workgroups, o);
   else
     combine_splits_kernel<<<cblocks, kCombineThreads, 0, stream>>>(
         a.part_acc, a.part_ml, seq_lens, B, num_heads, max_seq_len, plan.splits,

@@ -227,7 +227,7 @@ size_t dah_workspace_bytes_for(int B, int max_seq_len, int num_splits, int num_c
  * argument).  The *_ex calls are the calls above with the query-
  * head count num_heads in {16, 32, 40, 64} after B: q, q_out and o become
  * [B][num_heads][128], query head h reads KV head h / (num_heads / 8), and
- * the workspace scales with num_heads.  Everything else -- the cache pools,
+ * the workspace's partial results scale with num_heads.  Everything else -- the cache pools,
  * block table, sequence lengths, statuses -- is as above; num_heads outside
  * the set returns DAH_ERR_SHAPE.  The calls above are these with num_heads = 16.
  */

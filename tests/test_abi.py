@@ -113,7 +113,8 @@ def test_planner_is_consistent(B, L, n):
     else:
         assert mode == "balanced" and n == 0 and 64 <= B <= 4096
         assert p.workgroups == 256
-        assert p.workspace_bytes == (B + p.workgroups - 1) * slot_bytes
+        # partial slots, then B + 1 int32 page prefix sums for the merge
+        assert p.workspace_bytes == (B + p.workgroups - 1) * slot_bytes + (B + 1) * 4
     if n == 1:
         assert mode == "per_sequence"
     if n > 1:
@@ -270,12 +271,14 @@ def test_planner_ex_scales_the_workspace_with_heads(H, dt, B, L, n):
         # the matrix-core kernel takes the balanced plan from 32 sequences
         assert native.PLAN_MODES[ph.mode] == "balanced"
         assert native.PLAN_MODES[p16.mode] == "split"
-        assert ph.workspace_bytes == (B + ph.workgroups - 1) * H * 130 * 4
+        assert ph.workspace_bytes == (B + ph.workgroups - 1) * H * 130 * 4 + (B + 1) * 4
         return
-    # otherwise the cut of the positions does not depend on the head count
+    # otherwise the cut of the positions does not depend on the head count,
+    # and the partial slots scale with it (the balanced plan's prefix sums do not)
     assert (ph.mode, ph.splits, ph.pages_per_split, ph.workgroups) == \
         (p16.mode, p16.splits, p16.pages_per_split, p16.workgroups)
-    assert ph.workspace_bytes * 16 == p16.workspace_bytes * H
+    prefix = (B + 1) * 4 if native.PLAN_MODES[ph.mode] == "balanced" else 0
+    assert (ph.workspace_bytes - prefix) * 16 == (p16.workspace_bytes - prefix) * H
 
 
 @pytest.mark.parametrize("H", [0, 8, 15, 24, 48, 65, -16])
