@@ -395,6 +395,46 @@ def test_balanced_plan_with_more_workgroups_than_pages():
           label="balanced, T < G")
 
 
+@pytest.mark.parametrize("H", [16, 40])
+def test_balanced_out_of_domain_device_values(H):
+    """The balanced layout (its merge reads the page prefix sums the decode
+    leaves in the workspace) with out-of-domain device values: seq_len <= 0
+    gives o = 0, seq_len > max_seq_len or a page id outside the pool gives
+    o = NaN; every other sequence matches the per-sequence layout."""
+    import dataclasses
+    import torch
+    dah = _dah()
+    rng = np.random.default_rng(40)
+    lens = [int(x) for x in rng.integers(1, 2000, 80)]
+    lens[4] = 2000                   # spread over several workgroups
+    w = dataclasses.replace(_custom(len(lens), lens, dtype="bf16", seed=41), num_heads=H)
+    t, seq_lens, table, num_pages = build_layer(w)
+    L = int(max(lens))
+    assert dah.plan_decode(len(lens), L, num_heads=H, cache_dtype="bf16")["mode"] == "balanced"
+    sl = t["seq_lens"]
+    sl[1] = 0
+    sl[2] = -3
+    sl[3] = L + 1                    # above max_seq_len
+    t["block_table"][4, 3] = num_pages + 5
+
+    def step(n):
+        _, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], sl, L,
+                                    num_splits=n)
+        torch.cuda.synchronize()
+        return o
+
+    o_bal = step(0)
+    o_one = step(1)                  # the same append again (idempotent), one workgroup each
+    for o in (o_bal, o_one):
+        assert torch.equal(o[1], torch.zeros_like(o[1])) and torch.equal(o[2], torch.zeros_like(o[2]))
+        assert torch.isnan(o[3]).all() and torch.isnan(o[4]).all()
+    keep = [b for b in range(len(lens)) if b not in (1, 2, 3, 4)]
+    assert torch.isfinite(o_bal[keep]).all()
+    tol = 2.0 ** -16 * float(o_one[keep].abs().max())   # the matrix-core kernel's reference
+    assert torch.allclose(o_bal[keep], o_one[keep], atol=tol, rtol=0)
+
+
 @pytest.mark.parametrize("splits", [0, 1, 5])
 def test_balanced_ragged_batch_matches_oracle(splits):
     """A ragged batch of 96 sequences (1 .. 6000 positions, some sharing
