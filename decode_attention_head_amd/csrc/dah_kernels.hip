@@ -412,16 +412,17 @@ __device__ void step_q_out_only(const DecodeArgs& a, int b, int seq_len, int g, 
 // from registers and stores the new key and value in the cache.
 // qb: the row block of q and o (the sequence b for a decode; a chunk
 // token, attending over its own prefix of sequence b's pages, for chunks).
-template <int kDtype, bool kStep, int kG>
+template <int kDtype, bool kStep, int kG, int kGS = kG>
 __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb, int seq_len,
                                              int npages, int p0, int p1, bool write_q, bool to_o,
                                              size_t part_base, int part_stride, int g, int lane,
-                                             StepStash<kG>& stash) {
+                                             StepStash<kG>& stash, int h0 = 0) {
   constexpr int kH = kG * kKvHeads;
   const int wave = g;
   const int row = lane >> 4;
   const int col = lane & 15;
-  const size_t qrow0 = (size_t)qb * kH + g * kG;  // first query head row of this KV head
+  // This call's query heads: h0 .. h0 + kGS - 1 of the kG of KV head g.
+  const size_t qrow0 = (size_t)qb * kH + g * kG + h0;  // first query head row of the call
 
   // The block table is read-only for the whole launch: reading it through the
   // constant address space makes every (uniform) read a scalar load, counted
@@ -454,9 +455,9 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
   // The small per-wave loads go first: vector loads complete in order, so the
   // prologue's wait for them must not also wait for the first tile.
   // Query rows of this KV head, this lane's 8 dims (raw in the fused step).
-  float q[kG][8];
+  float q[kGS][8];
 #pragma unroll
-  for (int h = 0; h < kG; ++h) load8(a.q + (qrow0 + h) * kHeadDim + 8 * col, q[h]);
+  for (int h = 0; h < kGS; ++h) load8(a.q + (qrow0 + h) * kHeadDim + 8 * col, q[h]);
   float qw[8], kx[8], vx[8], kw8[8];
   if constexpr (kStep) {
     load8(a.q_gain + 8 * col, qw);
@@ -468,7 +469,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
   }
 
   // First tile in flight before the prologue's arithmetic.
-  constexpr bool kPrefetch = !(kDtype == DAH_F32 && kG == 5);
+  constexpr bool kPrefetch = !(kDtype == DAH_F32 && kGS == 5);
   Tile<kDtype> K0, V0, K1, V1;
   int id1 = bt[min(p0 + 1, last)];
   int id2 = bt[min(p0 + 2, last)];
@@ -488,11 +489,11 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
     float cr[8], sr[8];
     rope_table(pos, a.rope, lane, col, cr, sr);
 #pragma unroll
-    for (int h = 0; h < kG; ++h) {
+    for (int h = 0; h < kGS; ++h) {
       norm_rope_row(q[h], qw, a.eps, cr, sr, col);
-      if (write_q && row_writes(row, h)) {
-        stash.q[wave][h][0][col] = make_float4(q[h][0], q[h][1], q[h][2], q[h][3]);
-        stash.q[wave][h][1][col] = make_float4(q[h][4], q[h][5], q[h][6], q[h][7]);
+      if (write_q && row_writes(row, h0 + h)) {
+        stash.q[wave][h0 + h][0][col] = make_float4(q[h][0], q[h][1], q[h][2], q[h][3]);
+        stash.q[wave][h0 + h][1][col] = make_float4(q[h][4], q[h][5], q[h][6], q[h][7]);
       }
     }
     if (holds_last) {
@@ -511,13 +512,13 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
   // Pre-scale by log2(e)/sqrt(128) so that scores come out in log2 units for exp2.
   const float qscale = kLog2e * 0.08838834764831845f;  // 1/sqrt(128)
 #pragma unroll
-  for (int h = 0; h < kG; ++h)
+  for (int h = 0; h < kGS; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[h][e] *= qscale;
 
-  HeadState st[kG];
+  HeadState st[kGS];
 #pragma unroll
-  for (int h = 0; h < kG; ++h) st[h].init();
+  for (int h = 0; h < kGS; ++h) st[h].init();
 
   // Software pipeline over the pages: the tile of page p+1 is in flight while
   // page p is consumed.  In the steady-state loop both following pages exist,
@@ -537,9 +538,9 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
         V0.load(vbase + off, lane);
       }
       if (p == last && last_masked)
-        attend_tile<kDtype, true, kG>(K0, V0, q, st, row, last_valid);
+        attend_tile<kDtype, true, kGS>(K0, V0, q, st, row, last_valid);
       else
-        attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
+        attend_tile<kDtype, false, kGS>(K0, V0, q, st, row, kPage);
     }
   } else {
     int p = p0;
@@ -549,14 +550,14 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
       V1.load(vbase + off1, lane);
       const int id3 = bt[min(p + 3, last)];
       __builtin_amdgcn_sched_barrier(0);
-      attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
+      attend_tile<kDtype, false, kGS>(K0, V0, q, st, row, kPage);
       __builtin_amdgcn_sched_barrier(0);
       const int64_t off2 = offset_of(id2);
       K0.load(kbase + off2, lane);
       V0.load(vbase + off2, lane);
       const int id4 = bt[min(p + 4, last)];
       __builtin_amdgcn_sched_barrier(0);
-      attend_tile<kDtype, false, kG>(K1, V1, q, st, row, kPage);
+      attend_tile<kDtype, false, kGS>(K1, V1, q, st, row, kPage);
       __builtin_amdgcn_sched_barrier(0);
       id1 = id3;
       id2 = id4;
@@ -566,17 +567,17 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
       K1.load(kbase + off1, lane);
       V1.load(vbase + off1, lane);
       __builtin_amdgcn_sched_barrier(0);
-      attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
+      attend_tile<kDtype, false, kGS>(K0, V0, q, st, row, kPage);
       __builtin_amdgcn_sched_barrier(0);
       if (last_masked)
-        attend_tile<kDtype, true, kG>(K1, V1, q, st, row, last_valid);
+        attend_tile<kDtype, true, kGS>(K1, V1, q, st, row, last_valid);
       else
-        attend_tile<kDtype, false, kG>(K1, V1, q, st, row, kPage);
+        attend_tile<kDtype, false, kGS>(K1, V1, q, st, row, kPage);
     } else {
       if (last_masked)
-        attend_tile<kDtype, true, kG>(K0, V0, q, st, row, last_valid);
+        attend_tile<kDtype, true, kGS>(K0, V0, q, st, row, last_valid);
       else
-        attend_tile<kDtype, false, kG>(K0, V0, q, st, row, kPage);
+        attend_tile<kDtype, false, kGS>(K0, V0, q, st, row, kPage);
     }
   }
   if constexpr (kStep) {
@@ -595,7 +596,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
       unpack_slot<kDtype>(vw, vf);
       const bool mine = row == ((tail - 1) & 3);
 #pragma unroll
-      for (int h = 0; h < kG; ++h) {
+      for (int h = 0; h < kGS; ++h) {
         float sc = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) sc = fmaf(q[h][e], kf[e], sc);
@@ -606,17 +607,17 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
   }
 
 #pragma unroll
-  for (int h = 0; h < kG; ++h) {
+  for (int h = 0; h < kGS; ++h) {
     merge_rows(st[h]);
     if (bad_page) st[h].l = NAN;
   }
 #pragma unroll
-  for (int h = 0; h < kG; ++h) {
-    if (!row_writes(row, h)) continue;
+  for (int h = 0; h < kGS; ++h) {
+    if (!row_writes(row, h0 + h)) continue;
     if (to_o) {
       store8(a.o + (qrow0 + h) * kHeadDim + 8 * col, st[h].acc, 1.0f / st[h].l);
     } else {
-      const size_t part = part_base + (size_t)(g * kG + h) * part_stride;
+      const size_t part = part_base + (size_t)(g * kG + h0 + h) * part_stride;
       store8(a.part_acc + part * kHeadDim + 8 * col, st[h].acc, bad_page ? NAN : 1.0f);
       if (col == 0) reinterpret_cast<float2*>(a.part_ml)[part] = make_float2(st[h].m, st[h].l);
     }
@@ -624,14 +625,14 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
   if constexpr (kStep) {
     if (write_q) {
 #pragma unroll
-      for (int h = 0; h < kG; ++h) {
-        if (!row_writes(row, h)) continue;
+      for (int h = 0; h < kGS; ++h) {
+        if (!row_writes(row, h0 + h)) continue;
         float* qo = a.q_out + (qrow0 + h) * kHeadDim + 8 * col;
-        reinterpret_cast<float4*>(qo)[0] = stash.q[wave][h][0][col];
-        reinterpret_cast<float4*>(qo)[1] = stash.q[wave][h][1][col];
+        reinterpret_cast<float4*>(qo)[0] = stash.q[wave][h0 + h][0][col];
+        reinterpret_cast<float4*>(qo)[1] = stash.q[wave][h0 + h][1][col];
       }
     }
-    if (holds_last && row == 0) {
+    if (holds_last && row == 0 && h0 == 0) {
       // The new token's slot: page block_table[b][npages-1], slot tail - 1.
       const int id = bt[npages - 1];
       if (id >= 0 && id < a.num_pages) {
@@ -646,6 +647,27 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
         }
       }
     }
+  }
+}
+
+// decode_range over all kG query heads of the wave's KV head: for a float32
+// cache with 8 heads per KV head in two sweeps of 4 over the range (the
+// query rows, softmax states and two float32 tiles of all 8 heads do not fit
+// in registers; the second sweep reads the range's pages again).
+template <int kDtype, bool kStep, int kG>
+__device__ __forceinline__ void decode_range_heads(const DecodeArgs& a, int b, int qb,
+                                                   int seq_len, int npages, int p0, int p1,
+                                                   bool write_q, bool to_o, size_t part_base,
+                                                   int part_stride, int g, int lane,
+                                                   StepStash<kG>& stash) {
+  if constexpr (kDtype == DAH_F32 && kG == 8) {
+    decode_range<kDtype, kStep, kG, 4>(a, b, qb, seq_len, npages, p0, p1, write_q, to_o,
+                                       part_base, part_stride, g, lane, stash, 0);
+    decode_range<kDtype, kStep, kG, 4>(a, b, qb, seq_len, npages, p0, p1, write_q, to_o,
+                                       part_base, part_stride, g, lane, stash, 4);
+  } else {
+    decode_range<kDtype, kStep, kG>(a, b, qb, seq_len, npages, p0, p1, write_q, to_o, part_base,
+                                    part_stride, g, lane, stash);
   }
 }
 
@@ -1156,8 +1178,8 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_split_ker
                                  part_base, a.splits, g, lane, stash);
   } else {
     __shared__ StepStash<kG> stash;
-    decode_range<kDtype, kStep, kG>(a, b, b, seq_len, npages, p0, p1, split == 0, a.splits == 1,
-                                    part_base, a.splits, g, lane, stash);
+    decode_range_heads<kDtype, kStep, kG>(a, b, b, seq_len, npages, p0, p1, split == 0,
+                                          a.splits == 1, part_base, a.splits, g, lane, stash);
   }
 }
 
@@ -1248,8 +1270,8 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void decode_balanced_
       decode_range_mfma<kStep, kG>(a, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
                                    (size_t)(b + k) * kH, 1, g, lane_i, stash);
     else
-      decode_range<kDtype, kStep, kG>(a, b, b, a.seq_lens[b], npages, p0, p1, p0 == 0, whole,
-                                      (size_t)(b + k) * kH, 1, g, lane_i, stash);
+      decode_range_heads<kDtype, kStep, kG>(a, b, b, a.seq_lens[b], npages, p0, p1, p0 == 0,
+                                            whole, (size_t)(b + k) * kH, 1, g, lane_i, stash);
     s = seg_end;
     if (s >= e) break;
     do { ++b; } while (prefix[b + 1] == prefix[b]);  // next sequence with pages
@@ -1781,8 +1803,8 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void chunk_valu_kerne
   }
   const int len = seq_len - n + i + 1;  // positions 0 .. the token's own
   const int npages = (len + kPage - 1) / kPage;
-  decode_range<DAH_F32, false, kG>(a, b, t0 + i, len, npages, 0, npages, false, true, 0, 0, g,
-                                   lane, stash);
+  decode_range_heads<DAH_F32, false, kG>(a, b, t0 + i, len, npages, 0, npages, false, true, 0,
+                                         0, g, lane, stash);
 }
 
 // The weighted V sum of the shared-page kernel, transposed: D = V^T W^T with
