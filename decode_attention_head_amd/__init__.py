@@ -136,6 +136,11 @@ def plan_decode(B: int, max_seq_len: int, num_splits: int = 0, num_cus: int | No
 def workspace_bytes(B: int, max_seq_len: int, num_splits: int = 0,
                     num_cus: int | None = None, num_heads: int = NUM_HEADS,
                     cache_dtype="bf16") -> int:
+    """Bytes of device workspace paged_decode_gqa / decode_attn_step need for
+    these arguments: the partial results of cut sequences (and, under the
+    balanced plan, the batch's page prefix sums); 0 when no sequence is cut.
+    The contents need no initialisation.  num_cus: plan for that many compute
+    units instead of the current device's."""
     if num_heads != NUM_HEADS or _dtype_code(cache_dtype) != DAH_BF16:
         if num_cus is None:
             return int(lib().dah_workspace_bytes_ex(B, num_heads, _dtype_code(cache_dtype),
