@@ -458,3 +458,59 @@ def test_balanced_ragged_batch_matches_oracle(splits):
                          label=f"ragged step, splits={splits}")
     assert float(np.max(np.abs(q_out.cpu().numpy() - ref["q_out"]))) <= 1e-5
     _print(f"  ragged step splits={splits}: max abs {e_abs:.3g} rel {e_rel:.3g}")
+
+
+@pytest.mark.parametrize("H,splits", [(16, 0), (40, 0), (16, 5), (16, 1)])
+def test_step_under_graph_replay(H, splits):
+    """decode_attn_step captured in one HIP graph under the balanced plan
+    (the merge reads the prefix sums the decode leaves in the workspace),
+    fixed splits and one workgroup per sequence: every replay, with eager
+    work and synchronisations between replays, equals the eager result bit
+    for bit.  The cache is restored before each run."""
+    import dataclasses
+    import torch
+    dah = _dah()
+    rng = np.random.default_rng(42)
+    lens = [int(x) for x in rng.integers(1, 1500, 80)]
+    w = dataclasses.replace(_custom(len(lens), lens, dtype="bf16", seed=43), num_heads=H)
+    t, seq_lens, table, _ = build_layer(w)
+    L = int(max(lens))
+    plan = dah.plan_decode(len(lens), L, splits, num_heads=H, cache_dtype="bf16")
+    assert plan["mode"] == {0: "balanced", 5: "split", 1: "per_sequence"}[splits]
+    ws = torch.empty(max(dah.workspace_bytes(len(lens), L, splits, num_heads=H,
+                                             cache_dtype="bf16"), 256),
+                     dtype=torch.uint8, device="cuda")
+    q_out, o = torch.empty_like(t["q"]), torch.empty_like(t["q"])
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+
+    def step():
+        dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                             t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L,
+                             num_splits=splits, q_out=q_out, o=o, workspace=ws)
+
+    def restore():
+        t["k_pool"].copy_(k0)
+        t["v_pool"].copy_(v0)
+
+    step()
+    torch.cuda.synchronize()
+    want_o, want_q, want_k = o.clone(), q_out.clone(), t["k_pool"].clone()
+    restore()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        restore()
+        o.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, want_o), f"replay {i}: o differs"
+        assert torch.equal(q_out, want_q), f"replay {i}: q_out differs"
+        assert torch.equal(t["k_pool"], want_k), f"replay {i}: cache differs"
+        _ = (t["q"] * 2).sum().item()   # eager work between replays
