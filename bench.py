@@ -71,7 +71,8 @@ def parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="time paged_decode_gqa alone (profiling aid)")
     ap.add_argument("--no-read-probe", action="store_true",
-                    help="skip the streaming-read probe (practical bandwidth ceiling)")
+                    help="skip the streaming-read probe (practical bandwidth ceiling) and the "
+                         "paged-read probe (the decode's access pattern alone)")
     ap.add_argument("--chunk", type=int, default=0, metavar="N",
                     help="also time chunk_attn_step with N new tokens per sequence")
     ap.add_argument("--layer", action="store_true",
@@ -362,6 +363,26 @@ def main():
         probe_gbs = round(best, 1)
 
     kv_bytes = W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)   # per layer
+    paged_gbs = None
+    if not args.no_read_probe and plan["mode"] == "per_sequence":
+        # The decode's own access pattern without its arithmetic (one
+        # workgroup per sequence, wave g reading head g's tiles of every page):
+        # the ceiling of that pattern, for the one-workgroup-per-sequence plan.
+        from decode_attention_head_amd.probes import probe_paged_read
+        sink = torch.empty(8 * B, dtype=torch.int32, device=dev)
+
+        def paged():
+            probe_paged_read(t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], L, sink)
+        for _ in range(2):
+            paged()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(10):
+            paged()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        # the same algorithmic K/V bytes as `achieved`
+        paged_gbs = round(10 * kv_bytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9, 1)
     gbs = nl * kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (launch_ms * 1e-3) / 1e9
     traffic = read_traffic(w.name) if (args.num_splits == 0 and not args.decode_only) else None
@@ -417,6 +438,8 @@ def main():
             "launches_timed": len(starts),
             "probe_read_gbs": probe_gbs,
             "frac_of_probe_read": None if not probe_gbs else round(achieved / probe_gbs, 4),
+            "paged_read_gbs": paged_gbs,
+            "frac_of_paged_read": None if not paged_gbs else round(achieved / paged_gbs, 4),
             "algorithmic_bytes_per_launch": kv_bytes,
         },
         "cpu_baseline": cpu,

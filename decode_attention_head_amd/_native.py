@@ -68,6 +68,8 @@ SIGNATURES = {
 PROBE_SIGNATURES = {
     "dah_probe_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
     "dah_probe_read": (_c_int, [_vp, _c_size, _vp, _c_int, _vp]),
+    "dah_probe_paged_read": (_c_int, [_vp, _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int, _c_int,
+                                      _vp, _vp]),
 }
 
 _LIB = None

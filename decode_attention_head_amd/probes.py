@@ -46,3 +46,31 @@ def probe_read(src, sink, blocks: int, stream=None) -> int:
     check(probe_lib().dah_probe_read(src.data_ptr(), n, sink.data_ptr(), blocks,
                                      _stream(src, stream)), "dah_probe_read")
     return n
+
+
+def probe_paged_read(k_cache, v_cache, block_table, seq_lens, max_seq_len: int, sink,
+                     stream=None) -> None:
+    """Read the batch's cached pages through the block table in the decode
+    kernel's arrangement (include/dah_probe.h) without its arithmetic.  Pools
+    [num_pages, 8, 16, 128] (float32 or bfloat16), int32 block_table [B, P] and
+    seq_lens [B] on the GPU; sink an int32 GPU tensor of at least B * 8
+    elements.  Only launches (no synchronisation), so that it can be timed
+    back to back."""
+    import torch
+    if not all(t.is_cuda and t.is_contiguous() for t in (k_cache, v_cache, block_table, seq_lens,
+                                                          sink)):
+        raise ValueError("probe_paged_read needs contiguous GPU tensors")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or \
+            k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (8, 16, 128):
+        raise ValueError("probe_paged_read: pools of shape [num_pages, 8, 16, 128] expected")
+    if k_cache.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("probe_paged_read: float32 or bfloat16 pools")
+    B = block_table.shape[0]
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or \
+            seq_lens.shape != (B,) or sink.dtype != torch.int32 or sink.numel() < 8 * B:
+        raise ValueError("probe_paged_read: int32 block_table [B, P], seq_lens [B], sink >= 8 B")
+    dtype = 1 if k_cache.dtype == torch.bfloat16 else 0
+    check(probe_lib().dah_probe_paged_read(
+        k_cache.data_ptr(), v_cache.data_ptr(), dtype, k_cache.shape[0], block_table.data_ptr(),
+        block_table.shape[1], seq_lens.data_ptr(), B, int(max_seq_len), sink.data_ptr(),
+        _stream(k_cache, stream)), "dah_probe_paged_read")

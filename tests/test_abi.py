@@ -61,6 +61,12 @@ def test_probe_library_exports_every_declared_symbol():
     assert plib.dah_probe_copy(A + 4, A, 16, None) == 4
     assert plib.dah_probe_read(A, 0, A, 1, None) == 2
     assert plib.dah_probe_read(A, 16, A, 0, None) == 2
+    # paged read: NULL, unknown dtype, B < 1, max_seq_len past the table, misaligned pool
+    assert plib.dah_probe_paged_read(None, A, 1, 16, A, 4, A, 2, 64, A, None) == 1
+    assert plib.dah_probe_paged_read(A, A, 7, 16, A, 4, A, 2, 64, A, None) == 3
+    assert plib.dah_probe_paged_read(A, A, 1, 16, A, 4, A, 0, 64, A, None) == 2
+    assert plib.dah_probe_paged_read(A, A, 1, 16, A, 4, A, 2, 65, A, None) == 2
+    assert plib.dah_probe_paged_read(A + 4, A, 1, 16, A, 4, A, 2, 64, A, None) == 4
 
 
 def test_header_constants_match_spec_fixture():
