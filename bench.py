@@ -172,11 +172,16 @@ def time_block(dah, torch, w, t, L, ws, stream, args):
     q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
     q_out, o = torch.empty_like(q), torch.empty_like(q)
     y = torch.empty((B, hid), dtype=torch.float32, device=o.device)
+    o_ws = torch.empty(max(dah.linear_workspace_bytes(B, hid, H * W.HEAD_DIM), 256),
+                       dtype=torch.uint8, device=o.device)
 
     def qkv():
         dah.qkv_proj(p["x"], p["w_qkv"], H, q=q, k=k, v=v)
 
     def oproj():
+        dah.o_proj_ws(o, p["w_o"], y=y, workspace=o_ws)
+
+    def oproj_unsplit():
         dah.o_proj(o, p["w_o"], y=y)
 
     def step():
@@ -191,6 +196,7 @@ def time_block(dah, torch, w, t, L, ws, stream, args):
 
     n = 20
     qkv_us, o_us = _graph_us(torch, qkv, n), _graph_us(torch, oproj, n)
+    o_unsplit_us = _graph_us(torch, oproj_unsplit, n)
     step_us, whole_us = _graph_us(torch, step, n), _graph_us(torch, whole, n)
 
     def stats(us, n_out, k_in):
@@ -199,10 +205,14 @@ def time_block(dah, torch, w, t, L, ws, stream, args):
         return {"us": round(us, 2), "bytes": byts, "gbs": round(byts / us / 1e3, 1),
                 "tflops": round(flop / us / 1e6, 2)}
     n_qkv = (H + 2 * W.NUM_KV_HEADS) * W.HEAD_DIM
+    o_kernel, o_slices = dah.linear_ws_kernel(B, hid, H * W.HEAD_DIM)
     return {"qkv_proj": stats(qkv_us, n_qkv, hid), "o_proj": stats(o_us, hid, H * W.HEAD_DIM),
+            "o_proj_unsplit_us": round(o_unsplit_us, 2), "o_proj_k_slices": o_slices,
+            "o_proj_kernel": o_kernel,
             "step_us": round(step_us, 2), "block_us": round(whole_us, 2), "hidden": hid,
             "timing": "HIP graph replay of 20 calls, mean per call",
-            "note": "x [B,hidden] f32, bf16 weights; block = qkv_proj + decode_attn_step + o_proj"}
+            "note": "x [B,hidden] f32, bf16 weights; block = qkv_proj + decode_attn_step + "
+                    "o_proj_ws (k split into a workspace, the reduce included)"}
 
 
 def time_layer(dah, torch, w, t, L, args):

@@ -12,6 +12,7 @@ computation runs in the library's HIP kernels.
     decoder_layer_step   a whole layer around the block (norms, residuals, SwiGLU MLP)
     qkv_proj, o_proj     nodes attn.qkv_proj and attn.o_proj around them
     linear               the product both use (float32 x, bfloat16 weights)
+    linear_ws, o_proj_ws the same with k split over workgroups (a workspace)
 
 (Node names from the "Qwen3-0.6B" Model Spec page, "Compute-graph nodes".)
 
@@ -32,7 +33,8 @@ from ._native import DAH_BF16, DAH_F32, DahError, LIB_PATH, check, lib
 __all__ = [
     "qk_norm_rope_append", "paged_decode_gqa", "decode_attn_step", "plan_decode",
     "workspace_bytes", "DahError", "LIB_PATH", "NUM_HEADS", "NUM_KV_HEADS", "HEAD_DIM",
-    "PAGE_SIZE", "HEAD_COUNTS", "linear", "qkv_proj", "o_proj", "chunk_attn_step", "rmsnorm",
+    "PAGE_SIZE", "HEAD_COUNTS", "linear", "linear_ws", "linear_kernel", "linear_ws_kernel",
+    "linear_workspace_bytes", "qkv_proj", "o_proj", "o_proj_ws", "chunk_attn_step", "rmsnorm",
     "silu_mul", "decoder_layer_step", "layer_workspace_bytes", "LAYER_WEIGHTS",
 ]
 
@@ -288,6 +290,54 @@ def linear_kernel(T: int, N: int, K: int) -> int:
     return int(lib().dah_linear_kernel(int(T), int(N), int(K)))
 
 
+def linear_workspace_bytes(T: int, N: int, K: int) -> int:
+    """Workspace bytes dah_linear_ws needs for a T x N x K product (0 when it
+    does not split k)."""
+    return int(lib().dah_linear_workspace_bytes(int(T), int(N), int(K)))
+
+
+def linear_ws_kernel(T: int, N: int, K: int):
+    """(kernel, k slices) dah_linear_ws launches for a T x N x K product
+    (host only; kernel ids as linear_kernel)."""
+    ks = ctypes.c_int(0)
+    kernel = int(lib().dah_linear_ws_kernel(int(T), int(N), int(K), ctypes.byref(ks)))
+    return kernel, int(ks.value)
+
+
+def _linear_workspace(workspace, T, N, K, device):
+    torch = _torch()
+    need = linear_workspace_bytes(T, N, K)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _require(workspace, "workspace", workspace.dtype, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def linear_ws(x, w, *, residual=None, y=None, workspace=None, stream=None):
+    """y [T,N] = x [T,K] . w^T (+ residual [T,N]) with k split over
+    workgroups into a workspace (dah_linear_ws); the workspace (uint8, at
+    least linear_workspace_bytes) is allocated when not given."""
+    torch = _torch()
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("linear_ws: x must be [T,K] and w [N,K]")
+    T, K = x.shape
+    N = w.shape[0]
+    _require(x, "x", torch.float32, (T, K))
+    _require_weights(w, "w", (N, K), x.device)
+    if residual is not None:
+        _require(residual, "residual", torch.float32, (T, N), x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    _require(y, "y", torch.float32, (T, N), x.device)
+    ws, ws_bytes = _linear_workspace(workspace, T, N, K, x.device)
+    check(lib().dah_linear_ws(_ptr(x), _ptr(w), None if residual is None else _ptr(residual), T, N,
+                              K, _ptr(y), None if ws is None else _ptr(ws), ws_bytes,
+                              _stream(x.device, stream)), "dah_linear_ws")
+    return y
+
+
 def qkv_proj(x, w_qkv, num_heads: int = NUM_HEADS, *, q=None, k=None, v=None, stream=None):
     """attn.qkv_proj: x [T,hidden] float32, w_qkv [H*128 + 2048, hidden] bfloat16
     (q_proj, k_proj, v_proj rows stacked) -> (q [T,H,128], k [T,8,128],
@@ -326,6 +376,27 @@ def o_proj(o, w_o, *, y=None, stream=None):
     _require(y, "y", torch.float32, (T, hidden), o.device)
     check(lib().attn_o_proj(_ptr(o), _ptr(w_o), T, H, hidden, _ptr(y), _stream(o.device, stream)),
           "attn_o_proj")
+    return y
+
+
+def o_proj_ws(o, w_o, *, y=None, workspace=None, stream=None):
+    """o_proj with k split over workgroups into a workspace (attn_o_proj_ws;
+    linear_workspace_bytes(T, hidden, H*128) bytes, allocated when not
+    given)."""
+    torch = _torch()
+    if o.dim() != 3:
+        raise ValueError("o_proj_ws: o must be [T,H,128]")
+    T, H = o.shape[0], _heads(o)
+    hidden = w_o.shape[0]
+    _require(o, "o", torch.float32, (T, H, HEAD_DIM))
+    _require_weights(w_o, "w_o", (hidden, H * HEAD_DIM), o.device)
+    if y is None:
+        y = torch.empty((T, hidden), dtype=torch.float32, device=o.device)
+    _require(y, "y", torch.float32, (T, hidden), o.device)
+    ws, ws_bytes = _linear_workspace(workspace, T, hidden, H * HEAD_DIM, o.device)
+    check(lib().attn_o_proj_ws(_ptr(o), _ptr(w_o), T, H, hidden, _ptr(y),
+                               None if ws is None else _ptr(ws), ws_bytes,
+                               _stream(o.device, stream)), "attn_o_proj_ws")
     return y
 
 

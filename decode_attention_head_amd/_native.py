@@ -52,6 +52,10 @@ SIGNATURES = {
     "attn_o_proj": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "dah_linear_residual": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "dah_linear_kernel": (_c_int, [_c_int, _c_int, _c_int]),
+    "dah_linear_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "dah_linear_ws": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+    "attn_o_proj_ws": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+    "dah_linear_ws_kernel": (_c_int, [_c_int, _c_int, _c_int, _vp]),
     "dah_rmsnorm_linear": (_c_int, [_vp, _vp, _c_float, _vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "dah_rmsnorm": (_c_int, [_vp, _vp, _c_float, _c_int, _c_int, _vp, _vp]),
     "dah_silu_mul": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),

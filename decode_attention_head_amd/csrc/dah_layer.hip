@@ -82,10 +82,18 @@ int check_launch(const char* what) {
 
 size_t round_up(size_t n) { return (n + 255) / 256 * 256; }
 
-// Workspace of the layer: intermediates, then the attention's own workspace.
+// Workspace of the layer: intermediates, then one region for the
+// attention's own workspace and, once the attention is done with it (the
+// launches are stream-ordered), the k-slice partials of o_proj and down.
 struct LayerBuffers {
   size_t q, k, v, q_out, o, x1, gu, act, attn, total;
 };
+
+size_t shared_region(int B, int hidden, int inter, int num_heads, size_t attn_ws) {
+  const size_t o_split = dah_linear_workspace_bytes(B, hidden, num_heads * dah::kHeadDim);
+  const size_t down_split = dah_linear_workspace_bytes(B, hidden, inter);
+  return std::max(attn_ws, std::max(o_split, down_split));
+}
 
 LayerBuffers layer_buffers(int B, int hidden, int inter, int num_heads, size_t attn_ws) {
   LayerBuffers L = {};
@@ -104,7 +112,7 @@ LayerBuffers layer_buffers(int B, int hidden, int inter, int num_heads, size_t a
   L.x1 = take((size_t)B * hidden * f);
   L.gu = take((size_t)B * 2 * inter * f);
   L.act = take((size_t)B * inter * f);
-  L.attn = take(attn_ws);
+  L.attn = take(shared_region(B, hidden, inter, num_heads, attn_ws));
   L.total = at;
   return L;
 }
@@ -194,22 +202,26 @@ int decoder_layer_step(const float* x, const dah_layer_weights* w, int hidden, i
   float* gu = reinterpret_cast<float*>(ws + L.gu);
   float* act = reinterpret_cast<float*>(ws + L.act);
   void* attn_ws = attn > 0 ? ws + L.attn : nullptr;
+  const size_t split = shared_region(B, hidden, inter, num_heads, 0);
+  void* split_ws = split > 0 ? ws + L.attn : nullptr;
   const int qdim = num_heads * dah::kHeadDim;
 
-  // Six launches: input_norm folded into qkv_proj and post_attn_norm into
-  // gate_up (the products norm their input rows as they stream them), the
-  // residual adds into the stores of o_proj and down.  mlp.act keeps its own
+  // Six launches (eight when o_proj and down split k): input_norm folded
+  // into qkv_proj and post_attn_norm into gate_up (the products norm their
+  // input rows as they stream them), the residual adds into the stores of
+  // o_proj and down (or into their slice sums).  mlp.act keeps its own
   // kernel: folded into down it would be redone once per column tile.
   st = dah::qkv_proj(x, w->w_in, eps, w->w_qkv, B, hidden, num_heads, q, k, v, stream);
   if (st == DAH_OK)
     st = decode_attn_step_ex(q, k, v, w->q_gain, w->k_gain, eps, rope_theta, k_cache, v_cache,
                              cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
                              num_heads, max_seq_len, num_splits, q_out, o, attn_ws, attn, stream);
-  if (st == DAH_OK) st = dah_linear_residual(o, w->w_o, x, B, hidden, qdim, x1, stream);
+  if (st == DAH_OK) st = dah_linear_ws(o, w->w_o, x, B, hidden, qdim, x1, split_ws, split, stream);
   if (st == DAH_OK)
     st = dah_rmsnorm_linear(x1, w->w_post, eps, w->w_gate_up, B, 2 * inter, hidden, gu, stream);
   if (st == DAH_OK) st = dah_silu_mul(gu, B, inter, act, stream);
-  if (st == DAH_OK) st = dah_linear_residual(act, w->w_down, x1, B, hidden, inter, y, stream);
+  if (st == DAH_OK)
+    st = dah_linear_ws(act, w->w_down, x1, B, hidden, inter, y, split_ws, split, stream);
   return st;
 }
 

@@ -77,6 +77,14 @@ struct LinearArgs {
   int x_stride;         // floats per row of x
   const float* x_gain;  // kNorm: the norm's gain [K]
   float eps;            // kNorm
+  // k slices (linear_lds_kernel): workgroup blockIdx.x takes output tile
+  // blockIdx.x mod (the number of tiles) over k slice blockIdx.x / (the
+  // number of tiles), an equal 1 / ksplit of k.  With ksplit > 1 (kPlain,
+  // one segment only) each slice's products go to part[slice][T][N] and
+  // linear_reduce_kernel adds them, in slice order, and the segment's
+  // residual.
+  int ksplit;
+  float* part;
 };
 
 // What the products read as their input row x[t] (the kernels' kXMode):
@@ -348,9 +356,12 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
   const int wm = wave % kWM, wn = (wave / kWM) % kWN, wk = wave / (kWM * kWN);
   const int r = lane >> 4, c = lane & 15;
   const int n_tiles = a.N / kBN;
-  const int n0 = (blockIdx.x % n_tiles) * kBN;
-  const int m0 = (blockIdx.x / n_tiles) * kBM;
-  const int chunks = a.K / kBK;
+  const int tiles = ((a.T + kBM - 1) / kBM) * n_tiles;
+  const int tile = blockIdx.x % tiles, slice = blockIdx.x / tiles;
+  const int n0 = (tile % n_tiles) * kBN;
+  const int m0 = (tile / n_tiles) * kBM;
+  const int chunks = a.K / kBK / a.ksplit;
+  const int k_base = slice * chunks * kBK;
 
   // Coalesced tile loads: consecutive threads take consecutive 16 bytes of
   // a row.  Rows of x past T read as zero.
@@ -361,13 +372,13 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
     const int idx = tid + kLdsThreads * i;
     const int row = idx / (kBK / 4), t = m0 + row;
     xok[i] = t < a.T;
-    xsrc[i] = a.x + (size_t)(xok[i] ? t : 0) * a.x_stride + 4 * (idx % (kBK / 4));
+    xsrc[i] = a.x + (size_t)(xok[i] ? t : 0) * a.x_stride + k_base + 4 * (idx % (kBK / 4));
   }
   const uint16_t* wsrc[kW8];
 #pragma unroll
   for (int i = 0; i < kW8; ++i) {
     const int idx = tid + kLdsThreads * i;
-    wsrc[i] = a.w + (size_t)(n0 + idx / (kBK / 8)) * a.K + 8 * (idx % (kBK / 8));
+    wsrc[i] = a.w + (size_t)(n0 + idx / (kBK / 8)) * a.K + k_base + 8 * (idx % (kBK / 8));
   }
   struct Chunk {
     float4 x[kX4];
@@ -380,7 +391,8 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
     for (int i = 0; i < kX4; ++i) {
       b.x[i] = xok[i] ? *reinterpret_cast<const float4*>(xsrc[i] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (kXMode == kNorm)
-        b.g[i] = *reinterpret_cast<const float4*>(a.x_gain + k + 4 * ((tid + kLdsThreads * i) % (kBK / 4)));
+        b.g[i] = *reinterpret_cast<const float4*>(a.x_gain + k_base + k +
+                                                  4 * ((tid + kLdsThreads * i) % (kBK / 4)));
     }
 #pragma unroll
     for (int i = 0; i < kW8; ++i) b.w[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + k);
@@ -457,7 +469,8 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
     }
   }
 
-  const Segment sg = segment_of(a, n0);
+  const Segment sg = a.ksplit > 1 ? Segment{a.part + (size_t)slice * a.T * a.N, 0, a.N, nullptr}
+                                  : segment_of(a, n0);
   // kNorm: the rows' inverse RMS.  The kBK / 4 consecutive threads that stage
   // one row's chunk hold its sum of squares between them.
   __shared__ float row_scale[kXMode == kNorm ? kBM : 1];
@@ -515,9 +528,42 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- k slices
+
+// y = part[0] + ... + part[kS - 1] (+ res), added in slice order; one float4
+// per thread, every slice's load in flight at once.  part [kS][n4] float4,
+// y and res [n4] float4 (res may be y: each thread reads its own element
+// before it writes it).
+template <int kS>
+__global__ __launch_bounds__(256) void linear_reduce_kernel(const float4* part, size_t n4,
+                                                            const float4* res, float4* y) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 v[kS];
+#pragma unroll
+  for (int q = 0; q < kS; ++q) v[q] = part[q * n4 + i];
+  float4 sum = v[0];
+#pragma unroll
+  for (int q = 1; q < kS; ++q) {
+    sum.x += v[q].x;
+    sum.y += v[q].y;
+    sum.z += v[q].z;
+    sum.w += v[q].w;
+  }
+  if (res != nullptr) {
+    const float4 r = res[i];
+    sum.x += r.x;
+    sum.y += r.y;
+    sum.z += r.z;
+    sum.w += r.w;
+  }
+  y[i] = sum;
+}
+
 struct LinearConfig {
   int lds;          // 0: linear_splitk_kernel<mb, nb, mw>; else an LDS tile shape, by id
   int mb, nb, mw;
+  int ksplit = 1;   // k slices
 };
 
 // An LDS tile shape needs N, and every output segment's first column, to be
@@ -572,12 +618,50 @@ LinearConfig pick_config(const LinearArgs& a, int x_mode = kPlain) {
   return {0, 1, 1, 1};
 }
 
+// With a workspace for k slices (plain products into one segment), products
+// with K >= 2048 also consider splitting k: the largest LDS tile (64 x 128,
+// 64 x 64, 32 x 64, 32 x 32) whose tiles times 1, 4 or 8 slices (the
+// fewest) reach 512 workgroups with slices of 384 k or more; failing that,
+// 32 x 32 tiles over 8 slices (or 4) of 256 k or more.  (Two slices would
+// only pay for T < 32 with N >= 32768.)
+// Shorter k keeps pick_config's choice.  Swept on MI355X over T = 16 .. 512
+// and (N, K) = (1024, 2048 .. 8192), (4096 .. 10240, 1024), slices 1-8 on
+// every tile shape (back-to-back launch times, the reduce included): this
+// rule is within 4% of the fastest configuration wherever it splits, and up
+// to 2.4x faster than the unsplit choice (T = 16, N = 1024, K = 5120).
+constexpr int kSplitMinK = 2048;
+LinearConfig pick_split_config(const LinearArgs& a) {
+  if (a.K >= kSplitMinK) {
+    static const int kShapeBM[5] = {64, 64, 32, 32, 32}, kShapeBN[5] = {128, 64, 64, 32, 32};
+    static const int kShapeBK[5] = {64, 64, 64, 128, 256};
+    auto tiles = [&](int id) {
+      return (long long)((a.T + kShapeBM[id - 1] - 1) / kShapeBM[id - 1]) * (a.N / kShapeBN[id - 1]);
+    };
+    if (a.T >= 32)
+      for (int id = 1; id <= 3; ++id)
+        if (lds_fits(a, kShapeBN[id - 1], kShapeBK[id - 1]) && tiles(id) >= 512) return {id, 0, 0, 0, 1};
+    for (int id = 1; id <= 4; ++id)
+      for (int ks = 4; ks <= 8; ks *= 2)
+        if (a.K / ks >= 384 && lds_fits(a, kShapeBN[id - 1], kShapeBK[id - 1] * ks) &&
+            tiles(id) * ks >= 512)
+          return {id, 0, 0, 0, ks};
+    for (int ks = 8; ks >= 4; ks /= 2)
+      if (a.K / ks >= 256 && lds_fits(a, 32, 128 * ks)) return {(a.K / ks) % 512 == 0 ? 5 : 4, 0, 0, 0, ks};
+  }
+  return pick_config(a);
+}
+
+// Bytes of k-slice partial products a configuration needs.
+size_t split_bytes(const LinearArgs& a, const LinearConfig& c) {
+  return c.ksplit > 1 ? (size_t)c.ksplit * a.T * a.N * sizeof(float) : 0;
+}
+
 template <int kBM, int kBN, int kWM, int kWN, int kWK, int kKS, int kDepth, int kXMode>
 int launch_lds(const LinearArgs& a, hipStream_t stream) {
-  if (!lds_fits(a, kBN, 32 * kKS * kWK))
+  if (!lds_fits(a, kBN, 32 * kKS * kWK * a.ksplit))
     return dah::set_error(DAH_ERR_SHAPE, "linear: tile %dx%d does not divide N=%d, K=%d", kBM,
                           kBN, a.N, a.K);
-  const long long groups = (long long)((a.T + kBM - 1) / kBM) * (a.N / kBN);
+  const long long groups = (long long)((a.T + kBM - 1) / kBM) * (a.N / kBN) * a.ksplit;
   if (groups > INT32_MAX) return dah::set_error(DAH_ERR_SHAPE, "linear: grid too large");
   linear_lds_kernel<kBM, kBN, kWM, kWN, kWK, kKS, kDepth, kXMode>
       <<<dim3((unsigned)groups), kLdsThreads, 0, stream>>>(a);
@@ -597,10 +681,13 @@ int launch_lds_shape(int id, const LinearArgs& a, hipStream_t stream) {
 }
 
 template <int kMB, int kNB, int kMW, int kXMode>
-void launch_cfg(const LinearArgs& a, hipStream_t stream) {
+int launch_cfg(const LinearArgs& a, hipStream_t stream) {
   const int rows = 16 * kMB * kMW;
-  const dim3 grid(((a.T + rows - 1) / rows) * (a.N / (16 * kNB)));
-  linear_splitk_kernel<kMB, kNB, kMW, kXMode><<<grid, kWave * kLinWaves, 0, stream>>>(a);
+  const long long groups = (long long)((a.T + rows - 1) / rows) * (a.N / (16 * kNB));
+  if (groups > INT32_MAX) return dah::set_error(DAH_ERR_SHAPE, "linear: grid too large");
+  linear_splitk_kernel<kMB, kNB, kMW, kXMode>
+      <<<dim3((unsigned)groups), kWave * kLinWaves, 0, stream>>>(a);
+  return DAH_OK;
 }
 
 template <int kXMode>
@@ -608,7 +695,7 @@ int launch_mode(const LinearArgs& a, const LinearConfig& c, hipStream_t stream) 
   if (c.lds != 0) return launch_lds_shape<kXMode>(c.lds, a, stream);
   // The instantiated shapes; N is a multiple of 64, so every column tiling divides it.
 #define DAH_LIN_CASE(MB, NB, MW) \
-  if (c.mb == MB && c.nb == NB && c.mw == MW) { launch_cfg<MB, NB, MW, kXMode>(a, stream); return DAH_OK; }
+  if (c.mb == MB && c.nb == NB && c.mw == MW) return launch_cfg<MB, NB, MW, kXMode>(a, stream);
   DAH_LIN_CASE(1, 1, 1)
   DAH_LIN_CASE(2, 1, 1)
   DAH_LIN_CASE(2, 2, 1)
@@ -619,17 +706,43 @@ int launch_mode(const LinearArgs& a, const LinearConfig& c, hipStream_t stream) 
   return dah::set_error(DAH_ERR_HIP, "linear: no kernel for tile %d/%d/%d", c.mb, c.nb, c.mw);
 }
 
-// x_mode: kPlain or kNorm (a.x_gain, a.eps set); sets a.x_stride.
-int launch_linear(LinearArgs& a, hipStream_t stream, int x_mode = kPlain) {
+// The product under configuration c; with c.ksplit > 1 (kPlain, one
+// segment starting at column 0) the slices' partial products go to part
+// [ksplit][T][N] float32 and linear_reduce_kernel writes the segment.
+// Sets a.x_stride, a.ksplit and a.part.
+int launch_config(LinearArgs& a, const LinearConfig& c, int x_mode, float* part,
+                  hipStream_t stream) {
   a.x_stride = a.K;
-  const LinearConfig c = pick_config(a, x_mode);
-  const int st = x_mode == kNorm ? launch_mode<kNorm>(a, c, stream)
-                                 : launch_mode<kPlain>(a, c, stream);
+  a.ksplit = c.ksplit;
+  a.part = part;
+  if (c.ksplit > 1) {
+    if (x_mode != kPlain || a.nseg != 1 || a.seg[0].begin != 0 || a.seg[0].width != a.N)
+      return dah::set_error(DAH_ERR_HIP, "linear: k slices need a plain single-segment product");
+    if (c.lds == 0 || (c.ksplit != 4 && c.ksplit != 8))
+      return dah::set_error(DAH_ERR_HIP, "linear: k slices need an LDS tile and 4 or 8 slices");
+    if (part == nullptr || reinterpret_cast<uintptr_t>(part) % 16 != 0)
+      return dah::set_error(DAH_ERR_HIP, "linear: k slices need a 16-byte aligned workspace");
+  }
+  int st = x_mode == kNorm ? launch_mode<kNorm>(a, c, stream) : launch_mode<kPlain>(a, c, stream);
   if (st != DAH_OK) return st;
+  if (c.ksplit > 1) {
+    const size_t n4 = (size_t)a.T * a.N / 4;
+    const dim3 grid((unsigned)((n4 + 255) / 256));
+    const float4* p4 = reinterpret_cast<const float4*>(part);
+    const float4* r4 = reinterpret_cast<const float4*>(a.seg[0].res);
+    float4* y4 = reinterpret_cast<float4*>(a.seg[0].y);
+    if (c.ksplit == 4) linear_reduce_kernel<4><<<grid, 256, 0, stream>>>(p4, n4, r4, y4);
+    if (c.ksplit == 8) linear_reduce_kernel<8><<<grid, 256, 0, stream>>>(p4, n4, r4, y4);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return dah::set_error(DAH_ERR_HIP, "linear kernel launch failed: %s", hipGetErrorString(e));
   return DAH_OK;
+}
+
+// x_mode: kPlain or kNorm (a.x_gain, a.eps set).
+int launch_linear(LinearArgs& a, hipStream_t stream, int x_mode = kPlain) {
+  return launch_config(a, pick_config(a, x_mode), x_mode, nullptr, stream);
 }
 
 int check_norm(const float* gain, float eps, const char* who) {
@@ -716,6 +829,52 @@ int dah_linear_residual(const float* x, const void* w, const float* residual, in
   return launch_linear(a, static_cast<hipStream_t>(stream));
 }
 
+size_t dah_linear_workspace_bytes(int T, int N, int K) {
+  if (T < 1 || N < 64 || N % 64 != 0 || K < 256 || K % 256 != 0) return 0;
+  LinearArgs a = {};
+  a.T = T;
+  a.N = N;
+  a.K = K;
+  a.nseg = 1;
+  return split_bytes(a, pick_split_config(a));
+}
+
+int dah_linear_ws_kernel(int T, int N, int K, int* k_slices) {
+  if (T < 1 || N < 64 || N % 64 != 0 || K < 256 || K % 256 != 0) return -1;
+  LinearArgs a = {};
+  a.T = T;
+  a.N = N;
+  a.K = K;
+  a.nseg = 1;
+  const LinearConfig c = pick_split_config(a);
+  if (k_slices) *k_slices = c.ksplit;
+  return c.lds;
+}
+
+int dah_linear_ws(const float* x, const void* w, const float* residual, int T, int N, int K,
+                  float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  if (reinterpret_cast<uintptr_t>(residual) % 16 != 0)
+    return dah::set_error(DAH_ERR_ALIGN, "dah_linear_ws: residual needs 16-byte alignment");
+  int st = dah::validate_linear(x, w, T, N, K, y);
+  if (st != DAH_OK) return st;
+  LinearArgs a = {};
+  a.x = x;
+  a.w = static_cast<const uint16_t*>(w);
+  a.T = T;
+  a.N = N;
+  a.K = K;
+  a.nseg = 1;
+  a.seg[0] = Segment{y, 0, N, residual};
+  const LinearConfig c = pick_split_config(a);
+  const size_t need = split_bytes(a, c);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return dah::set_error(DAH_ERR_WORKSPACE, "dah_linear_ws: workspace of %zu bytes, need %zu",
+                          workspace ? workspace_bytes : (size_t)0, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return dah::set_error(DAH_ERR_ALIGN, "dah_linear_ws: workspace needs 256-byte alignment");
+  return launch_config(a, c, kPlain, static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+}
+
 int attn_qkv_proj(const float* x, const void* w_qkv, int T, int hidden, int num_heads, float* q,
                   float* k, float* v, void* stream) {
   return dah::qkv_proj(x, nullptr, 0.0f, w_qkv, T, hidden, num_heads, q, k, v, stream);
@@ -744,6 +903,14 @@ int attn_o_proj(const float* o, const void* w_o, int T, int num_heads, int hidde
   if (!dah::valid_heads(num_heads))
     return dah::set_error(DAH_ERR_SHAPE, "num_heads = %d, need 16, 32, 40 or 64", num_heads);
   return dah_linear(o, w_o, T, hidden, num_heads * dah::kHeadDim, y, stream);
+}
+
+int attn_o_proj_ws(const float* o, const void* w_o, int T, int num_heads, int hidden, float* y,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dah::valid_heads(num_heads))
+    return dah::set_error(DAH_ERR_SHAPE, "num_heads = %d, need 16, 32, 40 or 64", num_heads);
+  return dah_linear_ws(o, w_o, nullptr, T, hidden, num_heads * dah::kHeadDim, y, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -360,6 +360,43 @@ int dah_rmsnorm_linear(const float* x, const float* x_gain, float eps, const voi
                        int N, int K, float* y, void* stream);
 
 /*
+ * Products that split k over workgroups (the o_proj and down rows of the
+ * "Qwen3-0.6B" Model Spec page, "Compute-graph nodes": K = H*128 or 3072
+ * against N = 1024 outputs gives few output tiles for the chip).  Each
+ * workgroup multiplies one output tile over one of 4 or 8 equal k slices
+ * into a float32 partial product in the caller's workspace; a second launch
+ * adds the slices in slice order and the residual.  The sum is the same
+ * product up to float32 rounding order.
+ *
+ * dah_linear_workspace_bytes -- host only: the workspace dah_linear_ws needs
+ *   for a T x N x K product (k slices x T x N x 4 bytes), 0 when it does not
+ *   split k (K < 2048) or the shape is invalid.
+ *
+ * dah_linear_ws -- y = x . w^T (+ residual when residual is not NULL); shapes,
+ *   alignment and errors as dah_linear_residual, and workspace (device,
+ *   256-byte aligned, may be NULL when dah_linear_workspace_bytes is 0) of
+ *   workspace_bytes >= dah_linear_workspace_bytes(T, N, K), else
+ *   DAH_ERR_WORKSPACE before any launch.  residual may equal y; the
+ *   workspace must not overlap x, w, residual or y.  Its contents on entry
+ *   do not matter and are left undefined.
+ *
+ * attn_o_proj_ws -- attn_o_proj through dah_linear_ws (K = num_heads * 128).
+ *
+ * dah_linear_ws_kernel -- host only: the kernel dah_linear_ws launches (ids
+ *   as dah_linear_kernel) and, in *k_slices (may be NULL), its k slices (1 =
+ *   unsplit); -1 for an invalid shape.
+ */
+size_t dah_linear_workspace_bytes(int T, int N, int K);
+
+int dah_linear_ws(const float* x, const void* w, const float* residual, int T, int N, int K,
+                  float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+int attn_o_proj_ws(const float* o, const void* w_o, int T, int num_heads, int hidden, float* y,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+int dah_linear_ws_kernel(int T, int N, int K, int* k_slices);
+
+/*
  * dah_linear_kernel -- host only, no device call: which kernel dah_linear
  *   (and the projections built on it) launches for a T x N x K product:
  *   0 = the split-k kernel (decode's few rows), 1..5 = the LDS-tiled kernel
@@ -398,8 +435,10 @@ int dah_silu_mul(const float* gate_up, int T, int inter, float* act, void* strea
  *   num_heads, eps, rope_theta, the cache, block table, seq_lens, B,
  *   max_seq_len, num_splits   as for decode_attn_step_ex
  *   workspace    [device] at least dah_layer_workspace_bytes(...) bytes,
- *                256-byte aligned (the intermediates and the attention's
- *                workspace); contents need no initialisation.
+ *                256-byte aligned (the intermediates, then one region
+ *                shared by the attention's workspace and the k-slice
+ *                partials of o_proj and down, which run through
+ *                dah_linear_ws); contents need no initialisation.
  *
  * Eight launches in order on `stream` (nine with a cut sequence); the
  * attention's arguments are checked before the first.

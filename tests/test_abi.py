@@ -388,3 +388,77 @@ def test_linear_kernel_choice():
     import test_gpu_projections as tp
     reached = {lib.dah_linear_kernel(T, N, K) for T in tp.LINEAR_T for N, K in tp.LINEAR_NK}
     assert reached == {0, 1, 2, 3, 4, 5}
+
+
+MIB8 = 8 << 20   # dah_linear_ws's workspace for T = 256, N = 1024, K = 8192 (8 slices)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, A, None, 256, 1024, 8192, A, A, MIB8), 1),
+    ((A, A, None, 256, 1000, 8192, A, A, MIB8), 2),
+    ((A, A, None, 256, 1024, 8000, A, A, MIB8), 2),
+    ((A, A, A + 4, 256, 1024, 8192, A, A, MIB8), 4),
+    ((A, A, None, 256, 1024, 8192, A + 8, A, MIB8), 4),
+    ((A, A, None, 256, 1024, 8192, A, None, 0), 5),
+    ((A, A, None, 256, 1024, 8192, A, A, MIB8 - 1), 5),
+    ((A, A, None, 256, 1024, 8192, A, A + 16, MIB8), 4),
+])
+def test_linear_ws_rejects(args, status):
+    lib = _lib()
+    assert lib.dah_linear_ws(*args, None) == status
+    assert lib.dah_last_error().decode() != ""
+    assert lib.attn_o_proj_ws(A, A, 4, 48, 1024, A, A, MIB8, None) == 2
+
+
+def _ws_plan(lib, T, N, K):
+    ks = ctypes.c_int(0)
+    kernel = lib.dah_linear_ws_kernel(T, N, K, ctypes.byref(ks))
+    return kernel, ks.value
+
+
+def test_linear_ws_plan():
+    """The k-split rule of dah_linear_ws (host only): the measured o_proj and
+    down shapes take the tiles and slice counts the sweep found fastest; short
+    k, or enough tiles without slices, keep dah_linear's choice unsplit; the
+    workspace is slices x T x N floats; and the GPU parity cases reach every
+    tile shape over 8 slices and some over 4."""
+    lib = _lib()
+    want = {(512, 1024, 8192): (1, 8), (256, 1024, 8192): (2, 8), (128, 1024, 8192): (3, 8),
+            (64, 1024, 8192): (4, 8), (16, 1024, 8192): (5, 8), (16, 1024, 3072): (4, 8),
+            (256, 1024, 3072): (2, 8), (256, 1024, 2048): (3, 4), (128, 1024, 2048): (4, 4),
+            (1, 1024, 2048): (4, 8)}
+    for (T, N, K), plan in want.items():
+        assert _ws_plan(lib, T, N, K) == plan, (T, N, K)
+        assert lib.dah_linear_workspace_bytes(T, N, K) == plan[1] * T * N * 4
+    for T, N, K in ((1, 4096, 1024), (256, 4096, 1024), (256, 10240, 1024), (4096, 4096, 1024),
+                    (4096, 1024, 2048), (1000, 192, 256)):
+        assert _ws_plan(lib, T, N, K) == (lib.dah_linear_kernel(T, N, K), 1), (T, N, K)
+        assert lib.dah_linear_workspace_bytes(T, N, K) == 0
+    for bad in ((0, 64, 256), (4, 96, 2048), (4, 64, 2000)):
+        assert _ws_plan(lib, *bad)[0] == -1
+        assert lib.dah_linear_workspace_bytes(*bad) == 0
+    import test_gpu_projections as tp
+    reached = {_ws_plan(lib, *c) for c in tp.LINEAR_WS_CASES}
+    assert {k for k, s in reached if s == 8} == {1, 2, 3, 4, 5}
+    assert {k for k, s in reached if s == 4} == {3, 4}
+
+
+@pytest.mark.parametrize("B,H,L", [(256, 16, 2048), (256, 64, 2048), (32, 16, 16384),
+                                   (4, 40, 40960)])
+def test_layer_workspace_shares_one_region(B, H, L):
+    """dah_layer_workspace_bytes: the intermediates (each rounded up to 256
+    bytes), then one region as large as the larger of the attention's
+    workspace and the k-slice partials of o_proj and down."""
+    lib = _lib()
+    hidden, inter = 1024, 3072
+    r = lambda n: (n + 255) // 256 * 256   # noqa: E731
+    f = 4
+    inter_bytes = sum(r(n) for n in (B * H * 128 * f, B * 8 * 128 * f, B * 8 * 128 * f,
+                                     B * H * 128 * f, B * H * 128 * f, B * hidden * f,
+                                     B * 2 * inter * f, B * inter * f))
+    attn = lib.dah_workspace_bytes_ex(B, H, 1, L, 0)
+    split = max(lib.dah_linear_workspace_bytes(B, hidden, H * 128),
+                lib.dah_linear_workspace_bytes(B, hidden, inter))
+    assert split > 0
+    assert lib.dah_layer_workspace_bytes(B, hidden, inter, H, 1, L, 0) == \
+        inter_bytes + r(max(attn, split))

@@ -81,6 +81,52 @@ def test_linear_parity(T, N, K):
            f"rel-to-max {rel:.2e}")
 
 
+# T, N, K for dah_linear_ws: every LDS tile shape over 8 k slices, two over 4,
+# ragged row tails, one and seven rows, N not a multiple of 128 (test_abi
+# checks the plans these reach).
+LINEAR_WS_CASES = [(1, 1024, 2048), (7, 192, 2048), (16, 1024, 8192), (33, 1024, 2048),
+                   (64, 1024, 8192), (128, 1024, 2048), (128, 1024, 8192), (256, 1024, 2048),
+                   (256, 1024, 3072), (300, 1024, 4096), (512, 1024, 8192)]
+
+
+@pytest.mark.parametrize("residual", [False, True])
+@pytest.mark.parametrize("T,N,K", LINEAR_WS_CASES)
+def test_linear_ws_parity(T, N, K, residual):
+    """dah_linear_ws, k split over workgroups: against the oracle's product
+    (plus the residual, within its add's rounding), the workspace filled with
+    NaN beforehand (its contents on entry must not matter), a guard row after
+    y untouched; with the residual also in place (residual = y), equal to the
+    out-of-place result."""
+    import torch
+    dah = _dah()
+    kernel, slices = dah.linear_ws_kernel(T, N, K)
+    x = _rand((T, K), 400 + T)
+    w = _rand((N, K), 500 + N + K, 1.0 / np.sqrt(K), torch.bfloat16)
+    r = _rand((T, N), 600 + T) if residual else None
+    need = dah.linear_workspace_bytes(T, N, K)
+    assert need == slices * T * N * 4
+    ws = torch.full((need // 4,), float("nan"), device="cuda").view(torch.uint8)
+    y_all = torch.full((T + 1, N), float("nan"), device="cuda")
+    y = dah.linear_ws(x, w, residual=r, y=y_all[:T], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(y_all[T]).all(), "wrote past the output"
+    xr, wb = x.cpu().numpy(), _bits(w)
+    ref = P.linear(xr, wb)
+    bound = 2.0 ** -16 * P.linear(np.abs(xr), np.abs(O.bf16_bits_to_f64(wb)), "f64") + 1e-30
+    if residual:
+        ref = ref + r.cpu().numpy()
+        bound = bound + 2.0 ** -23 * np.abs(ref)
+        r2 = r.clone()
+        dah.linear_ws(x, w, residual=r2, y=r2, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(r2, y), "in place differs"
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+    worst = float(np.max(err / bound))
+    assert worst <= 1.0, f"error {worst:.3g} x the bound"
+    _print(f"[linear_ws] T={T} N={N} K={K} kernel {kernel} x {slices} slices "
+           f"residual={residual}: {worst:.3f} of bound")
+
+
 @pytest.mark.parametrize("H,hidden", [(16, 1024), (32, 2560), (40, 5120), (64, 5120)])
 @pytest.mark.parametrize("T", [1, 37, 256])
 def test_qkv_and_o_proj_parity(H, hidden, T):
@@ -94,6 +140,7 @@ def test_qkv_and_o_proj_parity(H, hidden, T):
     q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
     o = _rand((T, H, 128), 300 + H)
     y = dah.o_proj(o, p["w_o"])
+    y_ws = dah.o_proj_ws(o, p["w_o"])
     torch.cuda.synchronize()
     x = p["x"].cpu().numpy()
     y_qkv = np.concatenate([q.cpu().numpy().reshape(T, -1), k.cpu().numpy().reshape(T, -1),
@@ -104,13 +151,16 @@ def test_qkv_and_o_proj_parity(H, hidden, T):
         assert O.rel_to_max_err(got.cpu().numpy(), ref) <= 1e-5
     wo, ro = _check(y.cpu().numpy(), o.cpu().numpy().reshape(T, -1), _bits(p["w_o"]),
                     f"o_proj H={H}")
-    _print(f"[proj] H={H} hidden={hidden} T={T}: qkv {wq:.3f} / o {wo:.3f} of bound")
+    wo2, _ = _check(y_ws.cpu().numpy(), o.cpu().numpy().reshape(T, -1), _bits(p["w_o"]),
+                    f"o_proj_ws H={H}")
+    _print(f"[proj] H={H} hidden={hidden} T={T}: qkv {wq:.3f} / o {wo:.3f} / o_ws "
+           f"{wo2:.3f} ({dah.linear_ws_kernel(T, hidden, H * 128)}) of bound")
 
 
 @pytest.mark.parametrize("name,H", [("ragged_f32_b6", 16), ("ragged_f32_b6", 64),
                                     ("b256_s2048", 16), ("b256_s2048_h64", 64)])
 def test_attention_block_parity(name, H):
-    """x -> attn_qkv_proj -> decode_attn_step -> attn_o_proj against the
+    """x -> attn_qkv_proj -> decode_attn_step -> attn_o_proj_ws against the
     oracle's composed block.  The device's q, k, v carry the projection's
     error (x as two bf16 terms: ~2.5e-6 relative, measured) into the norm and
     the attention, so the composed gates are 1e-4 absolute on q_out and, for
@@ -128,7 +178,7 @@ def test_attention_block_parity(name, H):
     q_out, o = dah.decode_attn_step(q, k, v, t["q_gain"], t["k_gain"], t["k_pool"], t["v_pool"],
                                     t["block_table"], t["seq_lens"], int(seq_lens.max()),
                                     rope_theta=w.rope_theta)
-    y = dah.o_proj(o, p["w_o"])
+    y = dah.o_proj_ws(o, p["w_o"])
     torch.cuda.synchronize()
     x = p["x"].cpu().numpy()[sample]
     ref = P.attention_block(x, _bits(p["w_qkv"]), _bits(p["w_o"]), snap["q_gain"], snap["k_gain"],
@@ -143,13 +193,14 @@ def test_attention_block_parity(name, H):
     _print(f"  q_out {e_q:.2e}  o {e_o:.2e} (rel {r_o:.2e})  y {e_y:.2e} (rel {r_y:.2e})")
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("name", ["b256_s2048", "ragged_b32"])
-def test_block_under_graph_replay(name):
-    """The whole block (qkv_proj, decode_attn_step, o_proj) captured in one
-    HIP graph: every replay, with eager work and synchronisations between
-    replays, equals the eager result bit for bit (the library records no
-    memset, allocation or host synchronisation).  The cache is restored
-    before each run, since the step appends to it."""
+def test_block_under_graph_replay(name, split):
+    """The whole block (qkv_proj, decode_attn_step, o_proj or o_proj_ws)
+    captured in one HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager result bit for bit
+    (the library records no memset, allocation or host synchronisation).
+    The cache is restored before each run, since the step appends to it."""
     import torch
     dah = _dah()
     w = W.WORKLOADS[name]
@@ -162,12 +213,17 @@ def test_block_under_graph_replay(name):
     q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
     q_out, o = torch.empty_like(q), torch.empty_like(q)
     y = torch.empty((w.batch, w.hidden), device="cuda")
+    o_ws = torch.empty(max(dah.linear_workspace_bytes(w.batch, w.hidden, H * 128), 256),
+                       dtype=torch.uint8, device="cuda")
 
     def block():
         dah.qkv_proj(p["x"], p["w_qkv"], H, q=q, k=k, v=v)
         dah.decode_attn_step(q, k, v, t["q_gain"], t["k_gain"], t["k_pool"], t["v_pool"],
                              t["block_table"], t["seq_lens"], L, q_out=q_out, o=o, workspace=ws)
-        dah.o_proj(o, p["w_o"], y=y)
+        if split:
+            dah.o_proj_ws(o, p["w_o"], y=y, workspace=o_ws)
+        else:
+            dah.o_proj(o, p["w_o"], y=y)
 
     def restore():
         t["k_pool"].copy_(k0)
