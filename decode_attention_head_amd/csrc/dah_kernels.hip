@@ -1392,19 +1392,11 @@ __device__ __forceinline__ void merge_parts(const float* __restrict__ part_acc,
   }
 }
 
-// Empty sequence: o = 0 for seq_len <= 0, NaN for a length past max_seq_len.
-__device__ __forceinline__ void fill_row(float* out_row, int seq_len) {
-  if (threadIdx.x < 32) {
-    const float fill = seq_len < 1 ? 0.0f : NAN;
-    reinterpret_cast<float4*>(out_row)[threadIdx.x] = make_float4(fill, fill, fill, fill);
-  }
-}
-
 // DAH_PLAN_SPLIT: the non-empty splits of each (sequence, head); the row's
 // length decides how many of its `splits` slots count.
 __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, int B, int H, int max_seq_len, int splits,
+    const int32_t* __restrict__ seq_lens, int H, int max_seq_len, int splits,
     int pages_per_split, float* __restrict__ o) {
   const int unit = blockIdx.x;  // b * H + h
   const int b = unit / H;
@@ -1429,8 +1421,8 @@ constexpr int kBalancedMergeRows = kBalancedMergeThreads / 32;  // heads per wor
 
 __global__ __launch_bounds__(kBalancedMergeThreads) void combine_balanced_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ prefix, const int32_t* __restrict__ seq_lens, int B, int H,
-    int max_seq_len, int G, float* __restrict__ o) {
+    const int32_t* __restrict__ prefix, const int32_t* __restrict__ seq_lens, int B, int H, int G,
+    float* __restrict__ o) {
   const int groups = H / kBalancedMergeRows;
   const int b = blockIdx.x / groups;
   const int h = (blockIdx.x - b * groups) * kBalancedMergeRows + (threadIdx.x >> 5);
@@ -2465,10 +2457,10 @@ int launch_decode(const dah::Plan& plan, const float* q, const void* k_cache,
   static_assert(kBalancedMergeRows == 2, "every head count is even");
   if (plan.mode == DAH_PLAN_BALANCED)
     combine_balanced_kernel<<<cblocks / kBalancedMergeRows, kBalancedMergeThreads, 0, stream>>>(
-        a.part_acc, a.part_ml, a.prefix, seq_lens, B, num_heads, max_seq_len, plan.workgroups, o);
+        a.part_acc, a.part_ml, a.prefix, seq_lens, B, num_heads, plan.workgroups, o);
   else
     combine_splits_kernel<<<cblocks, kCombineThreads, 0, stream>>>(
-        a.part_acc, a.part_ml, seq_lens, B, num_heads, max_seq_len, plan.splits,
+        a.part_acc, a.part_ml, seq_lens, num_heads, max_seq_len, plan.splits,
         plan.pages_per_split, o);
   return check_launch("combine kernel");
 }
