@@ -7,7 +7,8 @@
 //
 // The products run on the matrix cores (dah_linear.hip), which also take the
 // hidden-size RMSNorms on their input rows and the residual adds in their
-// stores; the attention step runs in dah_kernels.hip.  This file holds the
+// stores (or in the reduce of their k slices: o_proj and down); the
+// attention step runs in dah_kernels.hip.  This file holds the
 // composition, the SwiGLU activation's kernel and the RMSNorm as a
 // standalone call (dah_rmsnorm).
 #include <hip/hip_runtime.h>
@@ -206,10 +207,11 @@ int decoder_layer_step(const float* x, const dah_layer_weights* w, int hidden, i
   void* split_ws = split > 0 ? ws + L.attn : nullptr;
   const int qdim = num_heads * dah::kHeadDim;
 
-  // Six launches (eight when o_proj and down split k): input_norm folded
-  // into qkv_proj and post_attn_norm into gate_up (the products norm their
-  // input rows as they stream them), the residual adds into the stores of
-  // o_proj and down (or into their slice sums).  mlp.act keeps its own
+  // Six launches, up to nine with the attention's merge and the slice
+  // reduces of o_proj and down: input_norm folded into qkv_proj and
+  // post_attn_norm into gate_up (the products norm their input rows as they
+  // stream them), the residual adds into the stores of o_proj and down (or
+  // into their slice sums).  mlp.act keeps its own
   // kernel: folded into down it would be redone once per column tile.
   st = dah::qkv_proj(x, w->w_in, eps, w->w_qkv, B, hidden, num_heads, q, k, v, stream);
   if (st == DAH_OK)

@@ -440,7 +440,10 @@ int dah_silu_mul(const float* gate_up, int T, int inter, float* act, void* strea
  *                partials of o_proj and down, which run through
  *                dah_linear_ws); contents need no initialisation.
  *
- * Eight launches in order on `stream` (nine with a cut sequence); the
+ * Six to nine launches in order on `stream`: qkv_proj (input_norm folded
+ * in), the attention step (plus its merge when a sequence is cut over
+ * workgroups), o_proj (plus its slice reduce when k is split), gate_up
+ * (post_attn_norm folded in), mlp.act, down (plus its slice reduce).  The
  * attention's arguments are checked before the first.
  */
 typedef struct {
