@@ -878,6 +878,35 @@ __device__ __forceinline__ void split3(const float (&x)[8], u32x4 (&out)[3]) {
 }
 
 // decode_range for a bfloat16 cache on the matrix cores; same contract.
+// Ranges of at least this many pages are visited in ascending page order
+// (decode_range_mfma); shorter ones, where the sort costs more than the
+// locality returns, in table order.
+constexpr int kSortMinPages = 64;
+
+// Sorts the 128 values a wave holds as element e = lane + 64 r (a0: r = 0,
+// a1: r = 1) into ascending order: a bitonic network, compare-exchanges at
+// distance 64 inside the lane and at shorter distances across lanes.
+__device__ __forceinline__ void sort128(int& a0, int& a1, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 128; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j == 64) {  // k = 128: ascending throughout
+        const int lo = min(a0, a1), hi = max(a0, a1);
+        a0 = lo;
+        a1 = hi;
+      } else {
+        const bool lower = (lane & j) == 0;
+        const int p0 = __shfl_xor(a0, j), p1 = __shfl_xor(a1, j);
+        const bool min0 = ((lane & k) == 0) == lower;         // e = lane
+        const bool min1 = (((lane + 64) & k) == 0) == lower;  // e = lane + 64
+        a0 = min0 ? min(a0, p0) : max(a0, p0);
+        a1 = min1 ? min(a1, p1) : max(a1, p1);
+      }
+    }
+  }
+}
+
 template <bool kStep, int kG>
 __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, int seq_len,
                                                   int npages, int p0, int p1, bool write_q,
@@ -937,12 +966,35 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
     }
   }
 
+  // The range's pages before its final one are visited in ascending
+  // physical order: every workgroup then sweeps the pool from low ids to
+  // high at about the same pace (on MI355X, B = 256, S = 2048: 1.2% faster
+  // than table order, which scatters the concurrent reads over the whole
+  // pool).  The final page, which may be masked, stays last; ranges of more
+  // than 129 pages keep table order.  Each wave sorts its own copy of the
+  // ids, so the 8 waves agree without a barrier.  Attention is independent
+  // of the order of positions (up to float32 rounding).
+  const int n_sorted = last - p0;
+  const bool sorted = n_sorted >= kSortMinPages && n_sorted <= 128;
+  int key0 = INT32_MAX, key1 = INT32_MAX;
+  if (sorted) {
+    const int32_t* ids = a.block_table + (size_t)b * a.max_pages_per_seq + p0;
+    if (lane < n_sorted) key0 = ids[lane];
+    if (lane + 64 < n_sorted) key1 = ids[lane + 64];
+    sort128(key0, key1, lane);
+  }
+  auto page_id = [&](int x) -> int {  // the page visited x - p0 th, x <= last
+    if (!sorted || x >= last) return bt[x];
+    const int i = x - p0;
+    return i < 64 ? __builtin_amdgcn_readlane(key0, i) : __builtin_amdgcn_readlane(key1, i - 64);
+  };
+
   KTileMfma K0, K1;
   TileV V0, V1;
-  int id1 = bt[min(p0 + 1, last)];
-  int id2 = bt[min(p0 + 2, last)];
+  int id1 = page_id(min(p0 + 1, last));
+  int id2 = page_id(min(p0 + 2, last));
   {
-    const int64_t off0 = offset_of(bt[p0]);
+    const int64_t off0 = offset_of(page_id(p0));
     K0.load(kbase + off0, lane);
     V0.load(vbase + off0, lane);
   }
@@ -1039,14 +1091,14 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
     const int64_t off1 = offset_of(id1);
     K1.load(kbase + off1, lane);
     V1.load(vbase + off1, lane);
-    const int id3 = bt[min(p + 3, last)];
+    const int id3 = page_id(min(p + 3, last));
     __builtin_amdgcn_sched_barrier(0);
     attend_page_mfma<false>(K0, V0, qb, st, lane, kPage);
     __builtin_amdgcn_sched_barrier(0);
     const int64_t off2 = offset_of(id2);
     K0.load(kbase + off2, lane);
     V0.load(vbase + off2, lane);
-    const int id4 = bt[min(p + 4, last)];
+    const int id4 = page_id(min(p + 4, last));
     __builtin_amdgcn_sched_barrier(0);
     attend_page_mfma<false>(K1, V1, qb, st, lane, kPage);
     __builtin_amdgcn_sched_barrier(0);

@@ -514,3 +514,34 @@ def test_step_under_graph_replay(H, splits):
         assert torch.equal(q_out, want_q), f"replay {i}: q_out differs"
         assert torch.equal(t["k_pool"], want_k), f"replay {i}: cache differs"
         _ = (t["q"] * 2).sum().item()   # eager work between replays
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_sorted_page_walk_matches_oracle(H):
+    """The matrix-core decode walks a range of 65 .. 129 pages in ascending
+    page order, its final (possibly masked) page last, and shorter or longer
+    ranges in table order.  Lengths on either side of both bounds, with
+    page-aligned and ragged tails, one workgroup per sequence: the fused step
+    (the new slot and every slot past the sequence poisoned with NaN first)
+    and the decode alone on its q_out, against the oracle."""
+    import dataclasses
+    import torch
+    dah = _dah()
+    lens = [1024, 1025, 1040, 1041, 1500, 2048, 2064, 2065, 2080]
+    w = dataclasses.replace(_custom(len(lens), lens, dtype="bf16", seed=41), num_heads=H)
+    t, seq_lens, table, _ = build_layer(w)
+    L = int(max(lens))
+    assert dah.plan_decode(len(lens), L, 1, num_heads=H)["kernel"] == "mfma"
+    snap = host_snapshot(t, seq_lens, table, range(len(lens)))
+    W.poison_unused(t, seq_lens, table, include_new_slot=True, value=float("nan"))
+    q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    L, num_splits=1)
+    o_dec = dah.paged_decode_gqa(q_out, t["k_pool"], t["v_pool"], t["block_table"],
+                                 t["seq_lens"], L, num_splits=1)
+    torch.cuda.synchronize()
+    ref = oracle_step(snap, "bf16")
+    for got, label in ((o, "step"), (o_dec, "decode")):
+        e_abs, e_rel = gates(got.cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
+                             label=f"sorted walk {label} H={H}")
+        _print(f"  sorted walk {label} H={H}: max abs {e_abs:.3g} rel {e_rel:.3g}")
