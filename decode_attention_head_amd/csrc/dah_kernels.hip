@@ -877,7 +877,6 @@ __device__ __forceinline__ void split3(const float (&x)[8], u32x4 (&out)[3]) {
   }
 }
 
-// decode_range for a bfloat16 cache on the matrix cores; same contract.
 // Ranges of at least this many pages are visited in ascending page order
 // (decode_range_mfma); shorter ones, where the sort costs more than the
 // locality returns, in table order.
@@ -907,6 +906,7 @@ __device__ __forceinline__ void sort128(int& a0, int& a1, int lane) {
   }
 }
 
+// decode_range for a bfloat16 cache on the matrix cores; same contract.
 template <bool kStep, int kG>
 __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, int seq_len,
                                                   int npages, int p0, int p1, bool write_q,
@@ -968,12 +968,13 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
 
   // The range's pages before its final one are visited in ascending
   // physical order: every workgroup then sweeps the pool from low ids to
-  // high at about the same pace (on MI355X, B = 256, S = 2048: 1.2% faster
-  // than table order, which scatters the concurrent reads over the whole
-  // pool).  The final page, which may be masked, stays last; ranges of more
-  // than 129 pages keep table order.  Each wave sorts its own copy of the
-  // ids, so the 8 waves agree without a barrier.  Attention is independent
-  // of the order of positions (up to float32 rounding).
+  // high at about the same pace, where table order scatters the concurrent
+  // reads over the whole pool (on MI355X, B = 256, S = 2048: 0.5% off the
+  // step, the sort included; 1.2% off the decode with rows sorted ahead of
+  // it).  The final page, which may be masked, stays last; ranges of fewer
+  // than 65 or more than 129 pages keep table order.  Each wave sorts its
+  // own copy of the ids, so the 8 waves agree without a barrier.  Attention
+  // is independent of the order of positions (up to float32 rounding).
   const int n_sorted = last - p0;
   const bool sorted = n_sorted >= kSortMinPages && n_sorted <= 128;
   int key0 = INT32_MAX, key1 = INT32_MAX;
