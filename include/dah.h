@@ -37,9 +37,13 @@
  *    they are preconditions, with a defined fault-free result when violated:
  *      seq_lens[b] <= 0               o[b] = 0, nothing appended, q_out[b] is
  *                                     the normed query rotated at pos 0
- *      seq_lens[b] > max_seq_len, or > max_pages_per_seq * 16,
- *      or a needed block_table entry outside [0, num_pages)
+ *      seq_lens[b] > max_seq_len, or > max_pages_per_seq * 16
  *                                     o[b] = NaN, nothing appended for b
+ *      a needed block_table entry outside [0, num_pages)
+ *                                     o[b] = NaN; nothing is read or written
+ *                                     through that entry (the new token is
+ *                                     still stored when its own page id is
+ *                                     in the pool)
  *    The new token's page must not be shared with another sequence.
  *
  * KV cache layout

@@ -545,3 +545,37 @@ def test_sorted_page_walk_matches_oracle(H):
         e_abs, e_rel = gates(got.cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
                              label=f"sorted walk {label} H={H}")
         _print(f"  sorted walk {label} H={H}: max abs {e_abs:.3g} rel {e_rel:.3g}")
+
+
+def test_sorted_page_walk_with_bad_and_repeated_ids():
+    """Ranges the decode sorts (94 pages, one workgroup per sequence): a page
+    id outside the pool gives o = NaN for that sequence, as in table order,
+    while the new token still lands in its own (valid) page; an id repeated
+    within a row counts its page twice, as the oracle reading through the
+    same table does."""
+    import torch
+    dah = _dah()
+    lens = [1500, 1500, 1500]
+    w = _custom(len(lens), lens, dtype="bf16", seed=43)
+    t, seq_lens, table, num_pages = build_layer(w)
+    L = int(max(lens))
+    table = table.copy()
+    table[2, 21] = table[2, 20]                        # sequence 2 reads page 20 twice
+    t["block_table"].copy_(torch.from_numpy(table))
+    snap = host_snapshot(t, seq_lens, table, [0, 2])
+    t["block_table"][1, 10] = num_pages + 7            # sequence 1: outside the pool
+    last1 = int(table[1, (lens[1] - 1) // 16])
+    slot1 = (lens[1] - 1) % 16
+    k1 = t["k_pool"][last1].clone()
+    q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    L, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1]).all()
+    after = t["k_pool"][last1]
+    assert torch.equal(after[:, :slot1], k1[:, :slot1]), "other slots changed"
+    assert not torch.equal(after[:, slot1], k1[:, slot1]), "new token not stored"
+    ref = oracle_step(snap, "bf16")
+    got = o[[0, 2]].cpu().numpy().astype(np.float64)
+    e_abs, e_rel = gates(got, ref["o"], None, 2e-2, label="sorted walk, repeated id")
+    _print(f"  sorted walk with bad/repeated ids: max abs {e_abs:.3g} rel {e_rel:.3g}")
