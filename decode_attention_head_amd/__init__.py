@@ -230,7 +230,8 @@ def decode_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_ta
                      max_seq_len: int, *, eps: float = 1e-6, rope_theta: float = 1e6,
                      num_splits: int = 0, q_out=None, o=None, workspace=None, stream=None):
     """One decode step of one layer: norm, RoPE, cache append, decodeGQA.
-    Returns (q_out, o)."""
+    Returns (q_out, o).  q_out=False skips the q_out store (the C call gets
+    NULL) and returns (None, o)."""
     torch = _torch()
     B, H = q.shape[0], _heads(q)
     dev = q.device
@@ -244,20 +245,21 @@ def decode_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_ta
         q_out = torch.empty_like(q)
     if o is None:
         o = torch.empty_like(q)
-    _require(q_out, "q_out", torch.float32, (B, H, HEAD_DIM), dev)
+    if q_out is not False:
+        _require(q_out, "q_out", torch.float32, (B, H, HEAD_DIM), dev)
     _require(o, "o", torch.float32, (B, H, HEAD_DIM), dev)
     ws, ws_bytes = _workspace(workspace, B, H, dt, max_seq_len, num_splits, dev)
     head = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
             _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
             block_table.shape[1], _ptr(seq_lens), B)
-    tail = (int(max_seq_len), int(num_splits), _ptr(q_out), _ptr(o),
+    tail = (int(max_seq_len), int(num_splits), None if q_out is False else _ptr(q_out), _ptr(o),
             None if ws is None else _ptr(ws), ws_bytes, _stream(dev, stream))
     if H == NUM_HEADS:
         st = lib().decode_attn_step(*head, *tail)
     else:
         st = lib().decode_attn_step_ex(*head, H, *tail)
     check(st, "decode_attn_step")
-    return q_out, o
+    return (None if q_out is False else q_out), o
 
 
 # ---------------------------------------------------------------- projections

@@ -386,6 +386,7 @@ __device__ __forceinline__ bool row_writes(int row, int h) { return row == (h & 
 // range): q_out is still the normed query, rotated at pos = seq_len - 1 (or 0).
 template <int kDtype, int kG>
 __device__ void step_q_out_only(const DecodeArgs& a, int b, int seq_len, int g, int lane) {
+  if (a.q_out == nullptr) return;  // the caller asked for o only
   constexpr int kH = kG * kKvHeads;
   const int row = lane >> 4, col = lane & 15;
   float qw[8], cr[8], sr[8];
@@ -623,7 +624,7 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, int b, int qb,
     }
   }
   if constexpr (kStep) {
-    if (write_q) {
+    if (write_q && a.q_out != nullptr) {
 #pragma unroll
       for (int h = 0; h < kGS; ++h) {
         if (!row_writes(row, h0 + h)) continue;
@@ -1147,7 +1148,7 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
     }
   }
   if constexpr (kStep) {
-    if (write_q) {
+    if (write_q && a.q_out != nullptr) {
       // Two 128-float rows per wave store: lanes 0-31 row h, lanes 32-63 row h + 1.
       const int half = lane >> 5, q4 = lane & 31;
 #pragma unroll
@@ -2583,11 +2584,13 @@ int decode_attn_step_ex(const float* q, const float* k_new, const float* v_new,
                         const int32_t* seq_lens, int B, int num_heads, int max_seq_len,
                         int num_splits, float* q_out, float* o, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  // q_out may be NULL (o only): the pointer checks then take q in its place.
+  const float* q_out_chk = q_out != nullptr ? q_out : q;
   int st = dah::validate_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache,
                                 v_cache, cache_dtype, num_pages, block_table, max_pages_per_seq,
-                                seq_lens, B, num_heads, q_out);
+                                seq_lens, B, num_heads, q_out_chk);
   if (st != DAH_OK) return st;
-  st = dah::validate_decode(q_out, k_cache, v_cache, cache_dtype, num_pages, block_table,
+  st = dah::validate_decode(q_out_chk, k_cache, v_cache, cache_dtype, num_pages, block_table,
                             max_pages_per_seq, seq_lens, B, num_heads, max_seq_len, num_splits,
                             o);
   if (st != DAH_OK) return st;

@@ -157,9 +157,10 @@ int paged_decode_gqa(const float* q, const void* k_cache, const void* v_cache, i
  * kernel launch (plus the merge when a sequence is cut): every decode
  * workgroup norms and rotates its own query heads, and the workgroup that
  * holds a sequence's last page norms, rotates and stores the new key and
- * value and attends to them.  Arguments are those of the two calls; q_out is
- * required and may equal q (in place with a cut sequence, the call makes the
- * two launches instead).
+ * value and attends to them.  Arguments are those of the two calls, except
+ * that q_out may be NULL: the step then writes o and the cache only (the
+ * pointer checks of q_out apply to q instead).  q_out may equal q (in place
+ * with a cut sequence, the call makes the two launches instead).
  */
 int decode_attn_step(const float* q, const float* k_new, const float* v_new,
                      const float* q_gain, const float* k_gain, float eps, float rope_theta,

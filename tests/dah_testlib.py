@@ -1,11 +1,18 @@
 """Helpers shared by the GPU tests: build workloads on the device, copy the
-pages a sampled set of sequences needs to the host (before the GPU step
-modifies the cache), and compare GPU results with the oracle.
+pages a set of sequences needs to the host (before the GPU step modifies the
+cache), and compare GPU results with the oracle.
 
 Only input marshalling lives here: every expected value is computed by the
-oracle from host copies of the generated inputs.
+oracle from host copies of the generated inputs.  The oracle runs one
+sequence at a time; ``oracle_map`` spreads those independent per-sequence
+evaluations over host threads (NumPy and its BLAS release the interpreter
+lock inside their array work), so that whole batches of the full-size
+workloads can be compared element by element within seconds.
 """
 from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -83,16 +90,47 @@ def sample_batch(seq_lens, k: int, seed: int = 0):
     return sorted(pick)
 
 
+def host_workers() -> int:
+    """Host threads for the oracle: the CPUs this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_map(fn, n_rows: int, chunk: int = 2):
+    """fn(rows) for consecutive chunks of the rows 0 .. n_rows-1 of a
+    snapshot, on a pool of host threads; the results (arrays, or dicts of
+    arrays, with the rows first) concatenated back in row order.  BLAS is
+    held to one thread per call meanwhile, so the rows run side by side
+    instead of oversubscribing the cores."""
+    from threadpoolctl import threadpool_limits
+    chunks = [list(range(i, min(n_rows, i + chunk))) for i in range(0, n_rows, chunk)]
+    if not chunks:
+        raise ValueError("oracle_map: no rows")
+    with threadpool_limits(limits=1):
+        with ThreadPoolExecutor(max_workers=min(host_workers(), len(chunks))) as ex:
+            parts = list(ex.map(fn, chunks))
+    if isinstance(parts[0], dict):
+        return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+    return np.concatenate(parts)
+
+
 def oracle_decode(snap, cache_dtype):
-    return O.paged_decode_gqa(snap["q"], snap["k_pool"], snap["v_pool"], snap["block_table"],
-                              snap["seq_lens"], cache_dtype)
+    """The oracle's decode over every sequence of a host snapshot."""
+    return oracle_map(lambda rows: O.paged_decode_gqa(
+        snap["q"], snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
+        cache_dtype, batch_indices=rows), len(snap["seq_lens"]))
 
 
 def oracle_step(snap, cache_dtype, eps=W.RMS_EPS, theta=W.ROPE_THETA):
-    """The oracle's decode step on a host snapshot (theta: the workload's RoPE base)."""
-    return O.decode_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"],
-                         snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
-                         cache_dtype, eps=eps, theta=theta)
+    """The oracle's decode step over every sequence of a host snapshot
+    (theta: the workload's RoPE base)."""
+    return oracle_map(lambda rows: O.decode_step(
+        snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"], snap["k_pool"],
+        snap["v_pool"], snap["block_table"], snap["seq_lens"], cache_dtype, eps=eps, theta=theta,
+        batch_indices=rows), len(snap["seq_lens"]))
 
 
 def read_slots(t, seq_lens, table, batch_indices):
@@ -148,16 +186,19 @@ def gates(o_gpu, o_ref, v_mean_dev, tol_abs, tol_rel=1e-4, label=""):
 
 
 def distance_to_uniform(o_ref, snap, cache_dtype):
-    """max |o_ref - mean_s v| over the sampled sequences and heads."""
-    worst = 0.0
-    for i in range(o_ref.shape[0]):
-        n = int(snap["seq_lens"][i])
-        v = O.gather_sequence(snap["v_pool"], snap["block_table"][i], n, cache_dtype)
-        mean = v.mean(axis=0)                                 # [8,128]
-        H = o_ref.shape[1]
-        for h in range(H):
-            worst = max(worst, float(np.max(np.abs(o_ref[i, h] - mean[h // (H // 8)]))))
-    return worst
+    """max |o_ref - mean_s v| over the snapshot's sequences and heads."""
+    H = o_ref.shape[1]
+
+    def worst(rows):
+        out = []
+        for i in rows:
+            n = int(snap["seq_lens"][i])
+            v = O.gather_sequence(snap["v_pool"], snap["block_table"][i], n, cache_dtype)
+            mean = v.mean(axis=0)                             # [8,128]
+            out.append(max(float(np.max(np.abs(o_ref[i, h] - mean[h // (H // 8)])))
+                           for h in range(H)))
+        return np.asarray(out)
+    return float(np.max(oracle_map(worst, o_ref.shape[0])))
 
 
 def bf16_alternative(exact: np.ndarray, fp32_rel: float = 4e-6):

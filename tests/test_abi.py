@@ -226,8 +226,14 @@ def test_append_rejects(kw, status):
     assert _append(**kw) == status
 
 
-@pytest.mark.parametrize("kw,status", BAD_APPEND + [(dict(max_len=65), 2), (dict(o=None), 1),
-                                                    (dict(ns=-2), 2), (dict(max_len=0), 2)])
+# decode_attn_step accepts a NULL q_out (o only); its other checks still apply
+BAD_STEP = [case for case in BAD_APPEND if case[0] != dict(qo=None)] + [
+    (dict(max_len=65), 2), (dict(o=None), 1), (dict(ns=-2), 2), (dict(max_len=0), 2),
+    (dict(qo=None, q=A + 4), 4), (dict(qo=None, o=None), 1), (dict(qo=None, max_len=65), 2),
+    (dict(qo=None, kn=None), 1), (dict(qo=None, dt=5), 3)]
+
+
+@pytest.mark.parametrize("kw,status", BAD_STEP)
 def test_step_rejects(kw, status):
     assert _step(**kw) == status
 
@@ -311,7 +317,7 @@ def test_ex_calls_validate_like_the_base_calls(H):
     assert lib.qk_norm_rope_append_ex(A, A, A, A, A, -1.0, 1e6, A, A, 1, 16, A, 4, A, 2, H, A,
                                       None) == 2
     assert lib.decode_attn_step_ex(A, A, A, A, A, 1e-6, 1e6, A, A, 1, 16, A, 4, A, 2, H, 64, 0,
-                                   None, A, None, 0, None) == 1
+                                   A, None, None, 0, None) == 1
 
 
 def test_planner_ex_rejects_unknown_dtype():

@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 from dah_testlib import (build_layer, check_rounded, cuda_available, distance_to_uniform, gates,
-                         host_snapshot, oracle_decode, oracle_step, read_slots, sample_batch)
+                         host_snapshot, oracle_decode, oracle_step, read_slots)
 from inputs import workloads as W
 
 pytestmark = [pytest.mark.gpu,
@@ -104,29 +104,29 @@ def test_small_decode_and_append(H, dtype):
 
 @pytest.mark.parametrize("H", HEADS)
 def test_full_size_step(H):
-    """B=256, S=2048 (the benchmark's cache) with H query heads, sampled."""
+    """B=256, S=2048 (the benchmark's cache) with H query heads, every sequence."""
     import torch
     dah = _dah()
     w = W.WORKLOADS[f"b256_s2048_h{H}"]
     _print(f"[family step] {w.name}")
     t, seq_lens, table, _ = build_layer(w)
-    sample = sample_batch(seq_lens, 6)
-    snap = host_snapshot(t, seq_lens, table, sample)
+    every = range(w.batch)
+    snap = host_snapshot(t, seq_lens, table, every)
     q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
                                     t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
                                     int(seq_lens.max()), rope_theta=w.rope_theta)
     torch.cuda.synchronize()
     ref = oracle_step(snap, "bf16", theta=w.rope_theta)
-    e_q = float(np.max(np.abs(q_out[sample].cpu().numpy() - ref["q_out"])))
+    e_q = float(np.max(np.abs(q_out.cpu().numpy() - ref["q_out"])))
     assert e_q <= 1e-5
-    k_slot, v_slot = read_slots(t, seq_lens, table, sample)
+    k_slot, v_slot = read_slots(t, seq_lens, table, every)
     from oracle import decode_attention as O
     _, k_exact = O.norm_rope(snap["q"], snap["k_new"], snap["q_gain"], snap["k_gain"],
                              snap["seq_lens"], theta=w.rope_theta)
     check_rounded(k_slot, k_exact)
     assert np.array_equal(v_slot, ref["v_slot"])
     dist = distance_to_uniform(ref["o"], snap, "bf16")
-    e_abs, e_rel = gates(o[sample].cpu().numpy().astype(np.float64), ref["o"], dist, 2e-2,
+    e_abs, e_rel = gates(o.cpu().numpy().astype(np.float64), ref["o"], dist, 2e-2,
                          label=w.name)
     _print(f"  q_out {e_q:.3g}  o max abs {e_abs:.3g}  rel-to-max {e_rel:.3g}")
 
@@ -137,7 +137,7 @@ def test_full_size_step(H):
 def test_split_and_balanced_decode(H, name):
     """The split plan (4 sequences up to 40,960 positions) and the balanced
     plan (128 log-uniform lengths; 32 ragged lengths, which the matrix-core
-    kernel also cuts evenly) with more query heads, sampled."""
+    kernel also cuts evenly) with more query heads, every sequence."""
     import torch
     dah = _dah()
     w = _with_heads(name, H)
@@ -146,14 +146,13 @@ def test_split_and_balanced_decode(H, name):
     if name != "long_b4_s40960":
         assert plan["mode"] == "balanced"
     t, seq_lens, table, _ = build_layer(w)
-    sample = sample_batch(seq_lens, 4)
-    snap = host_snapshot(t, seq_lens, table, sample)
+    snap = host_snapshot(t, seq_lens, table, range(w.batch))
     o = dah.paged_decode_gqa(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
                              int(seq_lens.max()))
     torch.cuda.synchronize()
     o_ref = oracle_decode(snap, "bf16")
     dist = distance_to_uniform(o_ref, snap, "bf16")
-    e_abs, e_rel = gates(o[sample].cpu().numpy().astype(np.float64), o_ref, dist, 2e-2,
+    e_abs, e_rel = gates(o.cpu().numpy().astype(np.float64), o_ref, dist, 2e-2,
                          label=f"{name} H={H}")
     _print(f"  o max abs {e_abs:.3g}  rel-to-max {e_rel:.3g}")
 
@@ -161,23 +160,23 @@ def test_split_and_balanced_decode(H, name):
 @pytest.mark.parametrize("H", [32, 64])
 def test_balanced_step(H):
     """The fused step under the balanced plan (32 ragged sequences, bf16
-    cache: the matrix-core kernel), sampled, q_out and the stored slot too."""
+    cache: the matrix-core kernel), every sequence, q_out and the stored slot too."""
     import torch
     dah = _dah()
     w = _with_heads("ragged_b32", H, 5e6)
     _print(f"[family balanced step] H={H}")
     t, seq_lens, table, _ = build_layer(w)
-    sample = sample_batch(seq_lens, 6)
-    snap = host_snapshot(t, seq_lens, table, sample)
+    every = range(w.batch)
+    snap = host_snapshot(t, seq_lens, table, every)
     q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
                                     t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
                                     int(seq_lens.max()), rope_theta=5e6)
     torch.cuda.synchronize()
     ref = oracle_step(snap, "bf16", theta=5e6)
-    assert float(np.max(np.abs(q_out[sample].cpu().numpy() - ref["q_out"]))) <= 1e-5
-    _, v_slot = read_slots(t, seq_lens, table, sample)
+    assert float(np.max(np.abs(q_out.cpu().numpy() - ref["q_out"]))) <= 1e-5
+    _, v_slot = read_slots(t, seq_lens, table, every)
     assert np.array_equal(v_slot, ref["v_slot"])
-    e_abs, e_rel = gates(o[sample].cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
+    e_abs, e_rel = gates(o.cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
                          label=f"H={H}")
     _print(f"  o max abs {e_abs:.3g}  rel-to-max {e_rel:.3g}")
 

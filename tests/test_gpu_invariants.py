@@ -12,7 +12,7 @@
   * batch independence, idempotent re-append, the defined results for
     out-of-domain device values, and the workspace check;
   * edge shapes: B = 1, seq_len 1, 15, 16, 17, page-aligned and ragged
-    tails, and the domain's maximum (B = 256, S = 40,960) on sampled outputs.
+    tails, and the domain's maximum (B = 256, S = 40,960) on 64 sequences.
 """
 import numpy as np
 import pytest
@@ -276,20 +276,29 @@ def test_large_gain_peaked_softmax():
 
 def test_domain_maximum_sampled():
     """B = 256 sequences of S = 40,960 positions (the shape domain's corners,
-    "At a glance"), checked on sampled sequences."""
+    "At a glance"): 64 seeded sequences (a quarter of the batch, over every
+    workgroup residue mod 8 and so every XCD) against the oracle, in two
+    halves so that the host holds 5 GB of pages at a time; every output
+    finite."""
     import torch
     w = W.Workload("max_b256_s40960", batch=256, cache_dtype="bf16", seed=33,
                    lens_kind="fixed", lens_args=(40960,))
     _print("[max] building 256 x 40960")
     t, seq_lens, table, _ = build_layer(w)
-    sample = sample_batch(seq_lens, 3, seed=5)
-    snap = host_snapshot(t, seq_lens, table, sample)
+    sample = sample_batch(seq_lens, 64, seed=5)
+    assert len({b % 8 for b in sample}) == 8
     o = _decode(t, 40960)
     torch.cuda.synchronize()
-    ref = oracle_decode(snap, "bf16")
-    e_abs, e_rel = gates(o[sample].cpu().numpy().astype(np.float64), ref, None, 2e-2, label="max")
-    _print(f"  max shape: max abs {e_abs:.3g} rel {e_rel:.3g}")
     assert torch.isfinite(o).all()
+    o_host = o.cpu().numpy().astype(np.float64)
+    worst_abs = worst_rel = 0.0
+    for half in (sample[:32], sample[32:]):
+        snap = host_snapshot(t, seq_lens, table, half)
+        ref = oracle_decode(snap, "bf16")
+        e_abs, e_rel = gates(o_host[half], ref, None, 2e-2, label="max")
+        worst_abs, worst_rel = max(worst_abs, e_abs), max(worst_rel, e_rel)
+        del snap
+    _print(f"  max shape, {len(sample)} sequences: max abs {worst_abs:.3g} rel {worst_rel:.3g}")
 
 
 @pytest.mark.parametrize("splits", [1, 3, 0])
@@ -579,3 +588,130 @@ def test_sorted_page_walk_with_bad_and_repeated_ids():
     got = o[[0, 2]].cpu().numpy().astype(np.float64)
     e_abs, e_rel = gates(got, ref["o"], None, 2e-2, label="sorted walk, repeated id")
     _print(f"  sorted walk with bad/repeated ids: max abs {e_abs:.3g} rel {e_rel:.3g}")
+
+
+def _balanced_segments(lens, workgroups):
+    """(sequence, first page, pages) of every segment the balanced decode
+    walks: the batch's pages in sequence order cut into `workgroups` ranges
+    [floor(k T / G), floor((k+1) T / G)), each split at sequence ends."""
+    pages = [W.pages_for(n) for n in lens]
+    prefix = np.concatenate([[0], np.cumsum(pages)])
+    T, G = int(prefix[-1]), int(workgroups)
+    segs = []
+    for k in range(G):
+        s, e = k * T // G, (k + 1) * T // G
+        while s < e:
+            b = int(np.searchsorted(prefix, s, side="right") - 1)
+            end = min(e, int(prefix[b + 1]))
+            segs.append((b, s - int(prefix[b]), end - s))
+            s = end
+    return segs
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_balanced_sorted_ranges_with_bad_and_repeated_ids(H):
+    """The balanced plan with workgroup ranges of 65 .. 129 pages, which the
+    matrix-core decode walks in ascending page order, most of them starting
+    in the middle of a sequence and some sharing a workgroup with the end of
+    the previous sequence.  Every slot past each sequence (and the new
+    token's slot) NaN-poisoned, one page id repeated inside a row (the
+    oracle reading through the same table counts that page twice), one id
+    outside the pool (that sequence gives NaN, its neighbours in the same
+    workgroups are unaffected).  The fused step and the decode alone on its
+    q_out, every other sequence against the oracle."""
+    import dataclasses
+    import torch
+    dah = _dah()
+    rng = np.random.default_rng(50 + H)
+    lens = [int(x) for x in rng.integers(2000, 9000, 64)]
+    w = dataclasses.replace(_custom(len(lens), lens, dtype="bf16", seed=51), num_heads=H)
+    t, seq_lens, table, num_pages = build_layer(w)
+    L = int(max(lens))
+    plan = dah.plan_decode(len(lens), L, num_heads=H, cache_dtype="bf16")
+    assert plan["mode"] == "balanced" and plan["kernel"] == "mfma"
+    segs = _balanced_segments(lens, plan["workgroups"])
+    window = [sg for sg in segs if 65 <= sg[2] <= 129]
+    assert len(window) >= 0.6 * len(segs), "ranges outside the sorted walk's window"
+    assert sum(1 for sg in window if sg[1] > 0) >= 0.5 * len(segs), "few mid-sequence starts"
+    rep, bad = 9, 30                                   # the repeated-id and bad-id sequences
+    table = table.copy()
+    table[rep, 40] = table[rep, 39]                    # page 39 read twice, page 40's dropped
+    t["block_table"].copy_(torch.from_numpy(table))
+    keep = [b for b in range(len(lens)) if b != bad]
+    snap = host_snapshot(t, seq_lens, table, keep)
+    W.poison_unused(t, seq_lens, table, include_new_slot=True, value=float("nan"))
+    t["block_table"][bad, 50] = num_pages + 7          # after poisoning: the host table stays valid
+    q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    L)
+    o_dec = dah.paged_decode_gqa(q_out, t["k_pool"], t["v_pool"], t["block_table"],
+                                 t["seq_lens"], L)
+    torch.cuda.synchronize()
+    ref = oracle_step(snap, "bf16")
+    assert float(np.max(np.abs(q_out[keep].cpu().numpy() - ref["q_out"]))) <= 1e-5
+    for got, label in ((o, "step"), (o_dec, "decode")):
+        assert torch.isnan(got[bad]).all(), f"{label}: the bad id did not give NaN"
+        e_abs, e_rel = gates(got[keep].cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
+                             label=f"balanced sorted {label} H={H}")
+        _print(f"  balanced sorted ranges {label} H={H}: {len(window)} of {len(segs)} segments "
+               f"in 65..129 pages; max abs {e_abs:.3g} rel {e_rel:.3g}")
+
+
+def test_split_sorted_ranges_at_64_heads():
+    """Fixed splits of 107 pages (the long-context batch, 24 splits of its
+    2,560-page sequences) at 64 query heads: the matrix-core decode walks
+    every full split, each starting mid-sequence, in ascending page order;
+    tails NaN-poisoned, every sequence against the oracle, the fused step
+    and the decode alone."""
+    import dataclasses
+    import torch
+    dah = _dah()
+    w = dataclasses.replace(W.WORKLOADS["long_b4_s40960"], num_heads=64)
+    t, seq_lens, table, _ = build_layer(w)
+    L = int(seq_lens.max())
+    plan = dah.plan_decode(w.batch, L, 24, num_heads=64, cache_dtype="bf16")
+    assert plan["mode"] == "split" and plan["kernel"] == "mfma"
+    assert 65 <= plan["pages_per_split"] <= 128
+    snap = host_snapshot(t, seq_lens, table, range(w.batch))
+    W.poison_unused(t, seq_lens, table, include_new_slot=True, value=float("nan"))
+    q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    L, num_splits=24)
+    o_dec = dah.paged_decode_gqa(q_out, t["k_pool"], t["v_pool"], t["block_table"],
+                                 t["seq_lens"], L, num_splits=24)
+    torch.cuda.synchronize()
+    ref = oracle_step(snap, "bf16")
+    for got, label in ((o, "step"), (o_dec, "decode")):
+        e_abs, e_rel = gates(got.cpu().numpy().astype(np.float64), ref["o"], None, 2e-2,
+                             label=f"split sorted {label}")
+        _print(f"  split sorted ranges ({plan['pages_per_split']} pages) {label}: "
+               f"max abs {e_abs:.3g} rel {e_rel:.3g}")
+
+
+@pytest.mark.parametrize("H,splits", [(16, 1), (16, 0), (16, 3), (64, 1), (64, 0), (40, 5)])
+def test_step_without_q_out(H, splits):
+    """decode_attn_step with a NULL q_out writes o and the cache exactly as
+    the call that also stores q_out (the same launches, minus that store),
+    on every plan: one workgroup per sequence, balanced, fixed splits."""
+    import dataclasses
+    import torch
+    dah = _dah()
+    rng = np.random.default_rng(60 + H + splits)
+    lens = [int(x) for x in rng.integers(1, 3000, 72)] + [1, 16, 17, 2048]
+    w = dataclasses.replace(_custom(len(lens), lens, dtype="bf16", seed=61), num_heads=H)
+    t, seq_lens, table, _ = build_layer(w)
+    L = int(max(lens))
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    q_out, o = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    L, num_splits=splits)
+    k1, v1 = t["k_pool"].clone(), t["v_pool"].clone()
+    t["k_pool"].copy_(k0)
+    t["v_pool"].copy_(v0)
+    none, o2 = dah.decode_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                    t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                    L, num_splits=splits, q_out=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o2, o)
+    assert torch.equal(t["k_pool"], k1) and torch.equal(t["v_pool"], v1)

@@ -14,7 +14,7 @@ import dataclasses
 import numpy as np
 import pytest
 
-from dah_testlib import build_layer, cuda_available, gates, host_snapshot, sample_batch
+from dah_testlib import build_layer, cuda_available, gates, host_snapshot, oracle_map
 from inputs import workloads as W
 from oracle import decode_attention as O
 from oracle import layer as L
@@ -141,19 +141,20 @@ def test_decoder_layer_parity(name, H):
     dah = _dah()
     w, t, seq_lens, table, p = _layer_case(name, H)
     _print(f"[layer] {name} H={H}")
-    sample = sample_batch(seq_lens, 6)
-    snap = host_snapshot(t, seq_lens, table, sample)
+    every = list(range(w.batch))
+    snap = host_snapshot(t, seq_lens, table, every)
     weights = {n: p[n] for n in dah.LAYER_WEIGHTS}
     y = dah.decoder_layer_step(p["x"], weights, t["k_pool"], t["v_pool"], t["block_table"],
                                t["seq_lens"], int(seq_lens.max()), rope_theta=w.rope_theta)
     torch.cuda.synchronize()
     wnp = {n: (_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy())
            for n, v in weights.items()}
-    ref = L.decoder_layer(p["x"].cpu().numpy()[sample], wnp, snap["k_pool"], snap["v_pool"],
-                          snap["block_table"], snap["seq_lens"], w.cache_dtype, num_heads=H,
-                          theta=w.rope_theta)
+    x_host = p["x"].cpu().numpy()
+    ref = oracle_map(lambda rows: L.decoder_layer(
+        x_host, wnp, snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
+        w.cache_dtype, num_heads=H, theta=w.rope_theta, batch_indices=rows), w.batch, chunk=8)
     tol = 1e-4 if w.cache_dtype == "f32" else 2e-2
-    e_abs, e_rel = gates(y[sample].cpu().numpy().astype(np.float64), ref["y"], None, tol,
+    e_abs, e_rel = gates(y.cpu().numpy().astype(np.float64), ref["y"], None, tol,
                          label=f"{name} y")
     _print(f"  y max abs {e_abs:.2e}  rel-to-max {e_rel:.2e}")
 

@@ -49,3 +49,30 @@ def test_paged_read_probe_reads_the_decode_tiles(dtype):
     want = kx ^ vx
     want[sl_cpu < 1] = 0          # nothing read: the folded accumulator stays zero
     assert np.array_equal(got, want)
+
+
+def test_probe_copy_refuses_mismatched_sizes_before_launching():
+    """The copy probe takes its byte count from the tensors: a destination
+    smaller (or larger) than the source, as a clamped slice of a smaller
+    tensor gives, is refused before any launch, and the destination keeps
+    its contents.  A matching pair copies exactly."""
+    import torch
+    from decode_attention_head_amd.probes import probe_copy, probe_read
+    src = torch.arange(1 << 14, dtype=torch.int32, device="cuda")          # 64 KiB
+    small = torch.full((1 << 13,), -7, dtype=torch.int32, device="cuda")   # 32 KiB
+    big = torch.full((1 << 15,), -7, dtype=torch.int32, device="cuda")     # 128 KiB
+    for dst in (small, big, big[: (1 << 14) + 4]):
+        with pytest.raises(ValueError):
+            probe_copy(src, dst)
+    with pytest.raises(ValueError):
+        probe_copy(src[: 1 << 30], small)       # the slice clamps to 64 KiB: still refused
+    with pytest.raises(ValueError):
+        probe_copy(src[::2], small)             # not contiguous
+    torch.cuda.synchronize()
+    assert bool((small == -7).all()) and bool((big == -7).all())
+    with pytest.raises(ValueError):
+        probe_read(src, torch.zeros(4, dtype=torch.int32, device="cuda"), 8)   # sink too small
+    dst = torch.empty_like(src)
+    assert probe_copy(src, dst) == src.numel() * 4
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
