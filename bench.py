@@ -7,17 +7,30 @@ decode_attn_step (q/k RMSNorm, RoPE, cache append and split-S decodeGQA, in
 one kernel launch when one split suffices, plus the log-sum-exp combine
 otherwise) per layer of the workload -- one for every workload but
 stack28_b128, whose step runs its 28 layers, each with its own cache and
-gains.  HIP events recorded on the launch stream bracket the layer calls of
-every --event-every'th step (default 10): an event pair costs ~7 us of GPU
-time per step, which would otherwise be counted into the step time.  Inputs
-are synthetic, seeded and resident in HBM before timing starts.
+gains.  `value` is the workload's K/V bytes over the host-timed mean of K
+steps (W untimed warm-up steps first).  HIP events recorded on the launch
+stream bracket the calls of every --event-every'th step (by default enough
+for at least 10 launches) for the roofline figures.  Inputs are synthetic,
+seeded and resident in HBM before timing starts.
 
 The JSON line reports
   value           KV-read throughput, GB/s = (sum of seq_lens * 4096 B) / step time
   roofline        the step's decode kernel (dominant kernel): algorithmic KV
                   bytes per launch / its average duration measured with HIP
                   events on the launch stream, against MI355X's 8 TB/s HBM peak
-  cpu_baseline    the float64 CPU oracle on a bounded sample of the same workload
+  configs         the five workloads (tiny float32 B=2; ragged B=32; the B=256,
+                  S=2048 headline; 4 long contexts; the 28-layer ragged stack),
+                  each timed alone: 5 warm-up steps, then the median of 50 steps
+                  bracketed by HIP events, with a 1 GiB scratch read before each
+                  (outside the events) so that no step finds K/V in the
+                  last-level cache; plan, kernel, GB/s, % of 8 TB/s, seqs/s,
+                  and the error of the first step's o and q_out against the
+                  float64 oracle over every sequence (both layers 0 and 27 of
+                  the stack)
+  cpu_baseline    the float64 CPU oracle over every sequence of the headline
+                  workload on a pool of worker processes (one core each, all
+                  host cores), and its single-core rate; the same oracle runs
+                  give the per-config errors
 
 --chunk N also times chunk_attn_step with N new tokens per sequence (the
 workload's lengths counting them), under "chunk": HIP-graph-replayed time,
@@ -30,6 +43,8 @@ projections, residuals, SwiGLU MLP) on the same batch, graph-replayed.
 before the step, attn.o_proj after it) on the same batch and reports them under
 "block": per-launch durations (HIP events), their bytes and flops, and the
 whole x -> qkv_proj -> decode_attn_step -> o_proj pass.
+
+--kernel valu|mfma forces the decode kernel's form (measurement aid).
 """
 from __future__ import annotations
 
@@ -64,10 +79,17 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="b256_s2048", choices=sorted(W.WORKLOADS))
     ap.add_argument("--num-splits", type=int, default=0, help="0 = planner's choice")
-    ap.add_argument("--event-every", type=int, default=10, metavar="N",
-                    help="bracket the calls of every N-th timed step with HIP events")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="time budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--event-every", type=int, default=0, metavar="N",
+                    help="bracket the calls of every N-th timed step with HIP events "
+                         "(default: steps/10, at most 10, so that >= 10 launches are timed)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (its rate and each workload's error)")
+    ap.add_argument("--config-iters", type=int, default=50, metavar="N",
+                    help="timed steps per workload in the five-workload report (0 skips it)")
+    ap.add_argument("--kernel", choices=["valu", "mfma"], default=None,
+                    help="force the decode kernel form (sets DAH_DECODE_KERNEL; a measurement "
+                         "aid: the VALU form exists for float32 caches and up to 2 query heads "
+                         "per KV head with bfloat16)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time paged_decode_gqa alone (profiling aid)")
     ap.add_argument("--no-read-probe", action="store_true",
@@ -105,41 +127,114 @@ def read_traffic(workload: str):
     return float(m_val.group(1))
 
 
-def cpu_baseline(w, t, seq_lens, table, budget_s):
-    """Time the oracle's decode step, one sequence at a time, until the
-    budget is spent.  Host copies of each sequence's pages are made before
-    its timer starts."""
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
+# ---------------------------------------------------------------------------
+# CPU baseline leg: the float64 oracle on the host's cores.  A pool of worker
+# processes (spawned before this process touches the GPU, so no worker holds a
+# GPU context) maps the oracle's decode step over sequences; each config's
+# host copy of its inputs reaches the workers as memory-mapped .npy files.
+# The oracle's outputs on those sequences are also what each config's error
+# against the GPU is computed from.
+# ---------------------------------------------------------------------------
+
+_SNAP_KEYS = ("q", "k_new", "v_new", "q_gain", "k_gain", "k_pool", "v_pool", "block_table",
+              "seq_lens")
+_worker_snaps = {}
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)            # one core per worker process
+
+
+def _worker_rows(task):
+    """Oracle decode step over rows of a snapshot directory (worker side)."""
+    path, rows, cache_dtype, theta = task
+    snap = _worker_snaps.get(path)
+    if snap is None:
+        _worker_snaps.clear()
+        snap = {k: np.load(os.path.join(path, k + ".npy"), mmap_mode="r") for k in _SNAP_KEYS}
+        _worker_snaps[path] = snap
     from oracle import decode_attention as O
-    from dah_testlib import host_snapshot
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    order = np.random.default_rng(7).permutation(len(seq_lens))
-    done, elapsed, kv_bytes = 0, 0.0, 0
-    for b in order:
-        snap = host_snapshot(t, seq_lens, table, [int(b)])
-        t0 = time.perf_counter()
-        O.decode_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"],
+    r = O.decode_step(snap["q"], snap["k_new"], snap["v_new"], snap["q_gain"], snap["k_gain"],
                       snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
-                      w.cache_dtype, theta=w.rope_theta)
-        elapsed += time.perf_counter() - t0
-        done += 1
-        kv_bytes += W.algorithmic_kv_bytes(seq_lens[[int(b)]], w.cache_dtype)
-        if elapsed >= budget_s:
-            break
-    return {
-        "value": kv_bytes / elapsed / 1e9,
-        "unit": "GB/s",
-        "seqs_per_s": done / elapsed,
-        "cores": int(threads),
-        "host_cpus": len(os.sched_getaffinity(0)),
-        "kind": "oracle",
-        "sample": f"{done} of {len(seq_lens)} sequences of {w.name}, full decode step each "
-                  f"(float64 NumPy, {elapsed:.1f} s)",
-    }
+                      cache_dtype, theta=theta, batch_indices=rows)
+    return rows, r["q_out"], r["o"]
+
+
+def host_workers() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class OraclePool:
+    """Worker processes running the unchanged oracle, one core each."""
+
+    def __init__(self, workers: int):
+        import multiprocessing as mp
+        self.workers = workers
+        self.pool = mp.get_context("spawn").Pool(workers, initializer=_worker_init)
+        self.pool.map(_worker_init_done, range(workers))       # all started and warm
+        self.dirs = []
+
+    def _dump(self, snap: dict, tag: str) -> str:
+        import shutil
+        import tempfile
+        need = sum(np.asarray(snap[k]).nbytes for k in _SNAP_KEYS)
+        base = None                     # memory-backed /dev/shm when it has room, else /tmp
+        if os.path.isdir("/dev/shm") and shutil.disk_usage("/dev/shm").free > 2 * need:
+            base = "/dev/shm"
+        path = tempfile.mkdtemp(prefix=f"dah_oracle_{tag}_", dir=base)
+        self.dirs.append(path)
+        for k in _SNAP_KEYS:
+            np.save(os.path.join(path, k + ".npy"), np.ascontiguousarray(snap[k]))
+        return path
+
+    def run(self, snap: dict, tag: str, cache_dtype: str, theta: float, rows=None,
+            serial: bool = False):
+        """(q_out, o, seconds): the oracle over `rows` of the snapshot (all by
+        default), timed from submission to the last result.  serial: one
+        worker, one sequence at a time (the single-core rate)."""
+        path = self._dump(snap, tag)
+        n = len(snap["seq_lens"])
+        rows = list(range(n)) if rows is None else list(rows)
+        # longest sequences first, so that the pool's tail is short
+        order = sorted(rows, key=lambda b: -int(snap["seq_lens"][b]))
+        tasks = [(path, [b], cache_dtype, theta) for b in order]
+        self.pool.apply(_worker_rows, ((path, order[:1], cache_dtype, theta),))   # map the files
+        t0 = time.perf_counter()
+        if serial:
+            results = [self.pool.apply(_worker_rows, (tk,)) for tk in tasks]
+        else:
+            results = self.pool.map(_worker_rows, tasks, chunksize=1)
+        secs = time.perf_counter() - t0
+        H = snap["q"].shape[1]
+        q_out = np.zeros((n, H, W.HEAD_DIM))
+        o = np.zeros((n, H, W.HEAD_DIM))
+        for rws, qo, oo in results:
+            q_out[rws], o[rws] = qo, oo
+        import shutil
+        shutil.rmtree(path, ignore_errors=True)
+        return q_out[rows], o[rows], secs
+
+    def close(self):
+        import shutil
+        self.pool.terminate()
+        self.pool.join()
+        for path in self.dirs:
+            shutil.rmtree(path, ignore_errors=True)
+
+
+def _worker_init_done(_):
+    return os.getpid()
+
+
+def oracle_errors(q_gpu, o_gpu, q_ref, o_ref):
+    """max abs error and the pages' relative-to-max error ("Model conformance"
+    page, "How the comparison works", step 4) of o, and q_out's max abs."""
+    o_gpu = np.asarray(o_gpu, np.float64)
+    e = float(np.max(np.abs(o_gpu - o_ref)))
+    return {"o_max_abs": e, "o_rel_to_max": e / float(np.max(np.abs(o_ref))),
+            "q_out_max_abs": float(np.max(np.abs(np.asarray(q_gpu, np.float64) - q_ref))),
+            "finite": bool(np.all(np.isfinite(o_gpu)))}
 
 
 def _graph_us(torch, fn, n):
@@ -271,13 +366,112 @@ def time_chunk(dah, torch, w, seq_lens, num_pages, n):
             "timing": "HIP graph replay of 10 calls (append + attention launches), mean per call"}
 
 
+# The five workloads every run reports (tiny float32 reference, ragged B=32,
+# the B=256 S=2048 headline, long contexts, the 28-layer ragged stack).
+CONFIGS = ["tiny_f32_b2", "ragged_b32", "b256_s2048", "long_b4_s40960", "stack28_b128"]
+FLUSH_BYTES = 1 << 30   # scratch read between timed iterations (past the last-level cache)
+
+
+def time_config(dah, torch, name, flush, iters, warmup, num_splits, want_check):
+    """One workload: decode_attn_step over its layers, `warmup` untimed steps,
+    then `iters` steps each bracketed by HIP events on the launch stream with
+    a 1 GiB scratch read before it (outside the events), so that no step finds
+    the previous step's K/V in the last-level cache.  Returns the timing
+    record, and (when want_check) host snapshots of the checked layers taken
+    before any step and the GPU outputs of the first step, for the oracle."""
+    from dah_testlib import host_snapshot
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    w = W.WORKLOADS[name]
+    nl = w.num_layers
+    seq_lens = W.make_seq_lens(w)
+    table, num_pages = W.make_block_table(w, seq_lens)
+    layers = [W.make_layer(w, layer, dev, table=table, num_pages=num_pages, seq_lens=seq_lens)
+              for layer in range(nl)]
+    B, H, L = w.batch, w.num_heads, int(seq_lens.max())
+    plan = dah.plan_decode(B, L, num_splits, num_heads=H, cache_dtype=w.cache_dtype)
+    ws = torch.empty(max(dah.workspace_bytes(B, L, num_splits, num_heads=H,
+                                             cache_dtype=w.cache_dtype), 256),
+                     dtype=torch.uint8, device=dev)
+    checked = sorted({0, nl - 1})
+    snaps = {c: host_snapshot(layers[c], seq_lens, table, range(B)) for c in checked} \
+        if want_check else {}
+    q_out = torch.empty_like(layers[0]["q"])
+    o = torch.empty_like(layers[0]["q"])
+
+    def step():
+        for tl in layers:
+            dah.decode_attn_step(tl["q"], tl["k_new"], tl["v_new"], tl["q_gain"], tl["k_gain"],
+                                 tl["k_pool"], tl["v_pool"], tl["block_table"], tl["seq_lens"],
+                                 L, rope_theta=w.rope_theta, num_splits=num_splits, q_out=q_out,
+                                 o=o, workspace=ws)
+
+    outs = {}
+    if want_check:
+        for c, tl in enumerate(layers):
+            qo_c, o_c = dah.decode_attn_step(tl["q"], tl["k_new"], tl["v_new"], tl["q_gain"],
+                                             tl["k_gain"], tl["k_pool"], tl["v_pool"],
+                                             tl["block_table"], tl["seq_lens"], L,
+                                             rope_theta=w.rope_theta, num_splits=num_splits,
+                                             workspace=ws)
+            if c in snaps:
+                outs[c] = (qo_c.cpu().numpy(), o_c.cpu().numpy())
+    from decode_attention_head_amd.probes import probe_read
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    for _ in range(warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        probe_read(flush, sink, 4096)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    med = float(np.median(us))
+    kv = nl * W.algorithmic_kv_bytes(seq_lens, w.cache_dtype)
+    rec = {
+        "batch": B, "layers": nl, "heads": H, "cache": w.cache_dtype,
+        "seq_lens": (f"all {L}" if int(seq_lens.min()) == L else
+                     f"{int(seq_lens.min())}..{L}, sum {int(seq_lens.sum())}"),
+        "plan": plan["mode"], "kernel": plan["kernel"], "workgroups": plan["workgroups"],
+        "splits": plan["splits"],
+        "kv_bytes_per_step": kv,
+        "step_us_median": round(med, 2),
+        "step_us_mean": round(float(np.mean(us)), 2),
+        "step_us_min_max": [round(float(us.min()), 2), round(float(us.max()), 2)],
+        "kv_gbs": round(kv / med / 1e3, 1),
+        "pct_hbm_peak": round(100.0 * kv / med / 1e3 / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(B / (med * 1e-6), 1),
+        "timing": f"HIP events around each of {iters} steps after {warmup} warm-up steps, "
+                  f"median; a {FLUSH_BYTES >> 30} GiB scratch read before each timed step",
+    }
+    del layers, ws
+    return rec, snaps, outs, w
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    if args.kernel:
+        os.environ["DAH_DECODE_KERNEL"] = args.kernel
+    # The oracle's worker processes start before anything touches the GPU.
+    pool = None if args.no_cpu_baseline else OraclePool(host_workers())
+    try:
+        run(args, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def run(args, pool):
     import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
     import decode_attention_head_amd as dah
 
     w = W.WORKLOADS[args.workload]
@@ -298,7 +492,6 @@ def main():
     ws_bytes = dah.workspace_bytes(B, L, args.num_splits, num_heads=H, cache_dtype=w.cache_dtype)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     q_outs = [torch.empty_like(t["q"]) for _ in range(nl)]
-    q_out = q_outs[0]
     o = torch.empty_like(t["q"])
     stream = torch.cuda.current_stream(dev)
 
@@ -314,16 +507,18 @@ def main():
         dah.paged_decode_gqa(q_outs[layer], tl["k_pool"], tl["v_pool"], tl["block_table"],
                              tl["seq_lens"], L, num_splits=args.num_splits, o=o, workspace=ws)
 
-    run = decode if args.decode_only else step
+    run_layer = decode if args.decode_only else step
     if args.decode_only:
         for layer in range(nl):
             step(layer)
     for _ in range(args.warmup):
         for layer in range(nl):
-            run(layer)
+            run_layer(layer)
     torch.cuda.synchronize()
 
-    every = max(1, args.event_every)
+    # Every `every`-th timed step's calls are bracketed by HIP events; by
+    # default at least 10 of them (every 2nd step of 20, every 10th of 200).
+    every = args.event_every or max(1, min(10, args.steps // 10))
     timed = [i for i in range(args.steps) if i % every == every - 1] or [args.steps - 1]
     starts = {(i, layer): torch.cuda.Event(enable_timing=True) for i in timed for layer in range(nl)}
     ends = {(i, layer): torch.cuda.Event(enable_timing=True) for i in timed for layer in range(nl)}
@@ -334,14 +529,15 @@ def main():
             ev = starts.get((i, layer))
             if ev is not None:
                 ev.record(stream)
-                run(layer)
+                run_layer(layer)
                 ends[(i, layer)].record(stream)
             else:
-                run(layer)
+                run_layer(layer)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    launch_ms = float(np.mean([starts[key].elapsed_time(ends[key]) for key in starts]))
+    launch_ms_all = [starts[key].elapsed_time(ends[key]) for key in starts]
+    launch_ms = float(np.mean(launch_ms_all))
 
     if args.copy_probe > 0:
         from decode_attention_head_amd.probes import probe_copy
@@ -395,15 +591,76 @@ def main():
         paged_gbs = round(10 * kv_bytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9, 1)
     gbs = nl * kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (launch_ms * 1e-3) / 1e9
-    traffic = read_traffic(w.name) if (args.num_splits == 0 and not args.decode_only) else None
+    default_run = args.num_splits == 0 and not args.decode_only and not args.kernel
+    traffic = read_traffic(w.name) if default_run else None
 
     block = time_block(dah, torch, w, t, L, ws, stream, args) if args.block else None
     chunk = time_chunk(dah, torch, w, seq_lens, num_pages, args.chunk) if args.chunk > 0 else None
     layer = time_layer(dah, torch, w, t, L, args) if args.layer else None
+    del layers, t, ws, q_outs, o
+    torch.cuda.empty_cache()
 
+    # The five workloads, each timed on its own, median of args.config_iters
+    # steps with the last-level cache flushed between them; then the
+    # oracle leg over their sequences (CPU rate, and each config's error).
+    configs = {}
     cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, t, seq_lens, table, args.cpu_seconds)
+    if args.config_iters > 0:
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        flush.fill_(1)
+        for name in CONFIGS:
+            rec, snaps, outs, cw = time_config(dah, torch, name, flush, args.config_iters, 5,
+                                               args.num_splits, pool is not None)
+            torch.cuda.empty_cache()
+            if pool is not None:
+                errs, osecs, oseqs, okv = [], 0.0, 0, 0
+                for c, snap in snaps.items():
+                    q_ref, o_ref, secs = pool.run(snap, f"{name}_{c}", cw.cache_dtype,
+                                                  cw.rope_theta)
+                    errs.append(oracle_errors(outs[c][0], outs[c][1], q_ref, o_ref))
+                    osecs += secs
+                    oseqs += len(snap["seq_lens"])
+                    okv += W.algorithmic_kv_bytes(snap["seq_lens"], cw.cache_dtype)
+                tol = 1e-5 if cw.cache_dtype == "f32" else 2e-2
+                worst = {k: max(e[k] for e in errs) for k in ("o_max_abs", "o_rel_to_max",
+                                                             "q_out_max_abs")}
+                rec["parity"] = {
+                    **{k: float(f"{v:.3g}") for k, v in worst.items()},
+                    "tol_max_abs": tol,
+                    "within": bool(all(e["finite"] for e in errs) and worst["o_max_abs"] <= tol
+                                   and worst["q_out_max_abs"] <= tol and
+                                   worst["o_rel_to_max"] <= 1e-4),
+                    "compared": f"every sequence of layer(s) {sorted(snaps)}: o and q_out of "
+                                f"the first step against the float64 oracle",
+                }
+                rec["oracle"] = {"seqs_per_s": round(oseqs / osecs, 2),
+                                 "kv_gbs": round(okv / osecs / 1e9, 3),
+                                 "seconds": round(osecs, 2), "cores": pool.workers}
+                if name == "b256_s2048":
+                    snap = snaps[0]
+                    n1 = min(len(snap["seq_lens"]), 32)
+                    _, _, s1 = pool.run(snap, f"{name}_serial", cw.cache_dtype, cw.rope_theta,
+                                        rows=range(n1), serial=True)
+                    kv1 = W.algorithmic_kv_bytes(snap["seq_lens"][:n1], cw.cache_dtype)
+                    cpu = {
+                        "value": round(okv / osecs / 1e9, 4),
+                        "unit": "GB/s",
+                        "seqs_per_s": round(oseqs / osecs, 2),
+                        "cores": pool.workers,
+                        "host_cpus": len(os.sched_getaffinity(0)),
+                        "kind": "oracle",
+                        "sample": f"all {oseqs} sequences of b256_s2048, one float64 NumPy "
+                                  f"decode step each, on {pool.workers} worker processes "
+                                  f"({osecs:.1f} s)",
+                        "single_core": {"value": round(kv1 / s1 / 1e9, 4), "unit": "GB/s",
+                                        "seqs_per_s": round(n1 / s1, 2),
+                                        "sample": f"{n1} sequences, one at a time, one core "
+                                                  f"({s1:.1f} s)"},
+                    }
+            configs[name] = rec
+            del snaps, outs
+        del flush
+        torch.cuda.empty_cache()
 
     line = {
         "metric": "paged GQA decode KV-read GB/s (% of HBM peak) and seqs/s at B=256",
@@ -427,6 +684,7 @@ def main():
             "layers": nl,
             "kv_bytes_per_step": nl * kv_bytes,
             "plan": plan["mode"],
+            "kernel": plan["kernel"],
             "workgroups": plan["workgroups"],
             "step": ("paged_decode_gqa" if args.decode_only else "decode_attn_step") +
                     (f" x {nl} layers" if nl > 1 else ""),
@@ -444,7 +702,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_source": (os.path.relpath(traffic_file(w.name), ROOT) +
+                               " (rocprofv3 FETCH_SIZE and WRITE_SIZE of this kernel source, "
+                               "scaled by a plain copy's counters)") if traffic else None,
             "avg_launch_us": round(launch_ms * 1e3, 2),
+            "median_launch_us": round(float(np.median(launch_ms_all)) * 1e3, 2),
             "launches_timed": len(starts),
             "probe_read_gbs": probe_gbs,
             "frac_of_probe_read": None if not probe_gbs else round(achieved / probe_gbs, 4),
@@ -454,6 +716,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if configs:
+        line["configs"] = configs
     if block is not None:
         line["block"] = block
     if chunk is not None:

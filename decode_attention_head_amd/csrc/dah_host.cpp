@@ -4,6 +4,8 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "dah.h"
 
@@ -142,6 +144,19 @@ int plan_decode(int B, int num_heads, int cache_dtype, int max_seq_len, int num_
     }
   }
   p.mfma = bf16 && (big_group || p.mode != DAH_PLAN_SPLIT);
+  // DAH_DECODE_KERNEL=valu or =mfma overrides that choice where the other
+  // form is built (a measurement aid, read once): the matrix-core form reads
+  // a bfloat16 cache only, the VALU form is built for bfloat16 up to 2 query
+  // heads per KV head.
+  static const int forced = []() -> int {
+    const char* e = getenv("DAH_DECODE_KERNEL");
+    if (e == nullptr) return -1;
+    if (strcmp(e, "valu") == 0) return DAH_KERNEL_VALU;
+    if (strcmp(e, "mfma") == 0) return DAH_KERNEL_MFMA;
+    return -1;
+  }();
+  if (forced == DAH_KERNEL_VALU && !big_group) p.mfma = false;
+  if (forced == DAH_KERNEL_MFMA && bf16) p.mfma = true;
   *out = p;
   return DAH_OK;
 }

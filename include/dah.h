@@ -187,6 +187,12 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
  *                          also the fallback for batches over 4096 sequences)
  *
  * num_splits: 0 = automatic, 1 = per sequence, n > 1 = at most n splits.
+ * The kernel (dah_decode_kernel below): the matrix-core form for a bfloat16
+ * cache except under fixed splits at 2 query heads per KV head; the
+ * environment variable DAH_DECODE_KERNEL=valu or =mfma, read once per
+ * process, overrides that where the other form is built (VALU: any float32
+ * cache, bfloat16 at 2 query heads per KV head; matrix cores: bfloat16) -- a
+ * measurement aid, reported here as well as used by the calls.
  * Returns a dah_status.
  */
 typedef enum {

@@ -216,3 +216,69 @@ def bf16_alternative(exact: np.ndarray, fp32_rel: float = 4e-6):
     flagged = np.abs(exact - mid) <= fp32_rel * np.maximum(np.abs(exact), row_scale)
     alt = np.where(flagged, O.round_to_bf16(other), rne)
     return rne, alt, flagged
+
+
+def appended_slot_slack(snap, ref, x, w_qkv_bits, num_heads, cache_dtype):
+    """Per (sequence, head, dim) bound on how far o may move because the
+    appended key and value, which the device derives from its own float32
+    projection of x, are stored in a bfloat16 cache as the other neighbour
+    of the oracle's rounding.  Both stores are correct roundings of a value
+    within the projection's error of a rounding midpoint.  Everything here
+    comes from oracle values and the projection's error bound alone.
+
+    The projection's elementwise bound is the projection gate,
+    (2^-16 + 2e-6) sum_k |x w| (x enters the matrix cores as two bf16 terms).
+    A value element within that bound of a midpoint may move by one bf16
+    step s_v; a key element within the bound carried through the norm
+    (2 ||e||/rms(k) max|gain|, plus float32 rounding of the norm and the
+    rotation, 4e-6 of the row) may move by s_k, shifting the new token's
+    score by at most dz = sum |q_d| s_k,d / sqrt(128).  With p the new
+    token's softmax weight and o_old the attention over the older positions
+    (o = (1 - p) o_old + p v_new), the move of o is at most
+        p s_v + p (1 - p) dz e^dz (|v_new - o_old| + s_v).
+    A float32 cache stores the device's value unrounded: no slack."""
+    from oracle import projections as P
+    o_ref = ref["o"]
+    if cache_dtype != "bf16":
+        return np.zeros_like(o_ref), 0
+    n, H = o_ref.shape[0], num_heads
+    G = H // 8
+    nq, nkv = H * 128, 8 * 128
+    absw = np.abs(O.bf16_bits_to_f64(w_qkv_bits))
+    eb = (2.0 ** -16 + 2e-6) * P.linear(np.abs(np.asarray(x, np.float64)), absw, "f64")
+    eb_k = eb[:, nq:nq + nkv].reshape(n, 8, 128)
+    eb_v = eb[:, nq + nkv:].reshape(n, 8, 128)
+
+    def flags(exact, err):
+        rne = O.round_to_bf16(exact)
+        s = bf16_spacing(exact)
+        other = np.where(exact >= rne, rne + s, rne - s)
+        return np.abs(exact - 0.5 * (rne + other)) <= err, s
+
+    flag_v, s_v = flags(ref["v"], eb_v)
+    _, k_exact = O.norm_rope(ref["q"], ref["k"], snap["q_gain"], snap["k_gain"], snap["seq_lens"])
+    rms = np.sqrt(np.mean(ref["k"] ** 2, axis=-1, keepdims=True)) + 1e-30
+    gain = float(np.max(np.abs(snap["k_gain"])))
+    d_k = (2.0 * np.sqrt(np.sum(eb_k ** 2, axis=-1, keepdims=True)) / rms * gain +
+           4e-6 * np.max(np.abs(k_exact), axis=-1, keepdims=True))
+    flag_k, s_k = flags(k_exact, d_k)
+
+    def p_new(rows):
+        out = []
+        for i in rows:
+            L = int(snap["seq_lens"][i])
+            k_old = O.gather_sequence(snap["k_pool"], snap["block_table"][i], L - 1, cache_dtype) \
+                if L > 1 else np.zeros((0, 8, 128))
+            k_all = np.concatenate([k_old, ref["k_slot"][i][None]], axis=0)
+            out.append(O.attention_weights(ref["q_out"][i], k_all)[:, -1])
+        return np.asarray(out)
+    p = oracle_map(p_new, n)[:, :, None]                                 # [n,H,1]
+    heads = np.arange(H) // G
+    sv = (s_v * flag_v)[:, heads]                                         # [n,H,128]
+    dz = np.sum(np.abs(ref["q_out"]) * (s_k * flag_k)[:, heads], axis=-1,
+                keepdims=True) / np.sqrt(128.0)
+    v_new = ref["v_slot"][:, heads]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o_old = np.where(p < 1.0, (o_ref - p * v_new) / (1.0 - p), v_new)
+    slack = p * sv + p * (1.0 - p) * dz * np.exp(dz) * (np.abs(v_new - o_old) + sv)
+    return slack, int(flag_v.sum() + flag_k.sum())

@@ -13,8 +13,8 @@ metric).
 import numpy as np
 import pytest
 
-from dah_testlib import (build_layer, cuda_available, gates, host_snapshot, read_slots,
-                         sample_batch)
+from dah_testlib import (appended_slot_slack, build_layer, cuda_available, host_snapshot,
+                         oracle_map, read_slots)
 from inputs import workloads as W
 from oracle import decode_attention as O
 from oracle import projections as P
@@ -172,25 +172,40 @@ def test_attention_block_parity(name, H):
     _print(f"[block] {name} H={H}")
     t, seq_lens, table, _ = build_layer(w)
     p = W.make_projections(w, 0, "cuda")
-    sample = sample_batch(seq_lens, 6)
-    snap = host_snapshot(t, seq_lens, table, sample)
+    snap = host_snapshot(t, seq_lens, table, range(w.batch))
     q, k, v = dah.qkv_proj(p["x"], p["w_qkv"], H)
     q_out, o = dah.decode_attn_step(q, k, v, t["q_gain"], t["k_gain"], t["k_pool"], t["v_pool"],
                                     t["block_table"], t["seq_lens"], int(seq_lens.max()),
                                     rope_theta=w.rope_theta)
     y = dah.o_proj_ws(o, p["w_o"])
     torch.cuda.synchronize()
-    x = p["x"].cpu().numpy()[sample]
-    ref = P.attention_block(x, _bits(p["w_qkv"]), _bits(p["w_o"]), snap["q_gain"], snap["k_gain"],
-                            snap["k_pool"], snap["v_pool"], snap["block_table"], snap["seq_lens"],
-                            w.cache_dtype, num_heads=H, theta=w.rope_theta)
+    x = p["x"].cpu().numpy()
+    wq_bits, wo_bits = _bits(p["w_qkv"]), _bits(p["w_o"])
+    ref = oracle_map(lambda rows: P.attention_block(
+        x, wq_bits, wo_bits, snap["q_gain"], snap["k_gain"], snap["k_pool"], snap["v_pool"],
+        snap["block_table"], snap["seq_lens"], w.cache_dtype, num_heads=H, theta=w.rope_theta,
+        batch_indices=rows), w.batch, chunk=8)
     tol = 1e-4 if w.cache_dtype == "f32" else 2e-2
-    e_q = float(np.max(np.abs(q_out[sample].cpu().numpy() - ref["q_out"])))
+    e_q = float(np.max(np.abs(q_out.cpu().numpy() - ref["q_out"])))
     assert e_q <= 1e-4, f"q_out {e_q:.3g}"
-    assert O.rel_to_max_err(q_out[sample].cpu().numpy(), ref["q_out"]) <= 1e-4
-    e_o, r_o = gates(o[sample].cpu().numpy().astype(np.float64), ref["o"], None, tol, label="o")
-    e_y, r_y = gates(y[sample].cpu().numpy().astype(np.float64), ref["y"], None, tol, label="y")
-    _print(f"  q_out {e_q:.2e}  o {e_o:.2e} (rel {r_o:.2e})  y {e_y:.2e} (rel {r_y:.2e})")
+    assert O.rel_to_max_err(q_out.cpu().numpy(), ref["q_out"]) <= 1e-4
+    # The appended slot may hold the other bf16 neighbour wherever the
+    # device's float32 projection lies within its error of a rounding
+    # midpoint; the slack bounds what that moves (dah_testlib).
+    slack, flagged = appended_slot_slack(snap, ref, x, wq_bits, H, w.cache_dtype)
+    slack_y = P.linear(slack.reshape(w.batch, -1), np.abs(O.bf16_bits_to_f64(wo_bits)), "f64")
+    for name_, got, want, sl in (("o", o, ref["o"], slack), ("y", y, ref["y"], slack_y)):
+        got = got.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), name_
+        err = np.abs(got - want)
+        scale = float(np.max(np.abs(want)))
+        assert float(err.max()) <= tol, f"{name_}: max abs {float(err.max()):.3g}"
+        over = err > 1e-4 * scale + sl
+        assert not over.any(), (f"{name_}: {int(over.sum())} elements exceed 1e-4 x max + slack; "
+                                f"worst {float(np.max(err - sl)) / scale:.3g} of max")
+        _print(f"  {name_}: rel-to-max {float(err.max()) / scale:.2e}, beyond the slack "
+               f"{float(np.max(err - sl)) / scale:.2e} ({flagged} near-midpoint slot elements)")
+    _print(f"  q_out {e_q:.2e}")
 
 
 @pytest.mark.parametrize("split", [False, True])
