@@ -262,6 +262,43 @@ def decode_attn_step(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_ta
     return (None if q_out is False else q_out), o
 
 
+def decode_attn_step_noalloc(q, k_new, v_new, q_gain, k_gain, k_cache, v_cache, block_table,
+                             seq_lens, max_seq_len: int, *, eps: float = 1e-6,
+                             rope_theta: float = 1e6, num_splits: int = 0, q_out=None, o=None,
+                             stream=None):
+    """decode_attn_step through decode_attn_step_noalloc: the split partials
+    live in the library's static device scratch (DAH_SCRATCH_BYTES), so the
+    C call allocates nothing.  q_out and o must then be given by a caller
+    that cannot allocate (here they are allocated when omitted); q_out=False
+    passes NULL.  Returns (q_out, o)."""
+    torch = _torch()
+    B, H = q.shape[0], _heads(q)
+    dev = q.device
+    _require(q, "q", torch.float32, (B, H, HEAD_DIM))
+    _require(k_new, "k_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(v_new, "v_new", torch.float32, (B, NUM_KV_HEADS, HEAD_DIM), dev)
+    _require(q_gain, "q_gain", torch.float32, (HEAD_DIM,), dev)
+    _require(k_gain, "k_gain", torch.float32, (HEAD_DIM,), dev)
+    dt = _check_cache(k_cache, v_cache, block_table, seq_lens, B, dev)
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if o is None:
+        o = torch.empty_like(q)
+    if q_out is not False:
+        _require(q_out, "q_out", torch.float32, (B, H, HEAD_DIM), dev)
+    _require(o, "o", torch.float32, (B, H, HEAD_DIM), dev)
+    st = lib().decode_attn_step_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(q_gain), _ptr(k_gain), eps, rope_theta,
+        _ptr(k_cache), _ptr(v_cache), dt, k_cache.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), B, H, int(max_seq_len), int(num_splits),
+        None if q_out is False else _ptr(q_out), _ptr(o), _stream(dev, stream))
+    check(st, "decode_attn_step_noalloc")
+    return (None if q_out is False else q_out), o
+
+
+SCRATCH_BYTES = 16 << 20   # DAH_SCRATCH_BYTES (include/dah.h)
+
+
 # ---------------------------------------------------------------- projections
 
 def _require_weights(w, name, shape, device):

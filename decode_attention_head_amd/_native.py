@@ -41,6 +41,9 @@ SIGNATURES = {
     "decode_attn_step_ex": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_float, _c_float, _vp, _vp, _c_int,
                                      _c_i64, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _c_int, _vp,
                                      _vp, _vp, _c_size, _vp]),
+    "decode_attn_step_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_float, _c_float, _vp,
+                                          _vp, _c_int, _c_i64, _vp, _c_int, _vp, _c_int, _c_int,
+                                          _c_int, _c_int, _vp, _vp, _vp]),
     "dah_plan_decode_ex": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.c_void_p]),
     "dah_workspace_bytes_ex": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),

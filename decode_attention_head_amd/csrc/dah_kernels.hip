@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "dah.h"
@@ -2250,6 +2251,42 @@ int device_cu_count(int* out) {
   return DAH_OK;
 }
 
+// The allocation-free step's scratch (decode_attn_step_noalloc): the split
+// partials and prefix sums that decode_attn_step_ex keeps in the caller's
+// workspace.  Each device that loads the library holds its own copy until
+// the process ends; every call on a device shares it.  Host code reaches it
+// only through the device address hipGetSymbolAddress returns for that
+// device (the array's name is a host-side stand-in, not a device pointer).
+static __device__ __align__(256) unsigned char scratch[DAH_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[64];
+std::mutex g_scratch_mutex;
+
+// This device's address of `scratch`, looked up once per device (with the
+// device current) and kept.
+int device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return dah::set_error(DAH_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64)
+    return dah::set_error(DAH_ERR_HIP, "device %d: the static scratch serves devices 0..63", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return dah::set_error(DAH_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                              hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DAH_OK;
+}
+
 // Calls f(std::integral_constant<int, G>{}) with the number G of query heads
 // per KV head; num_heads is one of 16, 32, 40, 64 (checked by the caller).
 template <class F>
@@ -2631,6 +2668,44 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
                              cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
                              kHeads, max_seq_len, num_splits, q_out, o, workspace,
                              workspace_bytes, stream);
+}
+
+int decode_attn_step_noalloc(const float* q, const float* k_new, const float* v_new,
+                             const float* q_gain, const float* k_gain, float eps,
+                             float rope_theta, void* k_cache, void* v_cache, int cache_dtype,
+                             int64_t num_pages, const int32_t* block_table,
+                             int max_pages_per_seq, const int32_t* seq_lens, int B,
+                             int num_heads, int max_seq_len, int num_splits, float* q_out,
+                             float* o, void* stream) {
+  const float* q_out_chk = q_out != nullptr ? q_out : q;
+  int st = dah::validate_append(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache,
+                                v_cache, cache_dtype, num_pages, block_table, max_pages_per_seq,
+                                seq_lens, B, num_heads, q_out_chk);
+  if (st != DAH_OK) return st;
+  st = dah::validate_decode(q_out_chk, k_cache, v_cache, cache_dtype, num_pages, block_table,
+                            max_pages_per_seq, seq_lens, B, num_heads, max_seq_len, num_splits,
+                            o);
+  if (st != DAH_OK) return st;
+  int cus = 0;
+  st = device_cu_count(&cus);
+  if (st != DAH_OK) return st;
+  dah::Plan plan;
+  st = dah::plan_decode(B, num_heads, cache_dtype, max_seq_len, num_splits, cus, &plan);
+  if (st != DAH_OK) return st;
+  if (plan.workspace > DAH_SCRATCH_BYTES)
+    return dah::set_error(DAH_ERR_WORKSPACE,
+                          "decode_attn_step_noalloc: the plan needs %zu bytes of scratch, the "
+                          "static scratch holds %zu (B=%d, %d heads, max_seq_len=%d, "
+                          "num_splits=%d); use decode_attn_step_ex with a workspace",
+                          plan.workspace, (size_t)DAH_SCRATCH_BYTES, B, num_heads, max_seq_len,
+                          num_splits);
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != DAH_OK) return st;
+  return decode_attn_step_ex(q, k_new, v_new, q_gain, k_gain, eps, rope_theta, k_cache, v_cache,
+                             cache_dtype, num_pages, block_table, max_pages_per_seq, seq_lens, B,
+                             num_heads, max_seq_len, num_splits, q_out, o, ws,
+                             DAH_SCRATCH_BYTES, stream);
 }
 
 int chunk_attn_step(const float* q, const float* k_new, const float* v_new, const float* q_gain,

@@ -264,6 +264,33 @@ int decode_attn_step_ex(const float* q, const float* k_new, const float* v_new,
                         size_t workspace_bytes, void* stream);
 
 /*
+ * decode_attn_step_noalloc -- decode_attn_step_ex without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split partials live in a static device array of DAH_SCRATCH_BYTES (16 MiB)
+ * that the library holds on each GPU it runs on until the process ends; the
+ * call allocates nothing and calls no allocating routine.  Arguments and
+ * results are those of decode_attn_step_ex (q_out may be NULL).
+ *
+ * A plan whose workspace (dah_workspace_bytes_ex) exceeds DAH_SCRATCH_BYTES
+ * returns DAH_ERR_WORKSPACE before anything is launched.  At 16 query heads
+ * that leaves room for the balanced plan up to 1,760 sequences and for
+ * B * splits <= 2,016 under fixed splits (a quarter of that at 64 heads);
+ * one workgroup per sequence needs none.  Every call on one GPU shares
+ * that GPU's array, which keeps the last call's contents (no call needs it
+ * cleared): calls that overlap on one GPU -- on different streams, or on one
+ * stream while another thread also calls -- race on it.
+ */
+#define DAH_SCRATCH_BYTES (16u << 20)
+int decode_attn_step_noalloc(const float* q, const float* k_new, const float* v_new,
+                             const float* q_gain, const float* k_gain, float eps,
+                             float rope_theta, void* k_cache, void* v_cache, int cache_dtype,
+                             int64_t num_pages, const int32_t* block_table,
+                             int max_pages_per_seq, const int32_t* seq_lens, int B,
+                             int num_heads, int max_seq_len, int num_splits, float* q_out,
+                             float* o, void* stream);
+
+/*
  * The planner and workspace size for num_heads query heads and a cache of
  * cache_dtype: with a bfloat16 cache and 32 or more heads the decode runs on
  * the matrix cores, and the balanced plan starts at 32 sequences instead of

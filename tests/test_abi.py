@@ -468,3 +468,34 @@ def test_layer_workspace_shares_one_region(B, H, L):
     assert split > 0
     assert lib.dah_layer_workspace_bytes(B, hidden, inter, H, 1, L, 0) == \
         inter_bytes + r(max(attn, split))
+
+
+def _noalloc(**kw):
+    lib = _lib()
+    a = dict(q=A, kn=A, vn=A, qg=A, kg=A, eps=1e-6, theta=1e6, k=A, v=A, dt=1, num_pages=16,
+             bt=A, mpps=4, sl=A, B=2, H=16, max_len=64, ns=0, qo=A, o=A, stream=None)
+    a.update(kw)
+    return lib.decode_attn_step_noalloc(a["q"], a["kn"], a["vn"], a["qg"], a["kg"], a["eps"],
+                                        a["theta"], a["k"], a["v"], a["dt"], a["num_pages"],
+                                        a["bt"], a["mpps"], a["sl"], a["B"], a["H"],
+                                        a["max_len"], a["ns"], a["qo"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", BAD_STEP + [(dict(H=24), 2), (dict(H=0), 2)])
+def test_noalloc_step_rejects(kw, status):
+    """The allocation-free step validates exactly like decode_attn_step
+    before it looks at the device or its scratch."""
+    assert _noalloc(**kw) == status
+    assert _lib().dah_last_error().decode() != ""
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="valid arguments would launch on a real GPU")
+def test_noalloc_without_gpu_reports_hip_error():
+    assert _noalloc() == 6
+
+
+def test_scratch_size_constant():
+    text = open(HEADER).read()
+    m = re.search(r"#define DAH_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    import decode_attention_head_amd as dah
+    assert m and int(m.group(1)) << int(m.group(2)) == dah.SCRATCH_BYTES == 16 << 20
