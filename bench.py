@@ -84,6 +84,7 @@ def parse():
                          "(default: steps/10, at most 10, so that >= 10 launches are timed)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (its rate and each workload's error)")
+    ap.add_argument("--cpu-seconds", type=float, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--config-iters", type=int, default=50, metavar="N",
                     help="timed steps per workload in the five-workload report (0 skips it)")
     ap.add_argument("--kernel", choices=["valu", "mfma"], default=None,
@@ -454,6 +455,8 @@ def time_config(dah, torch, name, flush, iters, warmup, num_splits, want_check):
 
 def main():
     args = parse()
+    if args.cpu_seconds is not None and args.cpu_seconds <= 0:   # older spelling
+        args.no_cpu_baseline = True
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)

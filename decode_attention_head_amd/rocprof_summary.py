@@ -58,6 +58,39 @@ def trace_summary(d: str) -> str:
     return "\n".join(out)
 
 
+def pair_summary(d: str, first: str, second: str) -> str:
+    """Per step of a split or balanced plan: the decode launch (kernel names
+    containing `first`), the idle time until the merge launch (`second`) that
+    follows it on the same queue starts, the merge launch, and the span from
+    the decode's start to the merge's end -- from the start and end
+    timestamps of a --kernel-trace run."""
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv")))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dec, gap, mrg, span = [], [], [], []
+    for a, b in zip(rows, rows[1:]):
+        if first in a["Kernel_Name"] and second in b["Kernel_Name"]:
+            s0, e0 = int(a["Start_Timestamp"]), int(a["End_Timestamp"])
+            s1, e1 = int(b["Start_Timestamp"]), int(b["End_Timestamp"])
+            dec.append(e0 - s0)
+            gap.append(s1 - e0)
+            mrg.append(e1 - s1)
+            span.append(e1 - s0)
+    if not dec:
+        return f"no {first} launch followed by {second}"
+
+    def stat(v):
+        v = sorted(v)
+        return f"{sum(v) / len(v) / 1e3:10.2f} {v[len(v) // 2] / 1e3:10.2f}"
+    return "\n".join([
+        f"pairs: {len(dec)}  ({first} -> {second})",
+        f"{'':24s} {'avg_us':>10s} {'median_us':>10s}",
+        f"{'decode launch':24s} {stat(dec)}",
+        f"{'gap before the merge':24s} {stat(gap)}",
+        f"{'merge launch':24s} {stat(mrg)}",
+        f"{'decode start to merge end':24s} {stat(span)}",
+    ])
+
+
 def _counter_means(d: str, counter: str):
     rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
     agg = collections.defaultdict(list)
@@ -140,6 +173,8 @@ def main():
     sub = ap.add_subparsers(dest="mode", required=True)
     t = sub.add_parser("trace")
     t.add_argument("dir")
+    t.add_argument("--pair", nargs=2, metavar=("DECODE", "MERGE"),
+                   help="also time each DECODE launch, the gap and the MERGE launch after it")
     c = sub.add_parser("traffic")
     c.add_argument("fetch_dir")
     c.add_argument("write_dir")
@@ -156,6 +191,8 @@ def main():
     a = ap.parse_args()
     if a.mode == "trace":
         body = trace_summary(a.dir)
+        if a.pair:
+            body += "\n" + pair_summary(a.dir, *a.pair)
     elif a.mode == "traffic":
         body = traffic_summary(a.fetch_dir, a.write_dir, a.copy_mib)
     else:

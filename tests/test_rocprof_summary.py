@@ -64,3 +64,24 @@ def test_counters_summary_wants_one_kernel_per_name(tmp_path):
                               ("decode_split_kernel<2>", "SQ_WAVES", 1.0)])
     with pytest.raises(ValueError):
         rs.counters_summary([str(tmp_path)], ["decode_split_kernel"])
+
+
+def test_pair_summary_times_decode_gap_and_merge(tmp_path):
+    # two steps: decode 50 us, 3 us idle, merge 4 us; an unrelated kernel between steps
+    rows = []
+    t = 1_000_000
+    for i in range(2):
+        rows.append(("KERNEL_DISPATCH", "void decode_split_kernel<1, true, 2, false>(DecodeArgs)",
+                     t, t + 50_000))
+        rows.append(("KERNEL_DISPATCH", "combine_splits_kernel(float const*, ...)",
+                     t + 53_000, t + 57_000))
+        rows.append(("KERNEL_DISPATCH", "probe_read_kernel(...)", t + 60_000, t + 61_000))
+        t += 100_000
+    _write(os.path.join(tmp_path, "host", "run_kernel_trace.csv"),
+           ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    out = rs.pair_summary(str(tmp_path), "decode_split_kernel", "combine").splitlines()
+    assert out[0].startswith("pairs: 2")
+    assert out[2].split()[-2:] == ["50.00", "50.00"]
+    assert out[3].split()[-2:] == ["3.00", "3.00"]
+    assert out[4].split()[-2:] == ["4.00", "4.00"]
+    assert out[5].split()[-2:] == ["57.00", "57.00"]
