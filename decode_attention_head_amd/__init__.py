@@ -501,6 +501,26 @@ def silu_mul(gate_up, *, act=None, stream=None):
     return act
 
 
+def rmsnorm_swiglu(x, x_gain, w_gate_up, *, eps: float = 1e-6, act=None, stream=None):
+    """post_attn_norm + gate_up + mlp.act in one launch (dah_rmsnorm_swiglu):
+    x [T,K] float32, x_gain [K] float32 or None (no norm), w_gate_up
+    [2I,K] bfloat16 (gate rows, then up rows) -> act [T,I] float32."""
+    torch = _torch()
+    T, K = x.shape
+    two_i = w_gate_up.shape[0]
+    _require(x, "x", torch.float32, (T, K))
+    _require_weights(w_gate_up, "w_gate_up", (two_i, K), x.device)
+    if x_gain is not None:
+        _require(x_gain, "x_gain", torch.float32, (K,), x.device)
+    act = torch.empty((T, two_i // 2), dtype=torch.float32, device=x.device) \
+        if act is None else act
+    _require(act, "act", torch.float32, (T, two_i // 2), x.device)
+    check(lib().dah_rmsnorm_swiglu(_ptr(x), None if x_gain is None else _ptr(x_gain), eps,
+                                   _ptr(w_gate_up), T, two_i // 2, K, _ptr(act),
+                                   _stream(x.device, stream)), "dah_rmsnorm_swiglu")
+    return act
+
+
 LAYER_WEIGHTS = ("w_in", "w_qkv", "q_gain", "k_gain", "w_o", "w_post", "w_gate_up", "w_down")
 
 

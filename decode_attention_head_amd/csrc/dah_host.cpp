@@ -84,10 +84,24 @@ int plan_decode(int B, int num_heads, int cache_dtype, int max_seq_len, int num_
   const bool balanced_fits =
       B <= kMaxBalancedBatch && static_cast<long long>(B) * max_pages < (1LL << 31);
   int want = 0;  // splits for DAH_PLAN_SPLIT
-  if (num_splits == 1 || (num_splits == 0 && B >= num_cus && max_pages <= kMaxPagesPerSplit)) {
+  // DAH_DECODE_PLAN=per_sequence, balanced or split overrides the automatic
+  // choice (num_splits == 0) where that plan applies (a measurement aid, read
+  // once).
+  static const int forced_plan = []() -> int {
+    const char* e = getenv("DAH_DECODE_PLAN");
+    if (e == nullptr) return -1;
+    if (strcmp(e, "per_sequence") == 0) return DAH_PLAN_PER_SEQUENCE;
+    if (strcmp(e, "balanced") == 0) return DAH_PLAN_BALANCED;
+    if (strcmp(e, "split") == 0) return DAH_PLAN_SPLIT;
+    return -1;
+  }();
+  const bool auto_plan = num_splits == 0 && forced_plan < 0;
+  if (num_splits == 1 || (num_splits == 0 && forced_plan == DAH_PLAN_PER_SEQUENCE) ||
+      (auto_plan && B >= num_cus && max_pages <= kMaxPagesPerSplit)) {
     p.mode = DAH_PLAN_PER_SEQUENCE;
   } else if (num_splits == 0 && balanced_fits &&
-             B >= (bf16 && big_group ? kBalancedMinBatchMfma : kBalancedMinBatch)) {
+             (forced_plan == DAH_PLAN_BALANCED ||
+              (auto_plan && B >= (bf16 && big_group ? kBalancedMinBatchMfma : kBalancedMinBatch)))) {
     p.mode = DAH_PLAN_BALANCED;
   } else {
     p.mode = DAH_PLAN_SPLIT;

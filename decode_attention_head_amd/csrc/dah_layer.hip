@@ -6,8 +6,9 @@
 //   y = x1 + down(silu(gate) * up),  [gate | up] = gate_up(h2)
 //
 // The products run on the matrix cores (dah_linear.hip), which also take the
-// hidden-size RMSNorms on their input rows and the residual adds in their
-// stores (or in the reduce of their k slices: o_proj and down); the
+// hidden-size RMSNorms on their input rows, the SwiGLU activation in gate_up's
+// store, and the residual adds in their stores (or in the reduce of their k
+// slices: o_proj and down); the
 // attention step runs in dah_kernels.hip.  This file holds the
 // composition, the SwiGLU activation's kernel and the RMSNorm as a
 // standalone call (dah_rmsnorm).
@@ -87,7 +88,7 @@ size_t round_up(size_t n) { return (n + 255) / 256 * 256; }
 // attention's own workspace and, once the attention is done with it (the
 // launches are stream-ordered), the k-slice partials of o_proj and down.
 struct LayerBuffers {
-  size_t q, k, v, q_out, o, x1, gu, act, attn, total;
+  size_t q, k, v, q_out, o, x1, act, attn, total;
 };
 
 size_t shared_region(int B, int hidden, int inter, int num_heads, size_t attn_ws) {
@@ -111,7 +112,6 @@ LayerBuffers layer_buffers(int B, int hidden, int inter, int num_heads, size_t a
   L.q_out = take((size_t)B * num_heads * dah::kHeadDim * f);
   L.o = take((size_t)B * num_heads * dah::kHeadDim * f);
   L.x1 = take((size_t)B * hidden * f);
-  L.gu = take((size_t)B * 2 * inter * f);
   L.act = take((size_t)B * inter * f);
   L.attn = take(shared_region(B, hidden, inter, num_heads, attn_ws));
   L.total = at;
@@ -200,19 +200,18 @@ int decoder_layer_step(const float* x, const dah_layer_weights* w, int hidden, i
   float* q_out = reinterpret_cast<float*>(ws + L.q_out);
   float* o = reinterpret_cast<float*>(ws + L.o);
   float* x1 = reinterpret_cast<float*>(ws + L.x1);
-  float* gu = reinterpret_cast<float*>(ws + L.gu);
   float* act = reinterpret_cast<float*>(ws + L.act);
   void* attn_ws = attn > 0 ? ws + L.attn : nullptr;
   const size_t split = shared_region(B, hidden, inter, num_heads, 0);
   void* split_ws = split > 0 ? ws + L.attn : nullptr;
   const int qdim = num_heads * dah::kHeadDim;
 
-  // Six launches, up to nine with the attention's merge and the slice
+  // Five launches, up to eight with the attention's merge and the slice
   // reduces of o_proj and down: input_norm folded into qkv_proj and
   // post_attn_norm into gate_up (the products norm their input rows as they
-  // stream them), the residual adds into the stores of o_proj and down (or
-  // into their slice sums).  mlp.act keeps its own
-  // kernel: folded into down it would be redone once per column tile.
+  // stream them), mlp.act into gate_up's store (each tile holds the gate and
+  // up columns of the same outputs), the residual adds into the stores of
+  // o_proj and down (or into their slice sums).
   st = dah::qkv_proj(x, w->w_in, eps, w->w_qkv, B, hidden, num_heads, q, k, v, stream);
   if (st == DAH_OK)
     st = decode_attn_step_ex(q, k, v, w->q_gain, w->k_gain, eps, rope_theta, k_cache, v_cache,
@@ -220,8 +219,7 @@ int decoder_layer_step(const float* x, const dah_layer_weights* w, int hidden, i
                              num_heads, max_seq_len, num_splits, q_out, o, attn_ws, attn, stream);
   if (st == DAH_OK) st = dah_linear_ws(o, w->w_o, x, B, hidden, qdim, x1, split_ws, split, stream);
   if (st == DAH_OK)
-    st = dah_rmsnorm_linear(x1, w->w_post, eps, w->w_gate_up, B, 2 * inter, hidden, gu, stream);
-  if (st == DAH_OK) st = dah_silu_mul(gu, B, inter, act, stream);
+    st = dah_rmsnorm_swiglu(x1, w->w_post, eps, w->w_gate_up, B, inter, hidden, act, stream);
   if (st == DAH_OK)
     st = dah_linear_ws(act, w->w_down, x1, B, hidden, inter, y, split_ws, split, stream);
   return st;

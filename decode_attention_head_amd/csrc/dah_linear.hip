@@ -85,7 +85,21 @@ struct LinearArgs {
   // residual.
   int ksplit;
   float* part;
+  // gated > 0 (mlp.act folded in): w has 2 gated rows, the gate rows
+  // [0, gated) then the up rows [gated, 2 gated).  The product's columns
+  // come in groups of 32: the first 16 read gate rows j .. j+15, the next
+  // 16 up rows j .. j+15 (weight_row), so the lane that holds gate[t][j]
+  // in one 16 x 16 accumulator block holds up[t][j] in the next, and the
+  // store writes act[t][j] = silu(gate) * up to seg[0] (width gated).
+  int gated;
 };
+
+// The weight row of product column n (n itself unless gated).
+__device__ __forceinline__ int weight_row(const LinearArgs& a, int n) {
+  if (a.gated == 0) return n;
+  const int j = ((n >> 5) << 4) | (n & 15);
+  return (n & 16) ? a.gated + j : j;
+}
 
 // What the products read as their input row x[t] (the kernels' kXMode):
 //   kPlain  x as stored;
@@ -134,6 +148,25 @@ __device__ __forceinline__ void store_block(const LinearArgs& a, const Segment& 
       const size_t at = (size_t)t * s.width;
       const float y = acc[v] * scale[v];
       col[at] = rcol != nullptr ? y + rcol[at] : y;
+    }
+  }
+}
+
+// Stores the SwiGLU activation of a (gate, up) pair of 16 x 16 accumulator
+// blocks whose top-left output is (m, j0) of act: act[t][j] = silu(g) * u
+// with g and u the row-scaled products, silu(z) = z / (1 + e^-z) (the
+// mlp.act row, siluMul).
+__device__ __forceinline__ void store_gated(const LinearArgs& a, int m, int j0, const f32x4& g,
+                                            const f32x4& u, int lane,
+                                            const float (&scale)[4] = {1.f, 1.f, 1.f, 1.f}) {
+  const int r = lane >> 4, c = lane & 15;
+  float* col = a.seg[0].y + j0 + c;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int t = m + 4 * r + v;
+    if (t < a.T) {
+      const float gz = g[v] * scale[v], uz = u[v] * scale[v];
+      col[(size_t)t * a.gated] = gz / (1.0f + expf(-gz)) * uz;
     }
   }
 }
@@ -195,7 +228,8 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
   const float* gp = a.x_gain + k_begin + 8 * r;  // kNorm
   const uint16_t* wp[kNB];
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) wp[nb] = a.w + (size_t)(n0 + 16 * nb + c) * a.K + k_begin + 8 * r;
+  for (int nb = 0; nb < kNB; ++nb)
+    wp[nb] = a.w + (size_t)weight_row(a, n0 + 16 * nb + c) * a.K + k_begin + 8 * r;
 
   using Step = LinStep<kMB, kNB, kXMode>;
   // Ordinary (cacheable) loads: row tiles that share a weight tile find it
@@ -298,14 +332,8 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
   // group g is wave g + kMW q.
   const Segment sg = segment_of(a, n0);
   const int m_base = m_tile * 16 * kMB * kMW;
-  for (int job = wave; job < kMW * kMB * kNB; job += kLinWaves) {
-    const int g = job / (kMB * kNB), blk = job % (kMB * kNB);
-    f32x4 t = part[g][blk][lane];
-#pragma unroll
-    for (int q = 1; q < kKS; ++q) t += part[g + kMW * q][blk][lane];
-    float scale[4] = {1.f, 1.f, 1.f, 1.f};
+  auto row_scale = [&](int g, int mb, float (&scale)[4]) {
     if constexpr (kXMode == kNorm) {
-      const int mb = blk / kNB;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         float sum = 0.0f;
@@ -314,6 +342,35 @@ __global__ __launch_bounds__(kWave * kLinWaves) void linear_splitk_kernel(Linear
         scale[v] = inv_rms(sum, a.K, a.eps);
       }
     }
+  };
+  if constexpr (kNB % 2 == 0) {
+   if (a.gated) {
+    // (gate, up) block pairs
+    constexpr int kPairs = kNB / 2;
+    for (int job = wave; job < kMW * kMB * kPairs; job += kLinWaves) {
+      const int g = job / (kMB * kPairs), pr = job % (kMB * kPairs);
+      const int mb = pr / kPairs, nb = 2 * (pr % kPairs);
+      f32x4 tg = part[g][mb * kNB + nb][lane], tu = part[g][mb * kNB + nb + 1][lane];
+#pragma unroll
+      for (int q = 1; q < kKS; ++q) {
+        tg += part[g + kMW * q][mb * kNB + nb][lane];
+        tu += part[g + kMW * q][mb * kNB + nb + 1][lane];
+      }
+      float scale[4] = {1.f, 1.f, 1.f, 1.f};
+      row_scale(g, mb, scale);
+      store_gated(a, m_base + 16 * kMB * g + 16 * mb, ((n0 + 16 * nb) >> 5) << 4, tg, tu, lane,
+                  scale);
+    }
+    return;
+   }
+  }
+  for (int job = wave; job < kMW * kMB * kNB; job += kLinWaves) {
+    const int g = job / (kMB * kNB), blk = job % (kMB * kNB);
+    f32x4 t = part[g][blk][lane];
+#pragma unroll
+    for (int q = 1; q < kKS; ++q) t += part[g + kMW * q][blk][lane];
+    float scale[4] = {1.f, 1.f, 1.f, 1.f};
+    row_scale(g, blk / kNB, scale);
     store_block(a, sg, m_base + 16 * kMB * g + 16 * (blk / kNB), n0 + 16 * (blk % kNB), t, lane,
                 scale);
   }
@@ -378,7 +435,8 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
 #pragma unroll
   for (int i = 0; i < kW8; ++i) {
     const int idx = tid + kLdsThreads * i;
-    wsrc[i] = a.w + (size_t)(n0 + idx / (kBK / 8)) * a.K + k_base + 8 * (idx % (kBK / 8));
+    wsrc[i] = a.w + (size_t)weight_row(a, n0 + idx / (kBK / 8)) * a.K + k_base +
+              8 * (idx % (kBK / 8));
   }
   struct Chunk {
     float4 x[kX4];
@@ -493,7 +551,23 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
     }
     return sc;
   };
+  static_assert(kSN % 2 == 0, "gate and up blocks pair up within a wave");
   if constexpr (kWK == 1) {
+    if (a.gated) {
+#pragma unroll
+      for (int mb = 0; mb < kSM; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < kSN; nb += 2) {
+          const int mrow = wm * (kBM / kWM) + 16 * mb;
+          float sc[4];
+          const auto s4 = scales(mrow);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sc[v] = s4[v];
+          store_gated(a, m0 + mrow, ((n0 + wn * (kBN / kWN) + 16 * nb) >> 5) << 4, acc[mb][nb],
+                      acc[mb][nb + 1], lane, sc);
+        }
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < kSM; ++mb)
 #pragma unroll
@@ -513,6 +587,27 @@ __global__ __launch_bounds__(kLdsThreads) void linear_lds_kernel(LinearArgs a) {
 #pragma unroll
       for (int nb = 0; nb < kSN; ++nb) part[wk][(sub * kSM + mb) * kSN + nb][lane] = acc[mb][nb];
     __syncthreads();
+    if (a.gated) {
+      for (int job = wave; job < kWM * kWN * kSM * (kSN / 2); job += kLdsThreads / kWave) {
+        const int js = job / (kSM * (kSN / 2)), mb = (job / (kSN / 2)) % kSM;
+        const int nb = 2 * (job % (kSN / 2));
+        const int base = (js * kSM + mb) * kSN + nb;
+        f32x4 tg = part[0][base][lane], tu = part[0][base + 1][lane];
+#pragma unroll
+        for (int q = 1; q < kWK; ++q) {
+          tg += part[q][base][lane];
+          tu += part[q][base + 1][lane];
+        }
+        const int mrow = (js % kWM) * (kBM / kWM) + 16 * mb;
+        float sc[4];
+        const auto s4 = scales(mrow);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc[v] = s4[v];
+        store_gated(a, m0 + mrow, ((n0 + (js / kWM) * (kBN / kWN) + 16 * nb) >> 5) << 4, tg, tu,
+                    lane, sc);
+      }
+      return;
+    }
     for (int job = wave; job < kWM * kWN * kSM * kSN; job += kLdsThreads / kWave) {
       f32x4 t = part[0][job][lane];
 #pragma unroll
@@ -607,15 +702,18 @@ int pick_lds(const LinearArgs& a) {
 // the fastest shape or one within 3% of it in every case.
 // With the norm folded in (kNorm) the split-k tiles stop at 32 columns: the
 // gain in flight leaves no registers for 64.
+// A gated product (mlp.act folded in) needs its gate and up blocks side by
+// side in every wave: 2 or 4 column blocks per wave.
 LinearConfig pick_config(const LinearArgs& a, int x_mode = kPlain) {
   const int lds = pick_lds(a);
   if (lds != 0) return {lds, 0, 0, 0};
+  const int min_nb = a.gated ? 2 : 1;
   if (a.T > 16) {
     const int m_tiles = (a.T + 31) / 32;
-    for (int nb = x_mode == kPlain ? 4 : 2; nb >= 1; nb /= 2)
+    for (int nb = x_mode == kPlain ? 4 : 2; nb >= min_nb; nb /= 2)
       if (m_tiles * (a.N / (16 * nb)) >= kLinMinGroups) return {0, 2, nb, 1};
   }
-  return {0, 1, 1, 1};
+  return {0, 1, min_nb, 1};
 }
 
 // With a workspace for k slices (plain products into one segment), products
@@ -697,6 +795,7 @@ int launch_mode(const LinearArgs& a, const LinearConfig& c, hipStream_t stream) 
 #define DAH_LIN_CASE(MB, NB, MW) \
   if (c.mb == MB && c.nb == NB && c.mw == MW) return launch_cfg<MB, NB, MW, kXMode>(a, stream);
   DAH_LIN_CASE(1, 1, 1)
+  DAH_LIN_CASE(1, 2, 1)
   DAH_LIN_CASE(2, 1, 1)
   DAH_LIN_CASE(2, 2, 1)
   if constexpr (kXMode == kPlain) {
@@ -896,6 +995,28 @@ int dah_rmsnorm_linear(const float* x, const float* x_gain, float eps, const voi
   a.x_gain = x_gain;
   a.eps = eps;
   return launch_linear(a, static_cast<hipStream_t>(stream), kNorm);
+}
+
+int dah_rmsnorm_swiglu(const float* x, const float* x_gain, float eps, const void* w_gate_up,
+                       int T, int inter, int K, float* act, void* stream) {
+  int st = x_gain ? check_norm(x_gain, eps, "dah_rmsnorm_swiglu") : DAH_OK;
+  if (st == DAH_OK && (inter < 32 || inter % 32 != 0))
+    st = dah::set_error(DAH_ERR_SHAPE, "dah_rmsnorm_swiglu: inter = %d, need a positive "
+                        "multiple of 32", inter);
+  if (st == DAH_OK) st = dah::validate_linear(x, w_gate_up, T, 2 * inter, K, act);
+  if (st != DAH_OK) return st;
+  LinearArgs a = {};
+  a.x = x;
+  a.w = static_cast<const uint16_t*>(w_gate_up);
+  a.T = T;
+  a.N = 2 * inter;
+  a.K = K;
+  a.nseg = 1;
+  a.seg[0] = Segment{act, 0, inter, nullptr};
+  a.x_gain = x_gain;
+  a.eps = eps;
+  a.gated = inter;
+  return launch_linear(a, static_cast<hipStream_t>(stream), x_gain ? kNorm : kPlain);
 }
 
 int attn_o_proj(const float* o, const void* w_o, int T, int num_heads, int hidden, float* y,

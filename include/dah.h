@@ -192,7 +192,9 @@ int decode_attn_step(const float* q, const float* k_new, const float* v_new,
  * environment variable DAH_DECODE_KERNEL=valu or =mfma, read once per
  * process, overrides that where the other form is built (VALU: any float32
  * cache, bfloat16 at 2 query heads per KV head; matrix cores: bfloat16) -- a
- * measurement aid, reported here as well as used by the calls.
+ * measurement aid, reported here as well as used by the calls.  Likewise
+ * DAH_DECODE_PLAN=per_sequence, balanced or split replaces the automatic
+ * layout (num_splits 0) where that layout applies.
  * Returns a dah_status.
  */
 typedef enum {
@@ -398,6 +400,23 @@ int dah_rmsnorm_linear(const float* x, const float* x_gain, float eps, const voi
                        int N, int K, float* y, void* stream);
 
 /*
+ * dah_rmsnorm_swiglu -- the MLP's first half in one launch (the
+ * post_attn_norm, mlp.gate_up and mlp.act rows of the "Qwen3-0.6B" Model
+ * Spec page, "Compute-graph nodes"):
+ *   h = rmsnorm(x) as dah_rmsnorm_linear (x as stored when x_gain is NULL),
+ *   [gate | up] = h . w_gate_up^T, act[t][j] = silu(gate[t][j]) * up[t][j],
+ *   silu(z) = z / (1 + e^-z), j < inter.
+ *   x [T][K] float32; w_gate_up [2 inter][K] bfloat16, the gate rows then
+ *   the up rows (the checkpoint's order); act [T][inter] float32; inter a
+ *   positive multiple of 32, K of 256; 16-byte alignment.  Each product tile
+ *   holds gate and up columns of the same j side by side, so the activation
+ *   is applied as the tile is stored and [gate | up] is never written.
+ *   Errors as dah_rmsnorm_linear.
+ */
+int dah_rmsnorm_swiglu(const float* x, const float* x_gain, float eps, const void* w_gate_up,
+                       int T, int inter, int K, float* act, void* stream);
+
+/*
  * Products that split k over workgroups (the o_proj and down rows of the
  * "Qwen3-0.6B" Model Spec page, "Compute-graph nodes": K = H*128 or 3072
  * against N = 1024 outputs gives few output tiles for the chip).  Each
@@ -478,11 +497,11 @@ int dah_silu_mul(const float* gate_up, int T, int inter, float* act, void* strea
  *                partials of o_proj and down, which run through
  *                dah_linear_ws); contents need no initialisation.
  *
- * Six to nine launches in order on `stream`: qkv_proj (input_norm folded
+ * Five to eight launches in order on `stream`: qkv_proj (input_norm folded
  * in), the attention step (plus its merge when a sequence is cut over
- * workgroups), o_proj (plus its slice reduce when k is split), gate_up
- * (post_attn_norm folded in), mlp.act, down (plus its slice reduce).  The
- * attention's arguments are checked before the first.
+ * workgroups), o_proj (plus its slice reduce when k is split), gate_up with
+ * post_attn_norm and mlp.act folded in (dah_rmsnorm_swiglu), down (plus its
+ * slice reduce).  The attention's arguments are checked before the first.
  */
 typedef struct {
   const float* w_in;       /* input_norm gain [hidden], float32 */

@@ -452,16 +452,18 @@ def test_linear_ws_plan():
 @pytest.mark.parametrize("B,H,L", [(256, 16, 2048), (256, 64, 2048), (32, 16, 16384),
                                    (4, 40, 40960)])
 def test_layer_workspace_shares_one_region(B, H, L):
-    """dah_layer_workspace_bytes: the intermediates (each rounded up to 256
-    bytes), then one region as large as the larger of the attention's
-    workspace and the k-slice partials of o_proj and down."""
+    """dah_layer_workspace_bytes: the intermediates q, k, v, q_out, o, x1 and
+    the activation (each rounded up to 256 bytes; gate_up's output is never
+    stored, the activation is applied in its product), then one region as
+    large as the larger of the attention's workspace and the k-slice partials
+    of o_proj and down."""
     lib = _lib()
     hidden, inter = 1024, 3072
     r = lambda n: (n + 255) // 256 * 256   # noqa: E731
     f = 4
     inter_bytes = sum(r(n) for n in (B * H * 128 * f, B * 8 * 128 * f, B * 8 * 128 * f,
                                      B * H * 128 * f, B * H * 128 * f, B * hidden * f,
-                                     B * 2 * inter * f, B * inter * f))
+                                     B * inter * f))
     attn = lib.dah_workspace_bytes_ex(B, H, 1, L, 0)
     split = max(lib.dah_linear_workspace_bytes(B, hidden, H * 128),
                 lib.dah_linear_workspace_bytes(B, hidden, inter))

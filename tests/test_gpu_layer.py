@@ -127,6 +127,42 @@ def test_rmsnorm_linear_parity(T, N, K):
            f"{float(np.max(err / bound)):.3f} of bound")
 
 
+@pytest.mark.parametrize("inter,K,norm", [(3072, 1024, True), (1280, 2560, True),
+                                          (96, 256, True), (3072, 1024, False)])
+@pytest.mark.parametrize("T", [1, 7, 17, 33, 256, 300, 1000])
+def test_rmsnorm_swiglu_parity(T, inter, K, norm):
+    """dah_rmsnorm_swiglu: the RMS-normed rows' product with the gate and up
+    rows, the activation applied in the store, against the oracle's rmsnorm,
+    linear and silu_mul, on both product kernels.  Gate: with e the product
+    bound of the normed input for each of gate and up (as for
+    dah_rmsnorm_linear), act = silu(g) u moves by at most
+    1.1 e_g |u| + |silu(g)| e_u + 1.1 e_g e_u (|silu'| <= 1.1), plus the
+    float32 rounding of the activation (2e-6 of |act|)."""
+    import torch
+    dah = _dah()
+    x = _rand((T, K), 5 * T + K, 2.0)
+    g = (1.0 + 0.1 * _rand((K,), K + 1)) if norm else None
+    w = (_rand((2 * inter, K), inter + K) / np.sqrt(K)).to(torch.bfloat16)
+    act = torch.full((T + 1, inter), float("nan"), device="cuda")
+    dah.rmsnorm_swiglu(x, g, w, act=act[:T])
+    torch.cuda.synchronize()
+    assert torch.isnan(act[T]).all(), "wrote past the output"
+    xn = L.rmsnorm(x.cpu().numpy(), g.cpu().numpy()) if norm else x.cpu().numpy()
+    wb = _bits(w)
+    gu = P.linear(xn, wb)
+    ref = L.silu_mul(gu)
+    eb = (2.0 ** -16 + 2e-6) * P.linear(np.abs(xn), np.abs(O.bf16_bits_to_f64(wb)), "f64")
+    gate, up = gu[:, :inter], gu[:, inter:]
+    e_g, e_u = eb[:, :inter], eb[:, inter:]
+    silu = gate / (1.0 + np.exp(-gate))
+    bound = 1.1 * e_g * np.abs(up) + np.abs(silu) * e_u + 1.1 * e_g * e_u + \
+        2e-6 * np.abs(ref) + 1e-30
+    err = np.abs(act[:T].cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= bound), float(np.max(err / bound))
+    _print(f"[rmsnorm_swiglu] T={T} I={inter} K={K} norm={norm}: "
+           f"{float(np.max(err / bound)):.3f} of bound")
+
+
 def _layer_case(name, H):
     w = dataclasses.replace(W.WORKLOADS[name], num_heads=H)
     t, seq_lens, table, _ = build_layer(w)
