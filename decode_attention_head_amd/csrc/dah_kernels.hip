@@ -774,21 +774,25 @@ struct MfmaStash {
 };
 
 // Scores of one page: lane (r, c) gets head c at positions 4v + r.  One
-// accumulator per query term keeps three independent chains of four
-// products in flight instead of one chain of twelve.
-__device__ __forceinline__ f32x4 page_scores(const KTileMfma& K, const u32x4 (&qb)[4][3]) {
-  f32x4 s[3];
+// accumulator per query term (kT of them) keeps kT independent chains of
+// four products in flight instead of one chain of 4 kT.
+template <int kT>
+__device__ __forceinline__ f32x4 page_scores(const KTileMfma& K, const u32x4 (&qb)[4][kT]) {
+  f32x4 s[kT];
 #pragma unroll
-  for (int t = 0; t < 3; ++t) s[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < kT; ++t) s[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const bf16x8 a = __builtin_bit_cast(bf16x8, K.w[kk]);
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
+    for (int t = 0; t < kT; ++t)
       s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qb[kk][t]),
                                                       s[t], 0, 0, 0);
   }
-  return (s[0] + s[1]) + s[2];
+  f32x4 r = s[0];
+#pragma unroll
+  for (int t = 1; t < kT; ++t) r += s[t];
+  return r;
 }
 
 // Online-softmax state of the MFMA decode.  m and l are per lane for head c
@@ -862,14 +866,17 @@ __device__ __forceinline__ void attend_page_mfma(const KTileMfma& K, Tile<DAH_BF
   }
 }
 
-// Splits 8 float32 values into the three bfloat16 terms of the score
-// product's B operand.
-__device__ __forceinline__ void split3(const float (&x)[8], u32x4 (&out)[3]) {
+// Splits 8 float32 values into kT bfloat16 terms of the score product's B
+// operand, each the rounding of what the previous terms leave: three terms
+// hold a float32 value exactly (8 + 8 + 8 significant bits), two to a
+// relative 2^-18.
+template <int kT>
+__device__ __forceinline__ void split_terms(const float (&x)[8], u32x4 (&out)[kT]) {
   float rem[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) rem[e] = x[e];
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
+  for (int t = 0; t < kT; ++t) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[t][i] = pack_bf16x2(rem[2 * i], rem[2 * i + 1]);
@@ -1072,14 +1079,14 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
       const float4 x0 = sq[0], x1 = sq[1];
       x[0] = x0.x * qscale; x[1] = x0.y * qscale; x[2] = x0.z * qscale; x[3] = x0.w * qscale;
       x[4] = x1.x * qscale; x[5] = x1.y * qscale; x[6] = x1.z * qscale; x[7] = x1.w * qscale;
-      split3(x, qb[kk]);
+      split_terms<3>(x, qb[kk]);
     }
   } else {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qv[kk][e] *= qscale;
-      split3(qv[kk], qb[kk]);
+      split_terms<3>(qv[kk], qb[kk]);
     }
   }
   if (col >= kG) {
@@ -1745,7 +1752,7 @@ __global__ __launch_bounds__(kWave * kDecodeWavesPerBlock) void chunk_attn_kerne
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) qv[kk][e] *= qscale;
-    split3(qv[kk], qb[kk]);
+    split_terms<3>(qv[kk], qb[kk]);
   }
   if (!live) {
 #pragma unroll
@@ -1903,8 +1910,8 @@ __device__ __forceinline__ u32x2 read_v_tr(const char* base, int off) {
 // step_scores: K[j] holds page j's K tile; lane (r, c) gets column c's
 // scores at positions 4v + r of each page.  kMasked: column c sees only the
 // positions of page j below climit[j] (per lane; 0 = none of the page).
-template <int kP, bool kMasked>
-__device__ __forceinline__ void step_scores(const KTileMfma (&K)[kP], const u32x4 (&qb)[4][3],
+template <int kP, bool kMasked, int kT>
+__device__ __forceinline__ void step_scores(const KTileMfma (&K)[kP], const u32x4 (&qb)[4][kT],
                                             int lane, const int (&climit)[kP], f32x4 (&s)[kP]) {
   const int r = lane >> 4;
 #pragma unroll
@@ -1973,41 +1980,47 @@ __device__ __forceinline__ void step_weights_pv(const f32x4 (&s)[kP],
 }
 
 // Chunks of several tiles (prefill, longer verification): the tiles of one
-// KV head share each K/V page through LDS.  A workgroup of 8 waves takes one
-// sequence, kHG = 8 / kTG KV heads and kTG consecutive token tiles, one
-// (head, tile) per wave -- 8 tiles of one head for long chunks, 2 tiles of 4
-// heads for chunks of two tiles, so that every wave has work.  Pages go in
-// steps of kP (2, or 1 with 4 heads): per step the 512 threads load the
-// heads' K and V tiles of the step's pages (16 bytes per thread, page and
-// head, 8 pieces in flight per thread) and write them to one of three LDS
-// stages -- K with its 16-byte pieces XOR-swizzled by position (kswz), so
-// that the score product's reads (16 positions at one dim offset) fall on
-// distinct banks, V swizzled for the transpose reads (vswz) and zero past the
-// sequence (or past the last page); each wave then scores the step's pages
-// as chunk_attn_kernel does (step_scores) and, one step later, weighs them
-// and sums V (step_weights_pv).  The cache
-// is read once per kTG tiles, and the workgroups of one KV head (for
-// kTG = 8) are consecutive modulo 8, which keeps them on one XCD, where they
-// share the pages through L2.
+// KV head share each K/V page through LDS.  A workgroup of 4 waves, one per
+// SIMD, takes one sequence, kHG = 4 / kTG KV heads and kTG consecutive token
+// tiles, one (head, tile) per wave: 4 tiles of one head for long chunks, 2
+// tiles of 2 heads for chunks of two tiles.  Two workgroups share a CU, and
+// since each waits only at its own barriers, one's matrix-core products
+// overlap the other's LDS traffic and softmax; at 8 waves per workgroup the
+// barrier put every wave of the CU in the same phase, and the CU's matrix
+// cores ran about half the time.  Pages go in steps of kP (2 with one head,
+// 1 with two): per step the 256 threads load the heads' K and V tiles of the
+// step's pages (one 16-byte piece of K and one of V per thread, page and
+// head, kDepth steps in flight) and write them to one of three LDS stages --
+// K with its 16-byte pieces XOR-swizzled by position (kswz), so that the
+// score product's reads (16 positions at one dim offset) fall on distinct
+// banks, V swizzled for the transpose reads (vswz) and zero past the
+// sequence or past the last page; each wave then scores the step's pages
+// (step_scores) and, one step later, weighs them and sums V
+// (step_weights_pv).  The queries enter the score product as two bf16 terms
+// (to a relative 2^-18, the weights' own precision) rather than the decode's
+// three, which takes a sixth of the products.  The cache is read once per
+// kTG tiles, and the workgroups of one KV head (kTG = 4) are consecutive
+// modulo 8, which keeps them on one XCD, where they share the pages through
+// L2.
 
-constexpr int kChunkWaves = kDecodeWavesPerBlock;  // (head, tile) pairs per workgroup
-constexpr int kChunkRing = 8;                      // 16-byte pieces in flight per thread
-constexpr int kChunkPrefillMinTiles = 2;           // chunks of this many tiles share pages
+constexpr int kChunkWaves = 4;                // (head, tile) pairs per workgroup
+constexpr int kChunkQTerms = 2;               // bf16 terms of each query element
+constexpr int kChunkPrefillMinTiles = 2;      // chunks of this many tiles share pages
 
 template <int kG, int kTG>
-__global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(ChunkArgs a) {
   constexpr int kH = kG * kKvHeads;
-  constexpr int kTpt = 16 / kG;  // tokens per tile
+  constexpr int kTpt = 16 / kG;            // tokens per tile
   constexpr int kHG = kChunkWaves / kTG;   // KV heads per workgroup
-  constexpr int kP = kHG == 4 ? 1 : 2;     // pages per step
-  constexpr int kDepth = kChunkRing / (kHG * kP);  // steps in flight
+  constexpr int kP = kHG == 1 ? 2 : 1;     // pages per step
+  constexpr int kDepth = kHG == 1 ? 4 : 2;  // steps in flight (16 or 8 pieces per thread)
   using TileV = Tile<DAH_BF16>;
   constexpr int kTileBytes = (int)TileV::kTileBytes;
   constexpr int kHeadBytes = 2 * kTileBytes;  // K and V of one head and page in a stage
   constexpr int kPageBytes = kHG * kHeadBytes;
-  static_assert(kHG * kTG == kChunkWaves && kKvHeads % kHG == 0, "heads x tiles = 8 waves");
-  static_assert(kWave * kChunkWaves * 16 == kHeadBytes, "one 16-byte piece per thread and head");
-  static_assert(kDepth >= 2 && kDepth % 2 == 0, "stages alternate within the unrolled ring");
+  static_assert(kHG * kTG == kChunkWaves && kKvHeads % kHG == 0 && kHG <= 2,
+                "heads x tiles = 4 waves");
+  static_assert(kWave * kChunkWaves * 16 == kTileBytes, "one 16-byte piece per thread and tile");
   __shared__ __attribute__((aligned(16))) char stage[3][kP * kPageBytes];  // [stage][page][head][K|V]
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -2024,7 +2037,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   const int t0 = min(max(a.cu_tokens[b], 0), a.total);
   const int t1 = min(max(a.cu_tokens[b + 1], t0), a.total);
   const int n = t1 - t0;
-  const int tile0 = grp * kTG;
+  const int tile0 = grp * kTG;   // first tile of the workgroup
   if (tile0 * kTpt >= n) return;  // the whole workgroup
   const int tile = tile0 + tw;
   const int i0 = tile * kTpt;
@@ -2044,7 +2057,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
     return;  // the whole workgroup (the condition is uniform)
   }
 
-  // Within the preconditions every live tile is below a.tiles.
+  // Within the preconditions every live token is below a.tiles * kTpt.
   const int ntok = live ? min(kTpt, n - i0) : 1;
   const int pos0 = seq_len - n + i0;  // position of the wave's first token
   const int pmax = pos0 + ntok - 1;
@@ -2061,54 +2074,57 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   typedef const __attribute__((address_space(4))) int32_t* ConstI32;
   const ConstI32 bt = (ConstI32)(a.block_table + (size_t)b * a.max_pages_per_seq);
   const int64_t page_bytes = (int64_t)kKvHeads * kTileBytes;
-  // This thread's 16-byte piece of every page and head: K pieces for threads
-  // 0..255, V pieces for 256..511; its place in the stage (K and V swizzled).
-  const int kv = tid >> 8, piece = tid & 255;
-  const char* src = (kv ? a.v_cache : a.k_cache) + (int64_t)gh * kHG * kTileBytes + 16 * piece;
-  const int ppos = piece >> 4, pc = piece & 15;
-  const int dst = kv ? kTileBytes + 256 * ppos + 16 * (pc ^ (2 * vswz(ppos)))
-                     : 256 * ppos + 16 * (pc ^ kswz(ppos));
+  // This thread's 16-byte piece of every page and head's K and V tiles, and
+  // its places in the stage (K and V swizzled).
+  const char* ksrc = a.k_cache + (int64_t)gh * kHG * kTileBytes + 16 * tid;
+  const char* vsrc = a.v_cache + (int64_t)gh * kHG * kTileBytes + 16 * tid;
+  const int ppos = tid >> 4, pc = tid & 15;
+  const int kdst = 256 * ppos + 16 * (pc ^ kswz(ppos));
+  const int vdst = kTileBytes + 256 * ppos + 16 * (pc ^ (2 * vswz(ppos)));
   bool bad_page = false;
-  // The pieces of step s's pages (zeros for pages past `last`, which are not read).
-  auto fetch = [&](u32x4 (&out)[kP][kHG], int s) {
+  // The pieces of step s's pages.  Every step loads -- pages past `last`
+  // as page `last` again (their scores are masked, their V staged as zeros)
+  // -- so that no load is conditional and the wait for a ring slot counts
+  // only the loads issued before it.
+  auto fetch = [&](u32x4 (&out)[kP][kHG][2], int s) {
 #pragma unroll
     for (int j = 0; j < kP; ++j) {
       const int p = kP * s + j;
-      if (p <= last) {
-        const int id = bt[p];
-        const bool ok = id >= 0 && id < a.num_pages;
-        bad_page |= !ok && p <= wave_last;
-        const char* at = src + (int64_t)(ok ? id : 0) * page_bytes;
+      const int id = bt[min(p, last)];
+      const bool ok = id >= 0 && id < a.num_pages;
+      bad_page |= !ok && p <= wave_last;
+      const int64_t off = (int64_t)(ok ? id : 0) * page_bytes;
 #pragma unroll
-        for (int h = 0; h < kHG; ++h) out[j][h] = *reinterpret_cast<const u32x4*>(at + h * kTileBytes);
-      } else {
-#pragma unroll
-        for (int h = 0; h < kHG; ++h) out[j][h] = u32x4{0u, 0u, 0u, 0u};
+      for (int h = 0; h < kHG; ++h) {
+        out[j][h][0] = *reinterpret_cast<const u32x4*>(ksrc + off + h * kTileBytes);
+        out[j][h][1] = *reinterpret_cast<const u32x4*>(vsrc + off + h * kTileBytes);
       }
     }
   };
+  // Steps in whole rings: those past the last page only stage (no wave
+  // works on them).
   const int steps = (last + kP) / kP;
-  u32x4 ring[kDepth][kP][kHG];
+  const int steps_run = (steps + kDepth - 1) / kDepth * kDepth;
+  u32x4 ring[kDepth][kP][kHG][2];
 #pragma unroll
-  for (int i = 0; i < kDepth; ++i)
-    if (i < steps) fetch(ring[i], i);
+  for (int i = 0; i < kDepth; ++i) fetch(ring[i], i);
 
   float qv[4][8];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) load8(a.q + qrow * kHeadDim + 32 * kk + 8 * row, qv[kk]);
   const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  u32x4 qb[4][3];
+  u32x4 qb[4][kChunkQTerms];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) qv[kk][e] *= qscale;
-    split3(qv[kk], qb[kk]);
+    split_terms<kChunkQTerms>(qv[kk], qb[kk]);
   }
   if (!col_live) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int t = 0; t < 3; ++t) qb[kk][t] = u32x4{0u, 0u, 0u, 0u};
+      for (int t = 0; t < kChunkQTerms; ++t) qb[kk][t] = u32x4{0u, 0u, 0u, 0u};
   }
   PrefillState st;
   st.m = -INFINITY;
@@ -2141,59 +2157,60 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   bool prev_on = false;  // step s - 1 awaits its softmax and V sum
   int cur = 0;           // stage of step s
   int prev = 0;          // stage of step s - 1
-  for (int s0 = 0; s0 < steps; s0 += kDepth) {
+  for (int s0 = 0; s0 < steps_run; s0 += kDepth) {
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) {
       const int s = s0 + i;
-      if (s < steps) {
-        // V rows past the sequence (never written) are staged as zeros.
-        char* stg = &stage[cur][0];
+      char* stg = &stage[cur][0];
+#pragma unroll
+      for (int j = 0; j < kP; ++j) {
+        // V rows past the sequence (never written) or past the last page
+        // are staged as zeros.
+        const bool past = kP * s + j > last || kPage * (kP * s + j) + ppos >= seq_len;
+#pragma unroll
+        for (int h = 0; h < kHG; ++h) {
+          char* at = stg + j * kPageBytes + h * kHeadBytes;
+          *reinterpret_cast<u32x4*>(at + kdst) = ring[i][j][h][0];
+          *reinterpret_cast<u32x4*>(at + vdst) = past ? u32x4{0u, 0u, 0u, 0u} : ring[i][j][h][1];
+        }
+      }
+      __syncthreads();
+      fetch(ring[i], s + kDepth);
+      const int p0 = kP * s;
+      const bool on = p0 <= wave_last;
+      f32x4 scur[kP];
+      if (on) {
+        KTileMfma K[kP];
 #pragma unroll
         for (int j = 0; j < kP; ++j) {
-          const bool past = kv && kPage * (kP * s + j) + ppos >= seq_len;
+          const char* sp = stg + j * kPageBytes;
 #pragma unroll
-          for (int h = 0; h < kHG; ++h)
-            *reinterpret_cast<u32x4*>(stg + j * kPageBytes + h * kHeadBytes + dst) =
-                past ? u32x4{0u, 0u, 0u, 0u} : ring[i][j][h];
+          for (int kk = 0; kk < 4; ++kk) K[j].w[kk] = *reinterpret_cast<const u32x4*>(sp + kaddr[kk]);
         }
-        __syncthreads();
-        if (s + kDepth < steps) fetch(ring[i], s + kDepth);
-        const int p0 = kP * s;
-        const bool on = p0 <= wave_last;
-        f32x4 scur[kP];
-        if (on) {
-          KTileMfma K[kP];
+        if (p0 + kP - 1 < first_masked && p0 + kP - 1 <= wave_last) {
+          const int cl[kP] = {};
+          step_scores<kP, false>(K, qb, lane, cl, scur);
+        } else {
+          int cl[kP];
 #pragma unroll
           for (int j = 0; j < kP; ++j) {
-            const char* sp = stg + j * kPageBytes;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) K[j].w[kk] = *reinterpret_cast<const u32x4*>(sp + kaddr[kk]);
+            const int p = p0 + j;
+            cl[j] = p > wave_last ? 0 : p < first_masked ? kPage : climit_pos - kPage * p + 1;
           }
-          if (p0 + kP - 1 < first_masked && p0 + kP - 1 <= wave_last) {
-            const int cl[kP] = {};
-            step_scores<kP, false>(K, qb, lane, cl, scur);
-          } else {
-            int cl[kP];
-#pragma unroll
-            for (int j = 0; j < kP; ++j) {
-              const int p = p0 + j;
-              cl[j] = p > wave_last ? 0 : p < first_masked ? kPage : climit_pos - kPage * p + 1;
-            }
-            step_scores<kP, true>(K, qb, lane, cl, scur);
-          }
+          step_scores<kP, true>(K, qb, lane, cl, scur);
         }
-        if (prev_on) {
-          const char* vpage[kP];
-#pragma unroll
-          for (int j = 0; j < kP; ++j) vpage[j] = &stage[prev][j * kPageBytes];
-          step_weights_pv<kP>(sprev, vpage, vaddr, st);
-        }
-#pragma unroll
-        for (int j = 0; j < kP; ++j) sprev[j] = scur[j];
-        prev_on = on;
-        prev = cur;
-        cur = cur == 2 ? 0 : cur + 1;
       }
+      if (prev_on) {
+        const char* vpage[kP];
+#pragma unroll
+        for (int j = 0; j < kP; ++j) vpage[j] = &stage[prev][j * kPageBytes];
+        step_weights_pv<kP>(sprev, vpage, vaddr, st);
+      }
+#pragma unroll
+      for (int j = 0; j < kP; ++j) sprev[j] = scur[j];
+      prev_on = on;
+      prev = cur;
+      cur = cur == 2 ? 0 : cur + 1;
     }
   }
   if (prev_on) {
@@ -2209,7 +2226,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves) void chunk_prefill_kernel(Chun
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (ti >= ntok) return;
+  if (!col_live) return;
   const float scale = bad_page ? NAN : 1.0f / l;
   float* orow = a.o + (((size_t)t0 + i0 + ti) * kH + g * kG + hh) * kHeadDim + 4 * row;
 #pragma unroll
@@ -2415,14 +2432,12 @@ int launch_chunk(const float* q, const float* k_new, const float* v_new, const f
     if (st != DAH_OK) return;
     c.tiles = (max_chunk + kTpt - 1) / kTpt;
     if (c.tiles >= kChunkPrefillMinTiles) {
-      // Tiles per workgroup: 2 or 4 for chunks of that many tiles (4 or 2
-      // KV heads per workgroup), else 8 of one head.
+      // Tiles per workgroup: 2 for chunks of two tiles (2 KV heads per
+      // workgroup), else 4 of one head.
       if (c.tiles <= 2)
         launch_chunk_prefill<kG, 2>(c, B, stream);
-      else if (c.tiles <= 4)
-        launch_chunk_prefill<kG, 4>(c, B, stream);
       else
-        launch_chunk_prefill<kG, 8>(c, B, stream);
+        launch_chunk_prefill<kG, 4>(c, B, stream);
       st = check_launch("chunk_prefill_kernel");
     } else {
       chunk_attn_kernel<kG><<<dim3((unsigned)((long long)B * c.tiles)),

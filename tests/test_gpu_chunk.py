@@ -3,7 +3,8 @@ within the chunk: chunked prefill and verification of drafted tokens),
 through the C ABI, against the oracle's chunk_step.
 
 With a bfloat16 cache the kernels run on the matrix cores (q as three bf16
-terms, weights as two), so the gates are the bf16 ones: max abs error 2e-2,
+terms in the one-tile kernel and two in the shared-page one, weights as
+two), so the gates are the bf16 ones: max abs error 2e-2,
 relative-to-max <= 1e-4, and q_out within 1e-5.  A float32 cache runs every
 token as a VALU decode and gets the strict float32 gates: o and q_out within
 1e-5, appended keys within 1e-5 of the exact values.  The appended keys must be
@@ -239,8 +240,8 @@ def test_out_of_domain_sequences(c, over, dt):
     """seq_len < n_b or > max_seq_len (and n_b > max_chunk): NaN outputs,
     nothing appended; an empty chunk: nothing; other sequences unaffected.
     With a bfloat16 cache, chunks of 3 tokens take the one-tile kernel, of 20
-    the shared-page one (10 tiles in two workgroups per KV head); a float32
-    cache takes the per-token kernel."""
+    the shared-page one (three 8-token tiles, one workgroup per KV head); a
+    float32 cache takes the per-token kernel."""
     import torch
     lens_old = [20, 20, 20, 20] + ([20] if over else [])
     chunks = [c, c, 0, c] + ([c + 4] if over else [])
