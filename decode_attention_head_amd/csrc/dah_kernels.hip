@@ -886,10 +886,11 @@ __device__ __forceinline__ void split_terms(const float (&x)[8], u32x4 (&out)[kT
   }
 }
 
-// Ranges of at least this many pages are visited in ascending page order
+// Ranges whose pages before the final one number at least this many (65
+// pages or more in all) are visited in ascending page order
 // (decode_range_mfma); shorter ones, where the sort costs more than the
 // locality returns, in table order.
-constexpr int kSortMinPages = 64;
+constexpr int kSortMinLeadingPages = 64;
 
 // Sorts the 128 values a wave holds as element e = lane + 64 r (a0: r = 0,
 // a1: r = 1) into ascending order: a bitonic network, compare-exchanges at
@@ -985,7 +986,7 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeArgs& a, int b, in
   // own copy of the ids, so the 8 waves agree without a barrier.  Attention
   // is independent of the order of positions (up to float32 rounding).
   const int n_sorted = last - p0;
-  const bool sorted = n_sorted >= kSortMinPages && n_sorted <= 128;
+  const bool sorted = n_sorted >= kSortMinLeadingPages && n_sorted <= 128;
   int key0 = INT32_MAX, key1 = INT32_MAX;
   if (sorted) {
     const int32_t* ids = a.block_table + (size_t)b * a.max_pages_per_seq + p0;
