@@ -1,6 +1,7 @@
 """CPU checks of bench.py's host-side pieces: the oracle leg's process pool
 returns exactly what the oracle computes in-process (same sequences, same
-order, every row), in both its parallel and its single-core mode, and the
+order, every row), in both its parallel and its single-core mode and over
+repeated passes, and the
 benchmark refuses more than one GPU before touching any device."""
 import os
 import subprocess
@@ -52,6 +53,9 @@ def test_oracle_pool_matches_in_process_oracle():
         q1, o1, _ = pool.run(snap, "s", "bf16", 5e6, rows=[4, 0, 2], serial=True)
         assert np.array_equal(o1, want["o"][[4, 0, 2]])
         assert np.array_equal(q1, want["q_out"][[4, 0, 2]])
+        # repeated passes (the baseline's timing) return the same rows
+        q3, o3, _ = pool.run(snap, "r", "bf16", 5e6, repeat=3)
+        assert np.array_equal(q3, want["q_out"]) and np.array_equal(o3, want["o"])
     finally:
         pool.close()
     for path in pool.dirs:
