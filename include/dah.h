@@ -328,7 +328,10 @@ size_t dah_workspace_bytes_ex(int B, int num_heads, int cache_dtype, int max_seq
  *
  * Two launches (append, attention), no workspace.  A bfloat16 cache runs on
  * the matrix cores, each cached page read once per tile of 16/G tokens (or
- * once per 8 such tiles, shared through LDS, for longer chunks); a float32
+ * once per 4 such tiles, shared through LDS, for longer chunks: there q
+ * enters the score product as two bfloat16 terms, to a relative 2^-18 like
+ * the softmax weights, where the one-tile kernel and the decode use three);
+ * a float32
  * cache runs every token as its own decode on the VALU path (each token
  * reads its prefix: meant for verification-sized chunks and strict-parity
  * runs).  A sequence with
