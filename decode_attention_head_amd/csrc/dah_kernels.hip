@@ -1925,96 +1925,137 @@ __device__ __forceinline__ void step_scores(const KTileMfma (&K)[kP], const u32x
   }
 }
 
+// A lane's LDS offsets within a stage page: K piece kk of its score-product
+// row (kb + 64 (kk ^ kq)) and V transpose-read nb (vb + 32 (nb ^ vx)).  With
+// one block per wave the twelve offsets stay in registers; with two, whose
+// state leaves no room for them, they are formed at each use.
+template <bool kTable>
+struct StageOffsets {
+  int kb, kq, vb, vx;
+  __device__ __forceinline__ int k(int kk) const { return kb + 64 * (kk ^ kq); }
+  __device__ __forceinline__ int v(int nb) const { return vb + 32 * (nb ^ vx); }
+};
+template <>
+struct StageOffsets<true> {
+  int ko[4], vo[8];
+  __device__ __forceinline__ int k(int kk) const { return ko[kk]; }
+  __device__ __forceinline__ int v(int nb) const { return vo[nb]; }
+};
+
 // step_weights_pv: the online softmax over a step's scores and the weighted
-// sum of its V pages, vpage[j] the staged V of page j (vaddr: this lane's
-// transpose-read offsets).  The stage holds zeros for positions past the
-// sequence, so V needs no clearing.
-template <int kP>
-__device__ __forceinline__ void step_weights_pv(const f32x4 (&s)[kP],
-                                                const char* const (&vpage)[kP],
-                                                const int (&vaddr)[8], PrefillState& st) {
-  float pmax = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
-  if constexpr (kP == 2) pmax = fmaxf(pmax, fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  const float pm = max_over_rows(pmax);
-  const bool move = pm > st.m + kMaxLag;
-  if (__builtin_amdgcn_ballot_w64(move) != 0) {
-    const float mn = move ? pm : st.m;
-    const float alpha = mn == st.m ? 1.0f : fast_exp2(st.m - mn);
-    st.m = mn;
-    st.l *= alpha;
+// sum of its V pages, for the kCB 16-column blocks of a wave (each with its
+// own state): vpage[j] the staged V of page j, off this lane's transpose-read
+// offsets.  Every V operand read from the stage feeds all kCB blocks'
+// products.  The stage holds zeros for positions past the sequence, so V
+// needs no clearing.
+template <int kCB, int kP, class Off>
+__device__ __forceinline__ void step_weights_pv(const f32x4 (&s)[kCB][kP],
+                                                 const char* const (&vpage)[kP],
+                                                 const Off& off, PrefillState (&st)[kCB]) {
+  uint32_t hw[kCB][kP][2], lw[kCB][kP][2];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) st.acc[nb] *= alpha;
-  }
-  const float mu = st.m == -INFINITY ? 0.0f : st.m;
-  uint32_t hw[kP][2], lw[kP][2];
+  for (int cb = 0; cb < kCB; ++cb) {
+    float pmax = fmaxf(fmaxf(s[cb][0][0], s[cb][0][1]), fmaxf(s[cb][0][2], s[cb][0][3]));
+    if constexpr (kP == 2)
+      pmax = fmaxf(pmax, fmaxf(fmaxf(s[cb][1][0], s[cb][1][1]), fmaxf(s[cb][1][2], s[cb][1][3])));
+    const float pm = max_over_rows(pmax);
+    const bool move = pm > st[cb].m + kMaxLag;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float mn = move ? pm : st[cb].m;
+      const float alpha = mn == st[cb].m ? 1.0f : fast_exp2(st[cb].m - mn);
+      st[cb].m = mn;
+      st[cb].l *= alpha;
 #pragma unroll
-  for (int j = 0; j < kP; ++j) {
-    float p[4];
+      for (int nb = 0; nb < 8; ++nb) st[cb].acc[nb] *= alpha;
+    }
+    const float mu = st[cb].m == -INFINITY ? 0.0f : st[cb].m;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[j][v] - mu);
-    st.l += (p[0] + p[1]) + (p[2] + p[3]);
-    hw[j][0] = pack_bf16x2(p[0], p[1]);
-    hw[j][1] = pack_bf16x2(p[2], p[3]);
-    lw[j][0] = pack_bf16x2(p[0] - bf16_lo(hw[j][0]), p[1] - bf16_hi(hw[j][0]));
-    lw[j][1] = pack_bf16x2(p[2] - bf16_lo(hw[j][1]), p[3] - bf16_hi(hw[j][1]));
+    for (int j = 0; j < kP; ++j) {
+      float p[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[cb][j][v] - mu);
+      st[cb].l += (p[0] + p[1]) + (p[2] + p[3]);
+      hw[cb][j][0] = pack_bf16x2(p[0], p[1]);
+      hw[cb][j][1] = pack_bf16x2(p[2], p[3]);
+      lw[cb][j][0] = pack_bf16x2(p[0] - bf16_lo(hw[cb][j][0]), p[1] - bf16_hi(hw[cb][j][0]));
+      lw[cb][j][1] = pack_bf16x2(p[2] - bf16_lo(hw[cb][j][1]), p[3] - bf16_hi(hw[cb][j][1]));
+    }
   }
   if constexpr (kP == 2) {
-    const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{hw[0][0], hw[0][1], hw[1][0], hw[1][1]});
-    const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{lw[0][0], lw[0][1], lw[1][0], lw[1][1]});
+    bf16x8 bh[kCB], bl[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb) {
+      bh[cb] = __builtin_bit_cast(bf16x8, u32x4{hw[cb][0][0], hw[cb][0][1], hw[cb][1][0], hw[cb][1][1]});
+      bl[cb] = __builtin_bit_cast(bf16x8, u32x4{lw[cb][0][0], lw[cb][0][1], lw[cb][1][0], lw[cb][1][1]});
+    }
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const u32x2 t0 = read_v_tr(vpage[0], vaddr[nb]);
-      const u32x2 t1 = read_v_tr(vpage[1], vaddr[nb]);
+      const u32x2 t0 = read_v_tr(vpage[0], off.v(nb));
+      const u32x2 t1 = read_v_tr(vpage[1], off.v(nb));
       const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{t0[0], t0[1], t1[0], t1[1]});
-      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, st.acc[nb], 0, 0, 0);
-      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, st.acc[nb], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb) {
+        st[cb].acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[cb], st[cb].acc[nb], 0, 0, 0);
+        st[cb].acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[cb], st[cb].acc[nb], 0, 0, 0);
+      }
     }
   } else {
-    const bf16x8 bw = __builtin_bit_cast(bf16x8, u32x4{hw[0][0], hw[0][1], lw[0][0], lw[0][1]});
+    bf16x8 bw[kCB];
+#pragma unroll
+    for (int cb = 0; cb < kCB; ++cb)
+      bw[cb] = __builtin_bit_cast(bf16x8, u32x4{hw[cb][0][0], hw[cb][0][1], lw[cb][0][0], lw[cb][0][1]});
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const u32x2 t0 = read_v_tr(vpage[0], vaddr[nb]);
+      const u32x2 t0 = read_v_tr(vpage[0], off.v(nb));
       const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{t0[0], t0[1], t0[0], t0[1]});
-      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, st.acc[nb], 0, 0, 0);
+#pragma unroll
+      for (int cb = 0; cb < kCB; ++cb)
+        st[cb].acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[cb], st[cb].acc[nb], 0, 0, 0);
     }
   }
 }
 
 // Chunks of several tiles (prefill, longer verification): the tiles of one
 // KV head share each K/V page through LDS.  A workgroup of 4 waves, one per
-// SIMD, takes one sequence, kHG = 4 / kTG KV heads and kTG consecutive token
-// tiles, one (head, tile) per wave: 4 tiles of one head for long chunks, 2
-// tiles of 2 heads for chunks of two tiles.  Two workgroups share a CU, and
-// since each waits only at its own barriers, one's matrix-core products
-// overlap the other's LDS traffic and softmax; at 8 waves per workgroup the
-// barrier put every wave of the CU in the same phase, and the CU's matrix
-// cores ran about half the time.  Pages go in steps of kP (2 with one head,
-// 1 with two): per step the 256 threads load the heads' K and V tiles of the
-// step's pages (one 16-byte piece of K and one of V per thread, page and
+// SIMD, takes one sequence, kHG = 4 / kTG KV heads and kTG consecutive wave
+// tiles, one (head, wave tile) per wave: 4 wave tiles of one head for long
+// chunks, 2 of 2 heads for chunks of two tiles.  A wave tile is kCB
+// 16-column blocks of 16/G tokens each: with kCB = 2 (long chunks, where the
+// grid still gives two workgroups per compute unit) every K and V value the
+// wave reads from LDS feeds the products of both blocks, which halves the LDS
+// traffic per product.  Two workgroups share a CU, and since each waits only
+// at its own barriers, one's matrix-core products overlap the other's LDS
+// traffic and softmax; at 8 waves per workgroup the barrier put every wave of
+// the CU in the same phase, and the CU's matrix cores ran about half the
+// time.  Pages go in steps of kP (2 with one head and one block, else 1, for
+// the registers): per step the 256 threads load the heads' K and V tiles of
+// the step's pages (one 16-byte piece of K and one of V per thread, page and
 // head, kDepth steps in flight) and write them to one of three LDS stages --
 // K with its 16-byte pieces XOR-swizzled by position (kswz), so that the
 // score product's reads (16 positions at one dim offset) fall on distinct
 // banks, V swizzled for the transpose reads (vswz) and zero past the
 // sequence or past the last page; each wave then scores the step's pages
-// (step_scores) and, one step later, weighs them and sums V
+// (step_scores, per block) and, one step later, weighs them and sums V
 // (step_weights_pv).  The queries enter the score product as two bf16 terms
 // (to a relative 2^-18, the weights' own precision) rather than the decode's
 // three, which takes a sixth of the products.  The cache is read once per
-// kTG tiles, and the workgroups of one KV head (kTG = 4) are consecutive
+// kTG wave tiles, and the workgroups of one KV head (kTG = 4) are consecutive
 // modulo 8, which keeps them on one XCD, where they share the pages through
 // L2.
 
 constexpr int kChunkWaves = 4;                // (head, tile) pairs per workgroup
 constexpr int kChunkQTerms = 2;               // bf16 terms of each query element
 constexpr int kChunkPrefillMinTiles = 2;      // chunks of this many tiles share pages
+constexpr int kChunkWideMinGroups = 512;      // workgroups two-block waves must still give
 
-template <int kG, int kTG>
+template <int kG, int kTG, int kCB>
 __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(ChunkArgs a) {
   constexpr int kH = kG * kKvHeads;
-  constexpr int kTpt = 16 / kG;            // tokens per tile
+  constexpr int kTpb = 16 / kG;            // tokens per block
+  constexpr int kTpt = kCB * kTpb;         // tokens per wave tile
   constexpr int kHG = kChunkWaves / kTG;   // KV heads per workgroup
-  constexpr int kP = kHG == 1 ? 2 : 1;     // pages per step
-  constexpr int kDepth = kHG == 1 ? 4 : 2;  // steps in flight (16 or 8 pieces per thread)
+  constexpr int kP = kHG == 1 && kCB == 1 ? 2 : 1;  // pages per step
+  constexpr int kDepth = kHG == 1 ? 4 : 2;  // steps in flight (8 to 16 pieces per thread)
   using TileV = Tile<DAH_BF16>;
   constexpr int kTileBytes = (int)TileV::kTileBytes;
   constexpr int kHeadBytes = 2 * kTileBytes;  // K and V of one head and page in a stage
@@ -2028,7 +2069,8 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = wave / kTG, tw = wave - hw * kTG;   // the wave's local head and tile
   const int row = lane >> 4, col = lane & 15;
-  const int groups = (a.tiles + kTG - 1) / kTG;
+  const int wides = (a.tiles + kCB - 1) / kCB;
+  const int groups = (wides + kTG - 1) / kTG;
   constexpr int kHeadGroups = kKvHeads / kHG;
   const int gh = blockIdx.x % kHeadGroups;
   const int bg = blockIdx.x / kHeadGroups;
@@ -2053,8 +2095,8 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
           reinterpret_cast<float2*>(a.o + (((size_t)t0 + i) * kH + g * kG + h) * kHeadDim)[lane] =
               make_float2(NAN, NAN);
     };
-    if (live && tile < a.tiles) poison(i0, min(n, i0 + kTpt));
-    if (tile == 0) poison(a.tiles * kTpt, n);
+    if (live && kCB * tile < a.tiles) poison(i0, min(n, min(i0 + kTpt, a.tiles * kTpb)));
+    if (tile == 0) poison(a.tiles * kTpb, n);
     return;  // the whole workgroup (the condition is uniform)
   }
 
@@ -2067,10 +2109,17 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
   const int group_tokens = min(n, (tile0 + kTG) * kTpt);
   const int last = (seq_len - n + group_tokens - 1) / kPage;  // last page of any wave
   const int ti = col / kG, hh = col - ti * kG;
-  const bool col_live = live && ti < ntok;
-  const int climit_pos = pos0 + (col_live ? ti : ntok - 1);
-  const size_t qrow = ((size_t)t0 + (live ? i0 : 0) + (col_live ? ti : 0)) * kH + g * kG +
-                      (col_live ? hh : 0);
+  bool col_live[kCB];
+  int climit_pos[kCB];
+  size_t qrow[kCB];
+#pragma unroll
+  for (int cb = 0; cb < kCB; ++cb) {
+    const int tok = cb * kTpb + ti;
+    col_live[cb] = live && ti < kTpb && tok < ntok;
+    climit_pos[cb] = pos0 + (col_live[cb] ? tok : ntok - 1);
+    qrow[cb] = ((size_t)t0 + (live ? i0 : 0) + (col_live[cb] ? tok : 0)) * kH + g * kG +
+               (col_live[cb] ? hh : 0);
+  }
 
   typedef const __attribute__((address_space(4))) int32_t* ConstI32;
   const ConstI32 bt = (ConstI32)(a.block_table + (size_t)b * a.max_pages_per_seq);
@@ -2110,42 +2159,50 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
 #pragma unroll
   for (int i = 0; i < kDepth; ++i) fetch(ring[i], i);
 
-  float qv[4][8];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) load8(a.q + qrow * kHeadDim + 32 * kk + 8 * row, qv[kk]);
   const float qscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  u32x4 qb[4][kChunkQTerms];
+  u32x4 qb[kCB][4][kChunkQTerms];
+  PrefillState st[kCB];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int cb = 0; cb < kCB; ++cb) {
+    float qv[4][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[kk][e] *= qscale;
-    split_terms<kChunkQTerms>(qv[kk], qb[kk]);
+    for (int kk = 0; kk < 4; ++kk) load8(a.q + qrow[cb] * kHeadDim + 32 * kk + 8 * row, qv[kk]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[kk][e] *= qscale;
+      split_terms<kChunkQTerms>(qv[kk], qb[cb][kk]);
+    }
+    if (!col_live[cb]) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int t = 0; t < kChunkQTerms; ++t) qb[cb][kk][t] = u32x4{0u, 0u, 0u, 0u};
+    }
+    st[cb].m = -INFINITY;
+    st[cb].l = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) st[cb].acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  if (!col_live) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int t = 0; t < kChunkQTerms; ++t) qb[kk][t] = u32x4{0u, 0u, 0u, 0u};
-  }
-  PrefillState st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int kpos = 4 * (col & 3) + (col >> 2);  // sigma(col): the score product's K row
-  int kaddr[4];
+  // K: lane (row, col) reads row sigma(col) of the score product, pieces
+  // row + 4 kk (swizzled).  V: transpose reads of position 4 (col / 4) + row,
+  // dims 16 nb + 4 (col mod 4) of its head.  (row + 4 kk) ^ kswz splits into
+  // the low two bits and the rest, since the two addends share no bit.
+  const int kpos = 4 * (col & 3) + (col >> 2);  // sigma(col)
+  const int kb = hw * kHeadBytes + 256 * kpos + 16 * (row ^ (kswz(kpos) & 3));
+  const int kq = kswz(kpos) >> 2;
+  const int vP = 4 * (col >> 2) + row;
+  const int vb = hw * kHeadBytes + kTileBytes + 256 * vP + 16 * ((col & 3) >> 1) + 8 * (col & 1);
+  const int vx = vswz(vP);
+  StageOffsets<kCB == 1> off;
+  if constexpr (kCB == 1) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    kaddr[kk] = hw * kHeadBytes + 256 * kpos + 16 * ((row + 4 * kk) ^ kswz(kpos));
-  // Transpose-read offsets of V within a stage page: lane (row, col) points
-  // at position 4 (col / 4) + row, dims 16 nb + 4 (col mod 4) of its head.
-  int vaddr[8];
-  {
-    const int P = 4 * (col >> 2) + row;
-    const int base = hw * kHeadBytes + kTileBytes + 256 * P + 16 * ((col & 3) >> 1) + 8 * (col & 1);
+    for (int kk = 0; kk < 4; ++kk) off.ko[kk] = kb + 64 * (kk ^ kq);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) vaddr[nb] = base + 32 * (nb ^ vswz(P));
+    for (int nb = 0; nb < 8; ++nb) off.vo[nb] = vb + 32 * (nb ^ vx);
+  } else {
+    off = StageOffsets<false>{kb, kq, vb, vx};
   }
 
   // Software pipeline across steps: after step s's barrier a wave issues
@@ -2154,7 +2211,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
   // the VALU works on the other.  Three stages: step s writes stage s mod 3,
   // last read by step s - 3's K reads and step s - 2's V sum, both before
   // barrier s - 1.
-  f32x4 sprev[kP];
+  f32x4 sprev[kCB][kP];
   bool prev_on = false;  // step s - 1 awaits its softmax and V sum
   int cur = 0;           // stage of step s
   int prev = 0;          // stage of step s - 1
@@ -2179,36 +2236,42 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
       fetch(ring[i], s + kDepth);
       const int p0 = kP * s;
       const bool on = p0 <= wave_last;
-      f32x4 scur[kP];
+      f32x4 scur[kCB][kP];
       if (on) {
         KTileMfma K[kP];
 #pragma unroll
         for (int j = 0; j < kP; ++j) {
           const char* sp = stg + j * kPageBytes;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) K[j].w[kk] = *reinterpret_cast<const u32x4*>(sp + kaddr[kk]);
+          for (int kk = 0; kk < 4; ++kk) K[j].w[kk] = *reinterpret_cast<const u32x4*>(sp + off.k(kk));
         }
         if (p0 + kP - 1 < first_masked && p0 + kP - 1 <= wave_last) {
           const int cl[kP] = {};
-          step_scores<kP, false>(K, qb, lane, cl, scur);
-        } else {
-          int cl[kP];
 #pragma unroll
-          for (int j = 0; j < kP; ++j) {
-            const int p = p0 + j;
-            cl[j] = p > wave_last ? 0 : p < first_masked ? kPage : climit_pos - kPage * p + 1;
+          for (int cb = 0; cb < kCB; ++cb) step_scores<kP, false>(K, qb[cb], lane, cl, scur[cb]);
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < kCB; ++cb) {
+            int cl[kP];
+#pragma unroll
+            for (int j = 0; j < kP; ++j) {
+              const int p = p0 + j;
+              cl[j] = p > wave_last ? 0 : p < first_masked ? kPage : climit_pos[cb] - kPage * p + 1;
+            }
+            step_scores<kP, true>(K, qb[cb], lane, cl, scur[cb]);
           }
-          step_scores<kP, true>(K, qb, lane, cl, scur);
         }
       }
       if (prev_on) {
         const char* vpage[kP];
 #pragma unroll
         for (int j = 0; j < kP; ++j) vpage[j] = &stage[prev][j * kPageBytes];
-        step_weights_pv<kP>(sprev, vpage, vaddr, st);
+        step_weights_pv<kCB, kP>(sprev, vpage, off, st);
       }
 #pragma unroll
-      for (int j = 0; j < kP; ++j) sprev[j] = scur[j];
+      for (int cb = 0; cb < kCB; ++cb)
+#pragma unroll
+        for (int j = 0; j < kP; ++j) sprev[cb][j] = scur[cb][j];
       prev_on = on;
       prev = cur;
       cur = cur == 2 ? 0 : cur + 1;
@@ -2218,30 +2281,31 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
     const char* vpage[kP];
 #pragma unroll
     for (int j = 0; j < kP; ++j) vpage[j] = &stage[prev][j * kPageBytes];
-    step_weights_pv<kP>(sprev, vpage, vaddr, st);
+    step_weights_pv<kCB, kP>(sprev, vpage, off, st);
   }
   if (!live) return;
 
-  // Column col = (token ti, head hh): its sum over the four rows, then dims
-  // 16 nb + 4 row .. +3 of its output row from this lane.
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!col_live) return;
-  const float scale = bad_page ? NAN : 1.0f / l;
-  float* orow = a.o + (((size_t)t0 + i0 + ti) * kH + g * kG + hh) * kHeadDim + 4 * row;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
-    *reinterpret_cast<float4*>(orow + 16 * nb) =
-        make_float4(st.acc[nb][0] * scale, st.acc[nb][1] * scale, st.acc[nb][2] * scale,
-                    st.acc[nb][3] * scale);
+  for (int cb = 0; cb < kCB; ++cb) {
+    float l = st[cb].l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!col_live[cb]) continue;
+    const float scale = bad_page ? NAN : 1.0f / l;
+    float* orow = a.o + (((size_t)t0 + i0 + cb * kTpb + ti) * kH + g * kG + hh) * kHeadDim + 4 * row;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      *reinterpret_cast<float4*>(orow + 16 * nb) =
+          make_float4(st[cb].acc[nb][0] * scale, st[cb].acc[nb][1] * scale,
+                      st[cb].acc[nb][2] * scale, st[cb].acc[nb][3] * scale);
+  }
 }
 
-template <int kG, int kTG>
+template <int kG, int kTG, int kCB>
 void launch_chunk_prefill(const ChunkArgs& c, int B, hipStream_t stream) {
-  const long long groups = (c.tiles + kTG - 1) / kTG;
+  const long long groups = ((c.tiles + kCB - 1) / kCB + kTG - 1) / kTG;
   const long long heads = kKvHeads / (kChunkWaves / kTG);
-  chunk_prefill_kernel<kG, kTG>
+  chunk_prefill_kernel<kG, kTG, kCB>
       <<<dim3((unsigned)((long long)B * groups * heads)), kWave * kChunkWaves, 0, stream>>>(c);
 }
 
@@ -2434,11 +2498,15 @@ int launch_chunk(const float* q, const float* k_new, const float* v_new, const f
     c.tiles = (max_chunk + kTpt - 1) / kTpt;
     if (c.tiles >= kChunkPrefillMinTiles) {
       // Tiles per workgroup: 2 for chunks of two tiles (2 KV heads per
-      // workgroup), else 4 of one head.
+      // workgroup), else 4 of one head -- 4 waves of two 16-column blocks
+      // each where that still gives two workgroups per compute unit.
+      const long long wide_groups = ((c.tiles + 1) / 2 + 3) / 4;
       if (c.tiles <= 2)
-        launch_chunk_prefill<kG, 2>(c, B, stream);
+        launch_chunk_prefill<kG, 2, 1>(c, B, stream);
+      else if ((long long)B * kKvHeads * wide_groups >= kChunkWideMinGroups)
+        launch_chunk_prefill<kG, 4, 2>(c, B, stream);
       else
-        launch_chunk_prefill<kG, 4>(c, B, stream);
+        launch_chunk_prefill<kG, 4, 1>(c, B, stream);
       st = check_launch("chunk_prefill_kernel");
     } else {
       chunk_attn_kernel<kG><<<dim3((unsigned)((long long)B * c.tiles)),

@@ -264,12 +264,44 @@ def test_out_of_domain_sequences(c, over, dt):
     assert int(changed.sum()) == c * 8       # sequence 0's slots, 8 heads each
 
 
+def test_out_of_domain_on_two_block_waves():
+    """The same preconditions where the shared-page kernel takes two 16-column
+    blocks per wave (64 sequences of 64-token chunks at 16 heads: eight tiles
+    each, 512 workgroups): sequences that cannot hold their chunk, lie past
+    max_seq_len or bring more than max_chunk tokens get NaN and no append;
+    the others match the oracle."""
+    import torch
+    B, c = 64, 64
+    chunks = [c] * (B - 1) + [c + 4]
+    t, table, seq_lens, cu = W.make_chunk_inputs([100] * B, chunks, 16, "bf16", 17, "cuda")
+    max_seq_len = 100 + c
+    t["seq_lens"][1] = 2                    # cannot hold its chunk
+    t["seq_lens"][3] = max_seq_len + 37     # past max_seq_len
+    good = [0, 2, 5, 40, 62]
+    snap = _snapshot(t, table, t["seq_lens"].cpu().numpy(), cu, good)
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    q_out, o = _dah().chunk_attn_step(t["q"], t["k_new"], t["v_new"], t["q_gain"], t["k_gain"],
+                                      t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                      t["cu_tokens"], c, max_seq_len)
+    torch.cuda.synchronize()
+    for b in (1, 3, B - 1):                 # B - 1 holds c + 4 > max_chunk tokens
+        assert torch.isnan(o[int(cu[b]):int(cu[b + 1])]).all(), b
+    ok = torch.ones(o.shape[0], dtype=torch.bool, device=o.device)
+    for b in (1, 3, B - 1):
+        ok[int(cu[b]):int(cu[b + 1])] = False
+    assert torch.isfinite(o[ok]).all()
+    changed = (t["k_pool"] != k0).any(dim=3) | (t["v_pool"] != v0).any(dim=3)
+    assert int(changed.sum()) == c * (B - 3) * 8    # every valid token's slot, 8 heads
+    ref = _oracle(snap)
+    _check_o(o.cpu().numpy()[snap["tokens"]], snap, ref, 1e6, "two-block waves")
+
+
 @pytest.mark.parametrize("chunk,H,dt", [(4, 16, "bf16"), (16, 16, "bf16"), (64, 64, "bf16"),
-                                        (4, 40, "f32")])
+                                        (512, 16, "bf16"), (4, 40, "f32")])
 def test_chunk_under_graph_replay(chunk, H, dt):
     """chunk_attn_step captured in one HIP graph -- the one-tile kernel, the
-    shared-page kernel with 4 heads and with 1 head per workgroup, and the
-    float32 path: every replay, with eager work and synchronisations between
+    shared-page kernel with 2 heads and with 1 head per workgroup, with one
+    and with two 16-column blocks per wave, and the float32 path: every replay, with eager work and synchronisations between
     replays, equals the eager result bit for bit.  The cache is restored
     before each run, since the step appends to it."""
     import torch
