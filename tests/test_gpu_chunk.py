@@ -172,10 +172,13 @@ def test_f32_cache_chunks_every_token(H):
 
 @pytest.mark.parametrize("name,lens_old,chunk,B,H", [
     ("verify", 2044, 4, 64, 16), ("verify", 2044, 4, 64, 64),
-    ("prefill", 0, 1024, 4, 16), ("prefill_after_context", 3000, 512, 4, 40)])
+    ("prefill", 0, 1024, 4, 16), ("prefill_after_context", 3000, 512, 4, 40),
+    ("prefill_32_heads", 700, 512, 4, 32)])
 def test_large_chunks(name, lens_old, chunk, B, H):
     """Verification of 4 drafted tokens over 2,044 cached positions at B=64,
-    and chunked prefill of 512-1,024 tokens: every token of every sequence."""
+    and chunked prefill of 512-1,024 tokens at 16, 32 and 40 heads (the
+    prefill cases on two 16-column blocks per wave): every token of every
+    sequence."""
     rng = np.random.default_rng(B + chunk)
     olds = [lens_old + int(x) for x in rng.integers(0, 8, B)] if lens_old else [0] * B
     t, table, seq_lens, cu = W.make_chunk_inputs(olds, [chunk] * B, H, "bf16", 100 + H, "cuda")
