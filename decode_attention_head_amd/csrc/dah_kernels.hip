@@ -2080,7 +2080,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
   const int t0 = min(max(a.cu_tokens[b], 0), a.total);
   const int t1 = min(max(a.cu_tokens[b + 1], t0), a.total);
   const int n = t1 - t0;
-  const int tile0 = grp * kTG;   // first tile of the workgroup
+  const int tile0 = grp * kTG;   // first wave tile of the workgroup
   if (tile0 * kTpt >= n) return;  // the whole workgroup
   const int tile = tile0 + tw;
   const int i0 = tile * kTpt;
@@ -2100,7 +2100,7 @@ __global__ __launch_bounds__(kWave * kChunkWaves, 2) void chunk_prefill_kernel(C
     return;  // the whole workgroup (the condition is uniform)
   }
 
-  // Within the preconditions every live token is below a.tiles * kTpt.
+  // Within the preconditions every live token is below a.tiles * kTpb.
   const int ntok = live ? min(kTpt, n - i0) : 1;
   const int pos0 = seq_len - n + i0;  // position of the wave's first token
   const int pmax = pos0 + ntok - 1;
