@@ -299,6 +299,34 @@ def test_out_of_domain_on_two_block_waves():
     _check_o(o.cpu().numpy()[snap["tokens"]], snap, ref, 1e6, "two-block waves")
 
 
+@pytest.mark.parametrize("B,c", [(4, 4), (4, 20), (64, 64)])
+def test_page_ids_outside_the_pool(B, c):
+    """A block-table entry outside the pool (past num_pages, or negative)
+    among a sequence's cached pages: every token of that sequence attends to
+    it, so its outputs are NaN, nothing is read through it, and its chunk is
+    still appended (the tokens' own pages are valid); the other sequences
+    match the oracle.  Chunks of 4 tokens take the one-tile kernel, of 20
+    the shared-page kernel with one block per wave, 64 at B = 64 two blocks
+    per wave."""
+    import torch
+    t, table, seq_lens, cu = W.make_chunk_inputs([100] * B, [c] * B, 16, "bf16", 23 + c, "cuda")
+    num_pages = t["k_pool"].shape[0]
+    good = [0, 3] + ([10, B - 1] if B > 4 else [])
+    snap = _snapshot(t, table, seq_lens, cu, good)
+    t["block_table"][1, 2] = num_pages + 5
+    t["block_table"][2, 0] = -1
+    k0, v0 = t["k_pool"].clone(), t["v_pool"].clone()
+    q_out, o = _run(t, cu, seq_lens, c)
+    for b in (1, 2):
+        assert torch.isnan(o[int(cu[b]):int(cu[b + 1])]).all(), b
+    changed = (t["k_pool"] != k0).any(dim=3) | (t["v_pool"] != v0).any(dim=3)
+    assert int(changed.sum()) == c * B * 8      # every token appended, bad rows included
+    ref = _oracle(snap)
+    o_good = o.cpu().numpy()[snap["tokens"]]
+    assert np.isfinite(o_good).all()
+    _check_o(o_good, snap, ref, 1e6, f"page ids outside the pool, c={c}")
+
+
 @pytest.mark.parametrize("chunk,H,dt", [(4, 16, "bf16"), (16, 16, "bf16"), (64, 64, "bf16"),
                                         (512, 16, "bf16"), (4, 40, "f32")])
 def test_chunk_under_graph_replay(chunk, H, dt):
