@@ -32,6 +32,10 @@ The JSON line reports
                   host cores), repeated to about 10 s of work, and its
                   single-core rate (about 3 s); the oracle's first pass over
                   each workload gives the per-config errors
+  prefill         chunk_attn_step with 1,024 new tokens per sequence at the
+                  end of the four long_b4_s40960 contexts (--prefill-tokens):
+                  graph-replayed time, attention TFLOP/s and % of the bf16
+                  dense matrix-core peak
 
 --chunk N also times chunk_attn_step with N new tokens per sequence (the
 workload's lengths counting them), under "chunk": HIP-graph-replayed time,
@@ -65,6 +69,7 @@ sys.path.insert(0, ROOT)
 from inputs import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_head_amd", "csrc", "dah_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -99,6 +104,9 @@ def parse():
                          "paged-read probe (the decode's access pattern alone)")
     ap.add_argument("--chunk", type=int, default=0, metavar="N",
                     help="also time chunk_attn_step with N new tokens per sequence")
+    ap.add_argument("--prefill-tokens", type=int, default=1024, metavar="N",
+                    help="the prefill record: chunk_attn_step with N new tokens per sequence "
+                         "over the long_b4_s40960 lengths (0 skips it)")
     ap.add_argument("--layer", action="store_true",
                     help="also time decoder_layer_step on the same batch")
     ap.add_argument("--block", action="store_true",
@@ -607,6 +615,19 @@ def run(args, pool):
     del layers, t, ws, q_outs, o
     torch.cuda.empty_cache()
 
+    # The chunked-prefill record: N-token chunks at the end of the four long
+    # contexts, graph-replayed, against the bf16 dense matrix-core peak.
+    prefill = None
+    if args.prefill_tokens > 0:
+        pw = W.WORKLOADS["long_b4_s40960"]
+        p_lens = W.make_seq_lens(pw)
+        _, p_pages = W.make_block_table(pw, p_lens)
+        prefill = time_chunk(dah, torch, pw, p_lens, p_pages, args.prefill_tokens)
+        if "tflops" in prefill:
+            prefill = {"workload": pw.name, **prefill,
+                       "pct_bf16_dense_peak": round(100.0 * prefill["tflops"] / BF16_PEAK_TFLOPS, 2)}
+        torch.cuda.empty_cache()
+
     # The five workloads, each timed on its own, median of args.config_iters
     # steps with the last-level cache flushed between them; then the
     # oracle leg over their sequences (CPU rate, and each config's error).
@@ -740,6 +761,8 @@ def run(args, pool):
         line["block"] = block
     if chunk is not None:
         line["chunk"] = chunk
+    if prefill is not None:
+        line["prefill"] = prefill
     if layer is not None:
         line["layer"] = layer
     print(json.dumps(line), flush=True)
